@@ -1,0 +1,94 @@
+"""NumPy implementation of the counter-based input generator (see package docstring)."""
+import math
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+GAMMA = 0x9E3779B97F4A7C15          # SplitMix64 increment (odd, ~2**64 / golden ratio)
+_M1 = 0xBF58476D1CE4E5B9            # SplitMix64 finaliser multipliers
+_M2 = 0x94D049BB133111EB
+LANE_SUM_STD = math.sqrt((65536.0 * 65536.0 - 1.0) / 3.0)
+
+# Stream identifiers: one stream per tensor, so any element of any tensor can
+# be regenerated from (seed, stream, flat index) alone.
+TENSOR = {
+    "w_qkv": 0, "w_out": 1, "w_fc1": 2, "w_fc2": 3,
+    "b_qkv": 4, "b_out": 5, "b_fc1": 6, "b_fc2": 7,
+    "ln1_g": 8, "ln1_b": 9, "ln2_g": 10, "ln2_b": 11,
+}
+STREAM = {
+    "hidden": 1 << 20,        # C1/C2 hidden-state stream [B, P+T, h]
+    "prompt": (1 << 20) + 1,  # token ids [B, P]
+    "embed": (1 << 20) + 2,   # token embedding [V, h]
+    "pos": (1 << 20) + 3,     # learned positions [P+G+2, h]
+    "lnf_g": (1 << 20) + 4,
+    "lnf_b": (1 << 20) + 5,
+    "aux": (1 << 20) + 16,    # free streams for tests: aux + k
+}
+
+
+def layer_stream(layer: int, tensor: str) -> int:
+    """Stream id of one per-layer tensor."""
+    return layer * 64 + TENSOR[tensor]
+
+
+def mix64(z):
+    """SplitMix64 output function on a uint64 ndarray (wrapping arithmetic)."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(_M1)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(_M2)
+        return z ^ (z >> np.uint64(31))
+
+
+def _mix64_int(z: int) -> int:
+    z &= MASK64
+    z = ((z ^ (z >> 30)) * _M1) & MASK64
+    z = ((z ^ (z >> 27)) * _M2) & MASK64
+    return z ^ (z >> 31)
+
+
+def stream_key(seed: int, stream: int) -> int:
+    """Key of one stream: mix64(seed * GAMMA + stream)."""
+    return _mix64_int((seed * GAMMA + stream) & MASK64)
+
+
+def raw_u64(seed: int, stream: int, index) -> np.ndarray:
+    """64-bit outputs at the given flat indices (any integer array)."""
+    idx = np.asarray(index, dtype=np.uint64)
+    key = np.uint64(stream_key(seed, stream))
+    with np.errstate(over="ignore"):
+        ctr = key + (idx + np.uint64(1)) * np.uint64(GAMMA)
+    return mix64(ctr)
+
+
+def normal_scale_f32(sigma: float) -> np.float32:
+    """fp32 multiplier that maps the centred lane sum to standard deviation sigma."""
+    return np.float32(sigma / LANE_SUM_STD)
+
+
+def normal_f16(seed: int, stream: int, shape=None, sigma: float = 1.0, index=None,
+               chunk: int = 1 << 24) -> np.ndarray:
+    """fp16 variates with std ``sigma``: either a whole tensor of ``shape`` (flat
+    indices 0..n-1, row-major) or the elements at flat ``index``."""
+    if index is None:
+        n = int(np.prod(shape))
+        out = np.empty(n, dtype=np.float16)
+        for s in range(0, n, chunk):
+            e = min(n, s + chunk)
+            out[s:e] = normal_f16(seed, stream, sigma=sigma, index=np.arange(s, e, dtype=np.uint64))
+        return out.reshape(shape)
+    u = raw_u64(seed, stream, index)
+    m = np.uint64(0xFFFF)
+    lane_sum = ((u & m) + ((u >> np.uint64(16)) & m) + ((u >> np.uint64(32)) & m)
+                + (u >> np.uint64(48))).astype(np.int64) - 131070
+    return (lane_sum.astype(np.float32) * normal_scale_f32(sigma)).astype(np.float16)
+
+
+def token_ids(seed: int, stream: int, shape, vocab: int) -> np.ndarray:
+    """Uniform token ids in [0, vocab) as int32, flat indices 0..n-1."""
+    n = int(np.prod(shape))
+    u = raw_u64(seed, stream, np.arange(n, dtype=np.uint64))
+    with np.errstate(over="ignore"):
+        ids = ((u >> np.uint64(32)) * np.uint64(vocab)) >> np.uint64(32)
+    return ids.astype(np.int32).reshape(shape)

@@ -1,0 +1,94 @@
+"""Pins of the oracle's layer step and generation loop: causal consistency
+(prefill of P+1 tokens == prefill of P then one decode step, exact because a
+quantisation group never spans two tokens), a zero-weight layer that reduces
+to its residual path in closed form, and greedy-generation consistency."""
+import numpy as np
+
+import synth
+from oracle import (LayerConfig, ModelConfig, layer_params, pack_layer, new_cache, layer_step,
+                    generate, argmax_lowest, quantize, dequant_f64)
+from oracle.model import model_params, embed, lm_head_logits
+
+CFG = LayerConfig(hidden=256, heads=4, ffn=1024)
+
+
+def _x(B, T, h, seed=0):
+    return synth.normal_f16(seed, synth.STREAM["hidden"], (B, T, h), 1.0)
+
+
+def test_causal_consistency_prefill_vs_decode():
+    for bias in (0.0, 0.02):
+        p = layer_params(0, CFG, 0, bias)
+        pk = pack_layer(p, CFG)
+        x = _x(3, 13, 256)
+        c1 = new_cache(CFG, 3, 16)
+        full = layer_step(x, p, pk, c1, CFG, 0)
+        c2 = new_cache(CFG, 3, 16)
+        part = layer_step(x[:, :10], p, pk, c2, CFG, 0)
+        outs = [part["y"]]
+        for t in range(10, 13):
+            outs.append(layer_step(x[:, t:t + 1], p, pk, c2, CFG, t)["y"])
+        inc = np.concatenate(outs, 1)
+        assert np.array_equal(inc.view(np.uint16), full["y"].view(np.uint16))
+        for key in c1:
+            assert np.array_equal(c1[key][:, :, :13], c2[key][:, :, :13])
+
+
+def test_zero_weight_layer_reduces_to_residual_path():
+    p = layer_params(0, CFG, 1, bias_sigma=0.05)
+    for w in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+        p[w] = np.zeros_like(p[w])
+    pk = pack_layer(p, CFG)
+    x = _x(2, 5, 256, seed=2)
+    c = new_cache(CFG, 2, 8)
+    r = layer_step(x, p, pk, c, CFG, 0, want=("o",))
+    h = 256
+    x1 = (x.astype(np.float64) + p["b_out"].astype(np.float64)).astype(np.float16)
+    expect = (x1.astype(np.float64) + p["b_fc2"].astype(np.float64)).astype(np.float16)
+    assert np.array_equal(r["y"].view(np.uint16), expect.view(np.uint16))
+    # every token's key/value is the bias; the cache holds its quantisation at each position
+    bv = p["b_qkv"][2 * h:].reshape(4, 64)
+    vc, vm = quantize(bv)
+    for t in range(5):
+        assert np.array_equal(c["v_codes"][:, :, t], np.broadcast_to(vc, (2, 4, 32)))
+    # equal keys -> uniform attention -> o = reconstructed bias value
+    np.testing.assert_array_equal(r["o"].reshape(2, 5, 4, 64)[0, 3],
+                                  dequant_f64(vc, vm).astype(np.float16))
+
+
+def test_uncompressed_weights_and_cache_variant_runs_and_is_consistent():
+    cfg = LayerConfig(hidden=256, heads=4, ffn=512, compress_weight=False, compress_cache=False)
+    p = layer_params(0, cfg, 0)
+    pk = pack_layer(p, cfg)
+    assert pk["w_qkv"] is p["w_qkv"]
+    x = _x(2, 6, 256)
+    a = layer_step(x, p, pk, new_cache(cfg, 2, 8), cfg, 0)["y"]
+    c = new_cache(cfg, 2, 8)
+    layer_step(x[:, :5], p, pk, c, cfg, 0)
+    b = layer_step(x[:, 5:], p, pk, c, cfg, 5)["y"]
+    assert np.array_equal(a[:, 5:].view(np.uint16), b.view(np.uint16))
+
+
+def test_argmax_ties_lowest_index():
+    logits = np.array([[0.0, 2.0, 2.0, 1.0], [5.0, 5.0, 5.0, 5.0]])
+    assert argmax_lowest(logits).tolist() == [1, 0]
+
+
+def test_generate_matches_teacher_forced_prefill():
+    mcfg = ModelConfig(layer=CFG, layers=2, vocab=512, max_pos=32)
+    ids = synth.token_ids(0, synth.STREAM["prompt"], (2, 6), 512)
+    out = generate(ids, 4, 0, mcfg)
+    toks = out["tokens"]
+    assert toks.shape == (2, 4) and toks.min() >= 0 and toks.max() < 512
+    # logits of generated token t come from prefill over prompt + tokens 1..t-1
+    mp = model_params(0, mcfg)
+    lps = [layer_params(0, CFG, l) for l in range(2)]
+    pks = [pack_layer(p, CFG) for p in lps]
+    for t in range(4):
+        seq = np.concatenate([ids, toks[:, :t]], 1)
+        x = embed(seq, mp["embed"], mp["pos"], 0)
+        for l in range(2):
+            x = layer_step(x, lps[l], pks[l], new_cache(CFG, 2, 12), CFG, 0)["y"]
+        lg = lm_head_logits(x[:, -1], mp["lnf_g"], mp["lnf_b"], mp["embed"])
+        np.testing.assert_allclose(lg, out["logits"][t], rtol=1e-12, atol=1e-12)
+        assert np.array_equal(argmax_lowest(lg), toks[:, t])
