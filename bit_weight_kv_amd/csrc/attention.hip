@@ -1,0 +1,354 @@
+// Attention over the 4-bit KV cache: the decode kernel (K3, one new query
+// per sequence) and the causal prefill kernel (K5, T new queries).
+//
+// Cache format (FlexGen README, "Extreme Compression": the attention cache is
+// stored in 4 bits): per sequence b, head h and position j, head_dim/2 bytes
+// of nibble codes and one fp16 {min, scale} pair per 64 channels.  Keys and
+// values are reconstructed in registers (fp32 min + code * scale) and never
+// written back; the kernel reads 0.5625 bytes per cached element.
+//
+// Decode, per (b, h) work-group of 256 threads:
+//   1. scores: thread t takes positions t, t+256, ...; for each it streams the
+//      key's codes (16-byte loads) and computes q . k^ group by group as
+//      s_g * (q . c) + min_g * sum(q_g), so the reconstruction costs no extra
+//      multiply per element;  scores go to LDS;
+//   2. softmax with block max / sum reductions (exp2 of log2(e)-scaled scores);
+//   3. values: 16 lanes cover one position's codes (4 bytes = 8 channels per
+//      lane), 16 positions are in flight per block; each lane accumulates
+//      sum_j (p_j s_jg) c_ji and sum_j p_j min_jg, then the 16 partial sums
+//      are reduced through LDS.
+#include "common.h"
+
+namespace fq {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline float block_max256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ inline float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Codes of 8 consecutive channels (one word) as exact fp16 integers, 4 pairs
+// in natural channel order.
+__device__ inline void codes8_f16(uint32_t w, half2_t out[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const half2_t bias = {(half_t)-1024.0f, (half_t)-1024.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + j) << 16 | (uint32_t)j;
+    const uint32_t p = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    out[j] = __builtin_bit_cast(half2_t, p) + bias;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
+                                                               const uint8_t* __restrict__ kc,
+                                                               const uint16_t* __restrict__ km,
+                                                               const uint8_t* __restrict__ vc,
+                                                               const uint16_t* __restrict__ vm, int H, int64_t cap,
+                                                               int64_t b0, int len, uint16_t* __restrict__ out,
+                                                               int64_t ldo) {
+  constexpr int G = D / 64;       // groups per head
+  constexpr int WORDS = D / 8;    // 32-bit code words per position
+  constexpr int LPP = WORDS;      // lanes per position in the value pass
+  constexpr int SLOTS = 256 / LPP;
+  extern __shared__ float smem[];  // [len] probabilities, then [SLOTS][D] partial outputs
+  __shared__ float red[4];
+
+  const int b = blockIdx.y, h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t row0 = ((b0 + b) * H + h) * cap;  // first cache row of this (b, h)
+
+  // ---- query: fp16 pairs in registers, per-group sums of q ----
+  const uint16_t* qp = q + (int64_t)b * ldq + (int64_t)h * D;
+  half2_t qv[D / 2];
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    const uint4 r = *reinterpret_cast<const uint4*>(qp + i * 8);
+    qv[4 * i + 0] = __builtin_bit_cast(half2_t, r.x);
+    qv[4 * i + 1] = __builtin_bit_cast(half2_t, r.y);
+    qv[4 * i + 2] = __builtin_bit_cast(half2_t, r.z);
+    qv[4 * i + 3] = __builtin_bit_cast(half2_t, r.w);
+  }
+  float qsum[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += (float)qv[g * 32 + i].x + (float)qv[g * 32 + i].y;
+    qsum[g] = s;
+  }
+
+  // ---- scores ----
+  float* p = smem;
+  float lmax = -INFINITY;
+  for (int j = tid; j < len; j += 256) {
+    const uint4* crow = reinterpret_cast<const uint4*>(kc + (row0 + j) * (D / 2));
+    const uint32_t* mrow = reinterpret_cast<const uint32_t*>(km) + (row0 + j) * G;
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t mb = mrow[g];
+      float dc = 0.f;
+#pragma unroll
+      for (int v4 = 0; v4 < 2; ++v4) {
+        const uint4 c = crow[g * 2 + v4];
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          half2_t cc[4];
+          codes8_f16(w[k], cc);
+          const int base = (g * 64 + v4 * 32 + k * 8) / 2;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dc = __builtin_amdgcn_fdot2(cc[u], qv[base + u], dc, false);
+        }
+      }
+      s += h2f((uint16_t)(mb >> 16)) * dc + h2f((uint16_t)(mb & 0xFFFF)) * qsum[g];
+    }
+    s *= kLog2e;
+    p[j] = s;
+    lmax = fmaxf(lmax, s);
+  }
+  const float mx = block_max256(lmax, red);
+  float lsum = 0.f;
+  for (int j = tid; j < len; j += 256) {
+    const float e = exp2f(p[j] - mx);
+    p[j] = e;
+    lsum += e;
+  }
+  const float inv = 1.0f / block_sum256(lsum, red);  // also orders the p[] writes before the reads below
+
+  // ---- values ----
+  const int slot = tid / LPP, wl = tid % LPP;  // wl: code word (8 channels) of this lane
+  const int g = wl / 8;                        // group of those channels
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float bsum = 0.f;
+  for (int j = slot; j < len; j += SLOTS) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[wl];
+    const uint32_t mb = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + g];
+    const float pj = p[j];
+    const float a = pj * h2f((uint16_t)(mb >> 16));
+    bsum += pj * h2f((uint16_t)(mb & 0xFFFF));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += a * (float)((w >> (4 * k)) & 0xF);
+  }
+  float* part = smem + ((len + 3) & ~3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) part[slot * D + wl * 8 + k] = acc[k] + bsum;
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.f;
+#pragma unroll 4
+    for (int s2 = 0; s2 < SLOTS; ++s2) o += part[s2 * D + tid];
+    out[(int64_t)b * ldo + (int64_t)h * D + tid] = f2h(o * inv);
+  }
+}
+
+// ---- causal prefill: flash-style online softmax on the vector units --------
+// Block = 64 queries of one (b, h); 4 lanes per query, each owning D/4
+// channels.  Keys/values are reconstructed chunk by chunk (64 positions) into
+// LDS as fp32 and read back as broadcasts.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
+                                                                const uint8_t* __restrict__ kc,
+                                                                const uint16_t* __restrict__ km,
+                                                                const uint8_t* __restrict__ vc,
+                                                                const uint16_t* __restrict__ vm, int H, int64_t cap,
+                                                                int64_t b0, int T, int64_t pos,
+                                                                uint16_t* __restrict__ out, int64_t ldo) {
+  constexpr int QT = 64, KC = 64, PART = D / 4, G = D / 64;
+  __shared__ __attribute__((aligned(16))) float Ks[KC][D + 4];
+  __shared__ __attribute__((aligned(16))) float Vs[KC][D + 4];
+
+  const int tid = threadIdx.x;
+  const int qi = tid >> 2, part = tid & 3;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int t0 = blockIdx.x * QT;
+  const int t = t0 + qi;
+  const bool qok = t < T;
+  const int64_t qpos = pos + t;  // absolute position of this query
+  const int64_t row0 = ((b0 + b) * H + h) * cap;
+
+  float qf[PART];
+  {
+    const uint16_t* qp = q + ((int64_t)b * T + (qok ? t : 0)) * ldq + (int64_t)h * D + part * PART;
+#pragma unroll
+    for (int i = 0; i < PART; i += 8) {
+      const uint4 r = *reinterpret_cast<const uint4*>(qp + i);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qf[i + 2 * k] = h2f((uint16_t)(w[k] & 0xFFFF)) * kLog2e;
+        qf[i + 2 * k + 1] = h2f((uint16_t)(w[k] >> 16)) * kLog2e;
+      }
+    }
+  }
+  float o[PART];
+#pragma unroll
+  for (int i = 0; i < PART; ++i) o[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int64_t last_q = pos + min(T, t0 + QT) - 1;  // largest query position in the tile
+  const int64_t nkeys = last_q + 1;
+  for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
+    __syncthreads();
+    // reconstruct KC positions x D channels of K and V: 2*KC*D/8 words over 256 threads
+    for (int wi = tid; wi < 2 * KC * (D / 8); wi += 256) {
+      const int which = wi / (KC * (D / 8));
+      const int r = (wi / (D / 8)) % KC, w8 = wi % (D / 8);
+      const int64_t j = k0 + r;
+      float* dst = which ? &Vs[r][w8 * 8] : &Ks[r][w8 * 8];
+      if (j < nkeys) {
+        const uint8_t* cbase = which ? vc : kc;
+        const uint16_t* mbase = which ? vm : km;
+        const uint32_t w = reinterpret_cast<const uint32_t*>(cbase + (row0 + j) * (D / 2))[w8];
+        const uint32_t mb = reinterpret_cast<const uint32_t*>(mbase)[(row0 + j) * G + w8 / 8];
+        const float mn = h2f((uint16_t)(mb & 0xFFFF)), s = h2f((uint16_t)(mb >> 16));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[k] = mn + (float)((w >> (4 * k)) & 0xF) * s;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[k] = 0.f;
+      }
+    }
+    __syncthreads();
+    const int64_t kend = min((int64_t)KC, nkeys - k0);
+    for (int r = 0; r < kend; ++r) {
+      const int64_t j = k0 + r;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < PART; i += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(&Ks[r][part * PART + i]);
+        s += qf[i] * kv.x + qf[i + 1] * kv.y + qf[i + 2] * kv.z + qf[i + 3] * kv.w;
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (!qok || j > qpos) continue;  // causal mask (uniform across the 4 lanes of a query)
+      if (s > m) {
+        const float c = exp2f(m - s);
+        l *= c;
+#pragma unroll
+        for (int i = 0; i < PART; ++i) o[i] *= c;
+        m = s;
+      }
+      const float pj = exp2f(s - m);
+      l += pj;
+#pragma unroll
+      for (int i = 0; i < PART; i += 4) {
+        const float4 vv = *reinterpret_cast<const float4*>(&Vs[r][part * PART + i]);
+        o[i] += pj * vv.x;
+        o[i + 1] += pj * vv.y;
+        o[i + 2] += pj * vv.z;
+        o[i + 3] += pj * vv.w;
+      }
+    }
+  }
+  if (qok) {
+    const float inv = 1.0f / l;
+    uint16_t* op = out + ((int64_t)b * T + t) * ldo + (int64_t)h * D + part * PART;
+#pragma unroll
+    for (int i = 0; i < PART; i += 8) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)f2h(o[i + 2 * k] * inv) | ((uint32_t)f2h(o[i + 2 * k + 1] * inv) << 16);
+      *reinterpret_cast<uint4*>(op + i) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+fq_status check_kv(const fq_kv_layer* kv, const char* who) {
+  if (!kv) return fail(FQ_ERR_INVALID, std::string(who) + ": kv is NULL");
+  if (kv->group != FQ_GROUP) return fail(FQ_ERR_UNSUPPORTED, std::string(who) + ": only group 64 is implemented");
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(FQ_ERR_UNSUPPORTED, std::string(who) + ": head_dim must be 64 or 128");
+  if (!kv->k_codes || !kv->k_meta || !kv->v_codes || !kv->v_meta)
+    return fail(FQ_ERR_INVALID, std::string(who) + ": NULL cache buffer");
+  return FQ_OK;
+}
+
+}  // namespace
+}  // namespace fq
+
+using namespace fq;
+
+extern "C" fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
+                                         int64_t len, uint16_t* out, int64_t ldo, void* stream) {
+  clear_error();
+  FQ_TRY(check_kv(kv, "fq_decode_attention"));
+  const int64_t hd = (int64_t)kv->heads * kv->head_dim;
+  FQ_CHECK_ARG(b0 >= 0 && B >= 0 && b0 + B <= kv->batch, "fq_decode_attention: sequence range exceeds the cache");
+  FQ_CHECK_ARG(len >= 1 && len <= kv->capacity, "fq_decode_attention: len must be in [1, capacity]");
+  FQ_CHECK_ARG(ldq >= hd && ldo >= hd && ldq % 8 == 0, "fq_decode_attention: bad strides");
+  FQ_CHECK_ARG(len <= 30000, "fq_decode_attention: len above 30000 does not fit the LDS score buffer");
+  if (B == 0) return FQ_OK;
+  FQ_CHECK_ARG(q && out && (uintptr_t)q % 16 == 0, "fq_decode_attention: q/out NULL or q misaligned");
+  const int D = kv->head_dim;
+  const size_t lds = (size_t)((len + 3) & ~3) * sizeof(float) + (size_t)256 * 8 * sizeof(float);
+  const dim3 grid((unsigned)kv->heads, (unsigned)B);
+  hipStream_t st = as_stream(stream);
+  const int tk = timing_begin(st);
+  if (D == 128)
+    decode_attention_kernel<128><<<grid, dim3(256), lds, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                               kv->v_meta, kv->heads, kv->capacity, b0, (int)len,
+                                                               out, ldo);
+  else
+    decode_attention_kernel<64><<<grid, dim3(256), lds, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                              kv->v_meta, kv->heads, kv->capacity, b0, (int)len, out,
+                                                              ldo);
+  FQ_TRY(launch_check("decode_attention_kernel"));
+  if (tk >= 0) {
+    const double units = (double)B * kv->heads;
+    timing_end(tk, FQ_KC_DECODE_ATTN, units * 4.0 * len * D, units * (2.0 * len * D * 0.5625 + 4.0 * D), st);
+  }
+  return FQ_OK;
+}
+
+extern "C" fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0,
+                                          int64_t B, int64_t T, int64_t pos, uint16_t* out, int64_t ldo,
+                                          void* stream) {
+  clear_error();
+  FQ_TRY(check_kv(kv, "fq_prefill_attention"));
+  const int64_t hd = (int64_t)kv->heads * kv->head_dim;
+  FQ_CHECK_ARG(b0 >= 0 && B >= 0 && b0 + B <= kv->batch, "fq_prefill_attention: sequence range exceeds the cache");
+  FQ_CHECK_ARG(T >= 0 && pos >= 0 && pos + T <= kv->capacity, "fq_prefill_attention: positions exceed capacity");
+  FQ_CHECK_ARG(ldq >= hd && ldo >= hd && ldq % 8 == 0 && ldo % 8 == 0, "fq_prefill_attention: bad strides");
+  if (B == 0 || T == 0) return FQ_OK;
+  FQ_CHECK_ARG(q && out && (uintptr_t)q % 16 == 0 && (uintptr_t)out % 16 == 0,
+               "fq_prefill_attention: q/out NULL or misaligned");
+  const dim3 grid((unsigned)ceil_div(T, 64), (unsigned)kv->heads, (unsigned)B);
+  hipStream_t st = as_stream(stream);
+  const int tk = timing_begin(st);
+  if (kv->head_dim == 128)
+    prefill_attention_kernel<128><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                              kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
+                                                              out, ldo);
+  else
+    prefill_attention_kernel<64><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                             kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
+                                                             out, ldo);
+  FQ_TRY(launch_check("prefill_attention_kernel"));
+  if (tk >= 0) {
+    const double units = (double)B * kv->heads, d = kv->head_dim;
+    const double pairs = (double)T * pos + (double)T * (T + 1) / 2.0;  // (query, key) pairs under the causal mask
+    timing_end(tk, FQ_KC_PREFILL_ATTN, units * 4.0 * pairs * d,
+               units * (4.0 * T * d + 2.0 * (pos + T) * d * 0.5625), st);
+  }
+  return FQ_OK;
+}

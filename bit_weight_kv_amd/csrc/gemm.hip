@@ -1,0 +1,362 @@
+// Dequant-fused projection GEMM (K2) and its fp16-weight variant (K2f):
+//   C[M, N] = epilogue(A[M, K] * W^T),  A fp16 row-major, W [N, K].
+//
+// The compressed weight is the 4-bit group format (groups of 64 along K, fp16
+// {min, scale} per group; FlexGen README, "Extreme Compression").  Compute
+// runs on the reconstructed fp16 weight with fp32 accumulation on the gfx950
+// matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// Tiling (one K step = 64 = exactly one quantisation group per weight row):
+//   * a block of WM x WN waves owns a BM x BN tile of C;
+//   * per K step the block stages A[BM, 64] (fp16) and the reconstructed
+//     W[BN, 64] (fp16) in LDS, double-buffered, rows padded to 72 halves so
+//     the 16-lane fragment reads hit distinct banks;
+//   * the 4-bit codes are read from HBM as 16-byte vectors (32 codes), turned
+//     into fp16 with the exponent trick (0x6400 | code is the fp16 value
+//     1024 + code, exact) and reconstructed with one packed fp16 FMA, which
+//     rounds min + code * s once -- bit-identical to the reference
+//     reconstruction;
+//   * each wave runs (BM/WM/16) x (BN/WN/16) MFMA tiles per 32-wide k slice.
+// Blocks are remapped so that neighbouring M tiles of one N tile share an XCD
+// (the hardware deals consecutive block ids round-robin to the 8 XCDs, each
+// with its own L2), so one XCD's L2 serves all re-reads of a weight tile.
+// Split-K (grid.z) writes fp32 partials that a second kernel reduces and
+// passes through the epilogue; used when the M x N grid cannot fill 256 CUs.
+#include "common.h"
+
+namespace fq {
+namespace {
+
+constexpr int BK = 64;
+constexpr int LDS_STRIDE = BK + 8;  // halves per staged row (144 bytes)
+
+struct Epilogue {
+  const uint16_t* bias;
+  const uint16_t* residual;
+  int64_t ldr;
+  uint32_t flags;
+  float qscale;
+  int64_t qcols;
+  void* C;
+  int64_t ldc;
+};
+
+__device__ inline void epilogue_store(const Epilogue& e, int64_t m, int64_t n, float v) {
+  if (e.flags & FQ_EPI_BIAS) v += h2f(e.bias[n]);
+  if ((e.flags & FQ_EPI_QSCALE) && n < e.qcols) v *= e.qscale;
+  if (e.flags & FQ_EPI_RELU) v = fmaxf(v, 0.0f);
+  if (e.flags & FQ_EPI_RESIDUAL) v += h2f(e.residual[m * e.ldr + n]);
+  if (e.flags & FQ_EPI_F32OUT)
+    reinterpret_cast<float*>(e.C)[m * e.ldc + n] = v;
+  else
+    reinterpret_cast<uint16_t*>(e.C)[m * e.ldc + n] = f2h(v);
+}
+
+// 8 codes (one 32-bit word, element 2k in the low nibble of byte k) -> 8 fp16
+// values fp16(mn + c*s) in natural order, as 4 packed pairs.
+__device__ inline void dequant8(uint32_t w, half2_t mn2, half2_t s2, uint32_t out[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: c0 c2 c4 c6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: c1 c3 c5 c7
+  const half2_t bias = {(half_t)-1024.0f, (half_t)-1024.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // bytes [lo.b_j, 0, hi.b_j, 0] then exponent 0x64: halves (1024 + c_2j, 1024 + c_2j+1)
+    const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + j) << 16 | (uint32_t)j;
+    const uint32_t p = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    const half2_t c = __builtin_bit_cast(half2_t, p) + bias;  // exact: small integers
+    out[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool PACKED>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
+                                                             const uint8_t* __restrict__ codes,
+                                                             const uint16_t* __restrict__ meta,
+                                                             const uint16_t* __restrict__ w16, int64_t N, int64_t K,
+                                                             int k_tiles_per_split, Epilogue epi,
+                                                             float* __restrict__ partial) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  constexpr int A_CHUNKS = BM * 8;  // 16-byte chunks of A per K step
+  constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
+  constexpr int B_CHUNKS = PACKED ? BN * 2 : BN * 8;
+  constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+
+  // XCD-aware tile order: block ids b, b+8, b+16, ... run on one XCD; give
+  // them consecutive logical tiles (M fastest, so they share weight tiles).
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t nblk = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  int64_t logical = bid;
+  if (nblk >= 16) {
+    const int64_t per_xcd = nblk / 8;
+    const int64_t xcd = bid % 8, slot = bid / 8;
+    if (bid < per_xcd * 8) logical = xcd * per_xcd + slot;
+  }
+  const int64_t m0 = (logical % tiles_m) * BM;
+  const int64_t n0 = (logical / tiles_m) * BN;
+
+  const int KT = (int)(K / BK);
+  const int kt0 = blockIdx.z * k_tiles_per_split;
+  const int kt1 = min(KT, kt0 + k_tiles_per_split);
+
+  uint4 ra[A_PER_T];
+  uint4 rb[B_PER_T];
+  uint32_t rm[B_PER_T];
+
+  auto load_tiles = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int c = tid + i * NT;
+      ra[i] = make_uint4(0, 0, 0, 0);
+      if (c < A_CHUNKS) {
+        const int r = c >> 3, kc = c & 7;
+        const int64_t m = m0 + r;
+        if (m < M) ra[i] = *reinterpret_cast<const uint4*>(A + m * lda + (int64_t)kt * BK + kc * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+      const int c = tid + i * NT;
+      rb[i] = make_uint4(0, 0, 0, 0);
+      rm[i] = 0;
+      if (c < B_CHUNKS) {
+        if (PACKED) {
+          const int r = c >> 1, half = c & 1;
+          const int64_t n = n0 + r;
+          if (n < N) {
+            rb[i] = *reinterpret_cast<const uint4*>(codes + n * (K / 2) + (int64_t)kt * 32 + half * 16);
+            rm[i] = reinterpret_cast<const uint32_t*>(meta)[n * (K / 64) + kt];
+          }
+        } else {
+          const int r = c >> 3, kc = c & 7;
+          const int64_t n = n0 + r;
+          if (n < N) rb[i] = *reinterpret_cast<const uint4*>(w16 + n * K + (int64_t)kt * BK + kc * 8);
+        }
+      }
+    }
+  };
+
+  auto store_tiles = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int c = tid + i * NT;
+      if (c < A_CHUNKS) {
+        const int r = c >> 3, kc = c & 7;
+        *reinterpret_cast<uint4*>(&As[buf][r * LDS_STRIDE + kc * 8]) = ra[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+      const int c = tid + i * NT;
+      if (c < B_CHUNKS) {
+        if (PACKED) {
+          const int r = c >> 1, half = c & 1;
+          const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(rm[i] & 0xFFFF));
+          const half_t s = __builtin_bit_cast(half_t, (uint16_t)(rm[i] >> 16));
+          const half2_t mn2 = {mn, mn}, s2 = {s, s};
+          const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t o[4];
+            dequant8(w[q], mn2, s2, o);
+            *reinterpret_cast<uint4*>(&Bs[buf][r * LDS_STRIDE + half * 32 + q * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
+          }
+        } else {
+          const int r = c >> 3, kc = c & 7;
+          *reinterpret_cast<uint4*>(&Bs[buf][r * LDS_STRIDE + kc * 8]) = rb[i];
+        }
+      }
+    }
+  };
+
+  float4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  if (kt0 < kt1) {
+    load_tiles(kt0);
+    store_tiles(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const bool more = kt + 1 < kt1;
+      if (more) load_tiles(kt + 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        half8_t af[FM], bf[FN];
+        const int kofs = ks * 32 + 8 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[i] = *reinterpret_cast<const half8_t*>(&As[cur][(wm * TM + i * 16 + (lane & 15)) * LDS_STRIDE + kofs]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bf[j] = *reinterpret_cast<const half8_t*>(&Bs[cur][(wn * TN + j * 16 + (lane & 15)) * LDS_STRIDE + kofs]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+      if (more) store_tiles(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // D layout of the 16x16 MFMA: lane holds column lane%16, rows 4*(lane/16)+r.
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * TM + i * 16 + 4 * (lane >> 4) + r;
+        if (m < M && n < N) {
+          if (partial)
+            partial[((int64_t)blockIdx.z * M + m) * N + n] = acc[i][j][r];
+          else
+            epilogue_store(epi, m, n, acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
+                                                            int64_t N, Epilogue epi) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * N) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; ++z) s += partial[(int64_t)z * M * N + i];
+  epilogue_store(epi, i / N, i % N, s);
+}
+
+// Split-K workspace, grown on demand and kept for the life of the process.
+struct Workspace {
+  float* ptr = nullptr;
+  size_t bytes = 0;
+  int device = -1;
+};
+thread_local Workspace g_ws;
+
+fq_status get_workspace(size_t bytes, float** out) {
+  int dev = 0;
+  FQ_HIP(hipGetDevice(&dev));
+  if (g_ws.ptr && (g_ws.bytes < bytes || g_ws.device != dev)) {
+    FQ_HIP(hipDeviceSynchronize());
+    (void)hipFree(g_ws.ptr);
+    g_ws.ptr = nullptr;
+    g_ws.bytes = 0;
+  }
+  if (!g_ws.ptr) {
+    hipError_t e = hipMalloc(&g_ws.ptr, bytes);
+    if (e != hipSuccess) {
+      g_ws.ptr = nullptr;
+      return fail(FQ_ERR_OOM, "fq_dequant_gemm: split-K workspace allocation failed");
+    }
+    g_ws.bytes = bytes;
+    g_ws.device = dev;
+  }
+  *out = g_ws.ptr;
+  return FQ_OK;
+}
+
+template <int BM, int BN, int WM, int WN>
+fq_status run_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi, int splits,
+                   hipStream_t st) {
+  const int64_t tiles = ceil_div(M, BM) * ceil_div(W->n, BN);
+  const int KT = (int)(W->k / BK);
+  splits = std::max(1, std::min(splits, KT));
+  const int kps = (KT + splits - 1) / splits;
+  splits = (KT + kps - 1) / kps;
+  float* partial = nullptr;
+  if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * W->n * sizeof(float), &partial));
+  const dim3 grid((unsigned)tiles, 1, (unsigned)splits);
+  const dim3 block(WM * WN * 64);
+  if (W->kind == FQ_WEIGHT_PACKED4)
+    gemm_kernel<BM, BN, WM, WN, true><<<grid, block, 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, nullptr,
+                                                              W->n, W->k, kps, epi, partial);
+  else
+    gemm_kernel<BM, BN, WM, WN, false><<<grid, block, 0, st>>>(A, M, lda, nullptr, nullptr, W->w16, W->n, W->k, kps,
+                                                               epi, partial);
+  FQ_TRY(launch_check("gemm_kernel"));
+  if (splits > 1) {
+    splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * W->n, 256)), dim3(256), 0, st>>>(partial, splits, M, W->n, epi);
+    FQ_TRY(launch_check("splitk_reduce_kernel"));
+  }
+  return FQ_OK;
+}
+
+}  // namespace
+}  // namespace fq
+
+using namespace fq;
+
+extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
+                                     const uint16_t* bias, const uint16_t* residual, int64_t ldr, uint32_t epilogue,
+                                     float qscale, int64_t qscale_cols, void* C, int64_t ldc, void* stream) {
+  clear_error();
+  FQ_CHECK_ARG(W != nullptr, "fq_dequant_gemm: W is NULL");
+  FQ_CHECK_ARG(W->kind == FQ_WEIGHT_PACKED4 || W->kind == FQ_WEIGHT_F16, "fq_dequant_gemm: unknown weight kind");
+  const int64_t N = W->n, K = W->k;
+  FQ_CHECK_ARG(M >= 0 && N > 0 && K > 0, "fq_dequant_gemm: bad shape");
+  FQ_CHECK_ARG(K % 64 == 0, "fq_dequant_gemm: K must be a multiple of 64");
+  FQ_CHECK_ARG(lda >= K && lda % 8 == 0, "fq_dequant_gemm: lda must be >= K and a multiple of 8");
+  FQ_CHECK_ARG(ldc >= N, "fq_dequant_gemm: ldc < N");
+  if (W->kind == FQ_WEIGHT_PACKED4) {
+    if (W->packed.group != FQ_GROUP) return fail(FQ_ERR_UNSUPPORTED, "fq_dequant_gemm: only group 64 is implemented");
+    FQ_CHECK_ARG(W->packed.rows == N && W->packed.cols == K, "fq_dequant_gemm: packed shape differs from n/k");
+    FQ_CHECK_ARG(W->packed.codes && W->packed.meta, "fq_dequant_gemm: NULL packed weight");
+    FQ_CHECK_ARG(((uintptr_t)W->packed.codes % 16 == 0) && ((uintptr_t)W->packed.meta % 4 == 0),
+                 "fq_dequant_gemm: packed weight must be 16-byte aligned");
+  } else {
+    FQ_CHECK_ARG(W->w16 != nullptr && (uintptr_t)W->w16 % 16 == 0, "fq_dequant_gemm: fp16 weight NULL or misaligned");
+  }
+  FQ_CHECK_ARG(!(epilogue & FQ_EPI_BIAS) || bias, "fq_dequant_gemm: BIAS without bias");
+  FQ_CHECK_ARG(!(epilogue & FQ_EPI_RESIDUAL) || (residual && ldr >= N), "fq_dequant_gemm: RESIDUAL without residual");
+  if (M == 0) return FQ_OK;
+  FQ_CHECK_ARG(A && C, "fq_dequant_gemm: NULL A or C");
+  FQ_CHECK_ARG((uintptr_t)A % 16 == 0, "fq_dequant_gemm: A must be 16-byte aligned");
+  Epilogue epi{bias, residual, ldr, epilogue, qscale, qscale_cols, C, ldc};
+  hipStream_t st = as_stream(stream);
+  // Tile choice: enough tiles to fill 256 CUs, split-K when the grid is small.
+  const int KT = (int)(K / 64);
+  const int tk = timing_begin(st);
+  fq_status r;
+  if (M <= 32) {
+    const int64_t tiles = ceil_div(N, 64);
+    const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
+    r = run_gemm<32, 64, 1, 4>(A, M, lda, W, epi, splits, st);
+  } else if (M <= 256) {
+    const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
+    const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
+    r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
+  } else {
+    const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    const int splits = tiles >= 256 ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / tiles));
+    r = run_gemm<128, 128, 2, 2>(A, M, lda, W, epi, splits, st);
+  }
+  if (r == FQ_OK && tk >= 0) {
+    const double wbytes = W->kind == FQ_WEIGHT_PACKED4 ? 0.5625 * N * K : 2.0 * N * K;
+    const double cbytes = (epilogue & FQ_EPI_F32OUT) ? 4.0 * M * N : 2.0 * M * N;
+    const double bytes = 2.0 * M * K + wbytes + cbytes + ((epilogue & FQ_EPI_RESIDUAL) ? 2.0 * M * N : 0.0) +
+                         ((epilogue & FQ_EPI_BIAS) ? 2.0 * N : 0.0);
+    const int cls = (epilogue & FQ_EPI_F32OUT) ? FQ_KC_LM_HEAD : (M > 256 ? FQ_KC_GEMM_PREFILL : FQ_KC_GEMM_DECODE);
+    timing_end(tk, cls, 2.0 * M * N * K, bytes, st);
+  }
+  return r;
+}

@@ -1,0 +1,329 @@
+/*
+ * fq.h -- C ABI of libfq: 4-bit weight + 4-bit KV-cache decoding of OPT-style
+ * decoder layers on one AMD MI355X (gfx950).
+ *
+ * The method is FlexGen's (Sheng et al., "High-Throughput Generative Inference
+ * of Large Language Models with a Single GPU"): weights and the attention KV
+ * cache are compressed to 4 bits (FlexGen README, key features, "Extreme
+ * Compression"; pith.science abstract), compute runs on the reconstructed
+ * values, weights that do not fit in device memory are streamed layer by
+ * layer from pinned host memory with copies overlapped with compute (README,
+ * "Benchmark Results" discussion of the block schedule; awesome-repositories
+ * feature "Asynchronous Tensor Loading"), and throughput is generated tokens
+ * divided by prompt time plus generation time (README, "Benchmark Results",
+ * Metric bullet).
+ *
+ * Readings this library fixes where the pages are silent (the pages state only
+ * "4 bits"):
+ *   - group = 64 consecutive elements along the contiguous (last) axis;
+ *   - asymmetric min/max: code = clamp(rint_half_even((x - min) / s), 0, 15),
+ *     s = fp16((max - min) / 15) computed in IEEE fp32; min and s stored as an
+ *     fp16 pair per group; a -0 minimum and a zero scale are stored as +0;
+ *   - nibble order: element 2k in the low nibble of byte k;
+ *   - reconstruction for GEMM operands: fp16(min + code * s), one rounding.
+ *
+ * Conventions for every call:
+ *   - fp16 values travel as uint16_t bit patterns.
+ *   - Pointers documented "device" are HIP device memory owned by the caller;
+ *     "host" pointers are host memory owned by the caller.  No call keeps a
+ *     caller pointer after it returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous on that stream unless stated otherwise.
+ *   - Every call returns an fq_status; on failure fq_last_error() gives a
+ *     thread-local message.  Nothing aborts and no C++ exception crosses the
+ *     ABI.  Shape errors are detected on the host before any launch.
+ *   - Handles are not thread-safe; distinct handles may be used concurrently.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FQ_OK = 0,
+  FQ_ERR_INVALID = -1,     /* bad argument or shape */
+  FQ_ERR_UNSUPPORTED = -2, /* valid request outside what this build implements */
+  FQ_ERR_OOM = -3,         /* device or pinned-host allocation failed */
+  FQ_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} fq_status;
+
+#define FQ_GROUP 64
+
+/* Thread-local text of the last non-OK status ("" if none). */
+const char* fq_last_error(void);
+/* Library version string. */
+const char* fq_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Packed 4-bit tensor.  Logical fp16 matrix [rows, cols], cols % 64 == 0.
+ *   codes: device uint8  [rows, cols/2]        row-major, nibble pairs
+ *   meta:  device uint16 [rows, cols/64, 2]    fp16 {min, scale} per group   */
+typedef struct {
+  uint8_t* codes;
+  uint16_t* meta;
+  int64_t rows;
+  int64_t cols;
+  int32_t group; /* must be 64 */
+} fq_packed;
+
+/* Quantise an fp16 matrix group-wise to 4 bits (FlexGen README, "Extreme
+ * Compression": weights and attention cache stored in 4 bits).
+ *   x:   device fp16 [rows, cols], row stride ldx elements (ldx >= cols)
+ *   out: codes/meta device buffers of the sizes above; out->rows/cols must
+ *        equal rows/cols and out->group must be 64.
+ * Bit-exact with the reading in the header comment.  Errors: FQ_ERR_INVALID
+ * for cols % 64 != 0, ldx < cols, null pointers; FQ_ERR_UNSUPPORTED for a
+ * group other than 64. */
+fq_status fq_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const fq_packed* out,
+                      void* stream);
+
+/* Reconstruct a packed matrix to fp16: y[r, c] = fp16(min + code * s).
+ *   y: device fp16 [rows, cols] contiguous.  (Debug and test helper.) */
+fq_status fq_dequantize(const fq_packed* in, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Weight operand of a projection: W [N = out features, K = in features],
+ * either 4-bit packed (groups along K) or plain fp16 row-major [N, K]. */
+typedef enum { FQ_WEIGHT_PACKED4 = 0, FQ_WEIGHT_F16 = 1 } fq_weight_kind;
+
+typedef struct {
+  int32_t kind;        /* fq_weight_kind */
+  fq_packed packed;    /* kind == FQ_WEIGHT_PACKED4: rows = N, cols = K */
+  const uint16_t* w16; /* kind == FQ_WEIGHT_F16: device fp16 [N, K] */
+  int64_t n;           /* N */
+  int64_t k;           /* K, multiple of 64 */
+} fq_weight;
+
+/* Epilogue flags of fq_dequant_gemm, applied in this order in fp32:
+ *   BIAS:     v += bias[n]
+ *   QSCALE:   v *= qscale for columns n < qscale_cols (query scaling d^-1/2)
+ *   RELU:     v = max(v, 0)
+ *   RESIDUAL: v += residual[m, n]
+ * then one rounding to fp16 (or an fp32 store with F32OUT). */
+enum {
+  FQ_EPI_BIAS = 1u << 0,
+  FQ_EPI_QSCALE = 1u << 1,
+  FQ_EPI_RELU = 1u << 2,
+  FQ_EPI_RESIDUAL = 1u << 3,
+  FQ_EPI_F32OUT = 1u << 4
+};
+
+/* C[M, N] = epilogue(A[M, K] * W^T) with the weight reconstructed in
+ * registers (fp16) and fp32 accumulation on the matrix cores: the
+ * dequant-fused projection GEMM of the QKV, output and FFN layers.
+ *   A:        device fp16, row stride lda (>= K)
+ *   bias:     device fp16 [N] (FQ_EPI_BIAS) or NULL
+ *   residual: device fp16, row stride ldr (FQ_EPI_RESIDUAL) or NULL; may alias C
+ *             only when ldr == ldc (each element is read before it is written)
+ *   C:        device fp16 (or fp32 with FQ_EPI_F32OUT), row stride ldc (>= N)
+ * M may be 0 (no-op).  Errors: FQ_ERR_INVALID for K % 64 != 0, strides too
+ * small, null pointers required by the flags. */
+fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const uint16_t* bias,
+                          const uint16_t* residual, int64_t ldr, uint32_t epilogue, float qscale,
+                          int64_t qscale_cols, void* C, int64_t ldc, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* One layer of 4-bit KV cache (device memory; caller- or handle-owned):
+ *   k_codes, v_codes: uint8  [batch, heads, capacity, head_dim/2]
+ *   k_meta,  v_meta:  uint16 [batch, heads, capacity, head_dim/64, 2]
+ * One group = 64 consecutive head-dim channels of one token and head, so a
+ * group never spans two tokens.  head_dim % 64 == 0. */
+typedef struct {
+  uint8_t* k_codes;
+  uint16_t* k_meta;
+  uint8_t* v_codes;
+  uint16_t* v_meta;
+  int64_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int64_t capacity;
+  int32_t group; /* must be 64 */
+} fq_kv_layer;
+
+/* Quantise-on-append: the new tokens' K and V (fp16) become 4-bit cache
+ * entries (FlexGen README, "Extreme Compression": the attention cache is
+ * stored in 4 bits).
+ *   k, v: device fp16; row r = b*T + t holds heads*head_dim values of token
+ *         t of sequence b; row stride ld elements (e.g. the K and V column
+ *         blocks of a fused QKV activation with ld = 3*hidden)
+ *   writes cache positions pos..pos+T-1 of sequences b0..b0+B-1.
+ * Errors: FQ_ERR_INVALID if b0+B > batch or pos+T > capacity. */
+fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, const uint16_t* v, int64_t ld, int64_t b0,
+                       int64_t B, int64_t T, int64_t pos, void* stream);
+
+/* Decode attention over the packed cache: for each sequence b and head h,
+ * s_j = q . k^_j for j < len, p = softmax(s), o = sum_j p_j v^_j, with k^, v^
+ * reconstructed in registers in fp32 (min + code * s).
+ *   q:   device fp16 [B, heads*head_dim] row stride ldq, already scaled by
+ *        head_dim^-1/2
+ *   out: device fp16 [B, heads*head_dim] row stride ldo
+ *   uses cache sequences b0..b0+B-1, positions 0..len-1 (1 <= len <= capacity). */
+fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
+                              int64_t len, uint16_t* out, int64_t ldo, void* stream);
+
+/* Causal attention of T new tokens at positions pos..pos+T-1 (already
+ * appended to the cache): query t sees cache positions 0..pos+t.
+ *   q: device fp16 rows b*T + t, stride ldq (scaled);  out: same layout, ldo. */
+fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
+                               int64_t T, int64_t pos, uint16_t* out, int64_t ldo, void* stream);
+
+/* LayerNorm over rows: y = (x - mean) / sqrt(var + eps) * gamma + beta with
+ * fp32 statistics (biased variance) and one rounding to fp16.
+ *   x, y: device fp16 [M, h] with strides ldx, ldy;  gamma, beta: device fp16 [h]. */
+fq_status fq_layernorm(const uint16_t* x, int64_t M, int64_t h, int64_t ldx, const uint16_t* gamma,
+                       const uint16_t* beta, float eps, uint16_t* y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Model description (OPT-style pre-LayerNorm decoder, ReLU FFN). */
+typedef struct {
+  int32_t hidden;  /* h */
+  int32_t heads;   /* H, head_dim = h / H (multiple of 64) */
+  int32_t ffn;     /* F */
+  int32_t layers;  /* L */
+  int32_t vocab;   /* V (0: no embedding / LM head; layer-only model) */
+  int32_t max_pos; /* rows of the learned position table (positions used: p + 2) */
+} fq_model_config;
+
+/* Placement policy (FlexGen README, "Get Started": --percent places weights
+ * and cache; "Handle Out-of-memory": --compress-weight, --pin-weight). */
+typedef struct {
+  int32_t compress_weight; /* 1: 4-bit packed weights resident in HBM; 0: fp16 weights */
+  int32_t compress_cache;  /* must be 1 (4-bit KV cache) */
+  int32_t resident_layers; /* fp16 weights only: layers kept in HBM, the rest live in
+                              pinned host memory and are streamed; -1 = all resident */
+  int32_t host_layers;     /* fp16 streamed weights: distinct host layer blobs; layer l
+                              reads blob (l - resident_layers) % host_layers; 0 = one per layer */
+  int32_t overlap;         /* 1: prefetch layer l+1 on a copy stream while layer l computes */
+  int64_t max_tokens;      /* rows of the per-call activation workspace (0: default 16384) */
+} fq_policy;
+
+typedef struct fq_model fq_model;
+typedef struct fq_kv fq_kv;
+
+/* fp16 parameters of one layer (device pointers; the library copies or
+ * quantises them, it does not keep the pointers). */
+typedef struct {
+  const uint16_t* w_qkv; /* [3h, h] rows: q features, then k, then v */
+  const uint16_t* w_out; /* [h, h] */
+  const uint16_t* w_fc1; /* [F, h] */
+  const uint16_t* w_fc2; /* [h, F] */
+  const uint16_t* b_qkv; /* [3h] */
+  const uint16_t* b_out; /* [h] */
+  const uint16_t* b_fc1; /* [F] */
+  const uint16_t* b_fc2; /* [h] */
+  const uint16_t* ln1_g;
+  const uint16_t* ln1_b;
+  const uint16_t* ln2_g;
+  const uint16_t* ln2_b;
+} fq_layer_weights;
+
+fq_status fq_model_create(const fq_model_config* cfg, const fq_policy* policy, fq_model** out);
+fq_status fq_model_destroy(fq_model* m);
+
+/* Quantise (or copy) one layer's fp16 parameters into the model's store. */
+fq_status fq_model_set_layer(fq_model* m, int32_t layer, const fq_layer_weights* w, void* stream);
+
+/* Token embedding [V, h], position table [max_pos, h], final LN gamma/beta [h]
+ * (device fp16).  The LM head is tied to the token embedding. */
+fq_status fq_model_set_embeddings(fq_model* m, const uint16_t* embed, const uint16_t* pos,
+                                  const uint16_t* lnf_g, const uint16_t* lnf_b, void* stream);
+
+/* Random initialisation of every parameter on the device from the
+ * counter-based generator SplitMix64 (Steele, Lea, Flood 2014):
+ * element i of stream s is mix64(key(seed, s) + (i+1) * 0x9E3779B97F4A7C15);
+ * its four 16-bit lanes are summed (Irwin-Hall, centred) and scaled in fp32
+ * to std sigma, then rounded to fp16.  Weights: sigma 0.02.  bias_sigma == 0:
+ * biases 0, LN gamma 1, beta 0; otherwise biases/betas sigma bias_sigma and
+ * gammas sigma 1.  Linear weights are then quantised (compress_weight) or
+ * stored fp16 (resident or in pinned host memory).  Synchronous. */
+fq_status fq_model_init_random(fq_model* m, uint64_t seed, double bias_sigma, void* stream);
+
+/* Device view of one layer's packed weight (which: 0 qkv, 1 out, 2 fc1, 3 fc2). */
+fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, int32_t which, fq_packed* out);
+
+/* KV cache for `batch` sequences of up to `capacity` positions, all layers. */
+fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capacity, fq_kv** out);
+fq_status fq_kv_destroy(fq_kv* kv);
+fq_status fq_kv_layer_view(const fq_kv* kv, int32_t layer, fq_kv_layer* out);
+
+/* One decoder layer over T new tokens of sequences b0..b0+B-1 at positions
+ * pos..pos+T-1: LN1, QKV projection (+bias, query scaling), quantise-on-
+ * append of K/V, attention over the packed cache (causal for T > 1), output
+ * projection (+bias, +residual), LN2, FC1 (+bias, ReLU), FC2 (+bias,
+ * +residual).  fp16 storage points as in the header of the oracle's layer.
+ *   x, y: device fp16 [B*T, h] (may be the same buffer).
+ * B*T must not exceed the policy's max_tokens.  Layers whose fp16 weights
+ * live in host memory are copied in synchronously on `stream` first. */
+fq_status fq_layer_step(fq_model* m, int32_t layer, fq_kv* kv, int64_t b0, int64_t B, int64_t T, int64_t pos,
+                        const uint16_t* x, uint16_t* y, void* stream);
+
+/* Generation statistics (README, "Benchmark Results", Metric bullet:
+ * throughput = generated tokens / (prompt time + generation time)). */
+typedef struct {
+  double prefill_s;      /* prompt processing, incl. the first generated token */
+  double decode_s;       /* the remaining gen_len-1 steps */
+  double tokens_per_s;   /* B * gen_len / (prefill_s + decode_s) */
+  double h2d_bytes;      /* weight bytes streamed from host memory */
+  double h2d_s;          /* copy-stream busy time (sum of copy intervals) */
+} fq_gen_stats;
+
+/* Greedy generation: embed the prompt, prefill every layer (prompt chunked
+ * by sequences to fit max_tokens), final LN, LM head (tied embedding, fp32
+ * logits), argmax (ties to the lowest id) gives token 1; then gen_len-1
+ * decode steps.
+ *   prompt_ids: host int32 [B, P];  out_ids: host int32 [B, gen_len]
+ *   kv: a cache with batch >= B and capacity >= P + gen_len - 1
+ *   logits: optional device fp32 [gen_len, B, V] (NULL to skip)
+ * Synchronous: returns after the last token is on the host.  Timing uses
+ * HIP events on `stream`. */
+fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_ids, int64_t B, int64_t P, int64_t gen_len,
+                      int32_t* out_ids, float* logits, fq_gen_stats* stats, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Per-launch device timing (HIP events on the launching stream), grouped by
+ * kernel class, with each launch's algorithmic work: flops of the
+ * contraction and the bytes a single pass over its operands moves to or
+ * from HBM (packed weights 0.5625 B/element, fp16 2 B, fp32 4 B). */
+typedef enum {
+  FQ_KC_GEMM_PREFILL = 0, /* projection GEMMs with M > 256 rows */
+  FQ_KC_GEMM_DECODE = 1,  /* projection GEMMs with M <= 256 rows */
+  FQ_KC_LM_HEAD = 2,      /* fp32-output GEMMs (LM head) */
+  FQ_KC_DECODE_ATTN = 3,
+  FQ_KC_PREFILL_ATTN = 4,
+  FQ_KC_KV_APPEND = 5,
+  FQ_KC_QUANTIZE = 6,
+  FQ_KC_LAYERNORM = 7,
+  FQ_KC_COUNT = 8
+} fq_kernel_class;
+
+typedef struct {
+  int64_t launches;
+  double seconds; /* sum of per-launch device time */
+  double flops;   /* sum of algorithmic flops */
+  double bytes;   /* sum of algorithmic HBM bytes */
+} fq_kernel_stats;
+
+/* Start recording (clears earlier records).  Process-wide. */
+fq_status fq_timing_start(void);
+/* Stop, wait for the recorded events and fill out[FQ_KC_COUNT] (may be NULL). */
+fq_status fq_timing_stop(fq_kernel_stats* out);
+
+/* ------------------------------------------------------------------------ */
+/* Seeded synthetic inputs (the generator described at fq_model_init_random):
+ * fill device fp16 dst[0..n) with elements first..first+n-1 of stream `stream_id`. */
+fq_status fq_synth_normal_f16(uint16_t* dst, int64_t n, uint64_t seed, uint64_t stream_id, int64_t first,
+                              double sigma, void* stream);
+/* Token ids ((u >> 32) * vocab) >> 32 into device int32 dst[0..n). */
+fq_status fq_synth_token_ids(int32_t* dst, int64_t n, uint64_t seed, uint64_t stream_id, int32_t vocab,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

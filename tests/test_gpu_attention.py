@@ -1,0 +1,115 @@
+"""Decode attention (one query per sequence) and causal prefill attention over
+the packed cache, against the oracle's float64 softmax attention on the same
+cache contents.  The GPU fills its cache with its own quantise-on-append from
+the same fp16 K/V (bit-exactness of that step is tested separately)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from tests._util import dev, host, assert_close, log
+
+pytestmark = pytest.mark.gpu
+fq = pytest.importorskip("bit_weight_kv_amd")
+
+
+def _cache(B, H, d, n, cap, seed, b_off=0):
+    """fp16 K/V [B, n, H*d] from the generator -> GPU cache (appended) and oracle cache."""
+    h = H * d
+    k = synth.normal_f16(seed, synth.STREAM["aux"] + 20, (B * n, h), 1.0)
+    v = synth.normal_f16(seed, synth.STREAM["aux"] + 21, (B * n, h), 1.0)
+    kc = torch.zeros((B + b_off, H, cap, d // 2), dtype=torch.uint8, device="cuda:0")
+    km = torch.zeros((B + b_off, H, cap, d // 64, 2), dtype=torch.float16, device="cuda:0")
+    vc, vm = torch.zeros_like(kc), torch.zeros_like(km)
+    view = fq.kv_layer_view(kc, km, vc, vm)
+    kd, vd = dev(k), dev(v)
+    fq.fq_kv_append(view, kd, vd, h, b_off, B, n, 0)
+    torch.cuda.synchronize()
+    to4 = lambda a: np.ascontiguousarray(a.reshape(B, n, H, d).transpose(0, 2, 1, 3))
+    kh = oracle.dequant_f64(*oracle.quantize(to4(k)))
+    vh = oracle.dequant_f64(*oracle.quantize(to4(v)))
+    return view, (kc, km, vc, vm), kh, vh
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("length", [1, 2, 63, 64, 65, 300, 543])
+def test_decode_attention(d, length):
+    B, H = 3, 4
+    log(f"decode attention d={d} len={length}")
+    view, keep, kh, vh = _cache(B, H, d, length, length + 3, seed=d + length, b_off=1)
+    q = (synth.normal_f16(0, synth.STREAM["aux"] + 22, (B, H * d), 1.0).astype(np.float32)
+         * d ** -0.5).astype(np.float16)
+    out = torch.empty((B, H * d), dtype=torch.float16, device="cuda:0")
+    fq.fq_decode_attention(dev(q), view, 1, B, length, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention_decode(q.reshape(B, H, d), kh, vh).reshape(B, H * d)
+    assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"decode d={d} len={length}")
+
+
+def test_decode_attention_long_and_peaked():
+    """A long cache (4000 positions) and a query aligned with one key (peaked softmax)."""
+    B, H, d, n = 2, 2, 128, 4000
+    view, keep, kh, vh = _cache(B, H, d, n, n, seed=9)
+    q = np.zeros((B, H, d), np.float16)
+    q[:, :, :] = (kh[:, :, 1234, :] * 0.3).astype(np.float16)
+    out = torch.empty((B, H * d), dtype=torch.float16, device="cuda:0")
+    fq.fq_decode_attention(dev(q.reshape(B, H * d)), view, 0, B, n, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention_decode(q, kh, vh).reshape(B, H * d)
+    assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what="long/peaked")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T,pos", [(1, 0), (5, 0), (64, 0), (65, 0), (130, 0), (9, 7)])
+def test_prefill_attention_causal(d, T, pos):
+    B, H = 2, 3
+    log(f"prefill attention d={d} T={T} pos={pos}")
+    n = pos + T
+    view, keep, kh, vh = _cache(B, H, d, n, n + 1, seed=T + pos)
+    q = (synth.normal_f16(1, synth.STREAM["aux"] + 23, (B * T, H * d), 1.0).astype(np.float32)
+         * d ** -0.5).astype(np.float16)
+    out = torch.empty((B * T, H * d), dtype=torch.float16, device="cuda:0")
+    fq.fq_prefill_attention(dev(q), view, 0, B, T, pos, out)
+    torch.cuda.synchronize()
+    q4 = q.reshape(B, T, H, d).transpose(0, 2, 1, 3).astype(np.float64)
+    ref = np.empty((B, H, T, d))
+    for t in range(T):
+        ref[:, :, t] = oracle.attention_decode(q4[:, :, t], kh[:, :, :pos + t + 1], vh[:, :, :pos + t + 1])
+    ref = ref.transpose(0, 2, 1, 3).reshape(B * T, H * d)
+    assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill d={d} T={T} pos={pos}")
+
+
+def test_decode_full_size_sampled():
+    """OPT-175B shape at decode: batch 144, 96 heads x 128, 543 cached positions;
+    the cache is filled for all sequences, sampled (b, h) pairs are checked."""
+    B, H, d, n = 144, 96, 128, 543
+    h = H * d
+    log("decode attention full-size")
+    kc = torch.empty((B, H, n, d // 2), dtype=torch.uint8, device="cuda:0")
+    km = torch.empty((B, H, n, d // 64, 2), dtype=torch.float16, device="cuda:0")
+    vc, vm = torch.empty_like(kc), torch.empty_like(km)
+    view = fq.kv_layer_view(kc, km, vc, vm)
+    chunk = 16
+    kbuf = torch.empty((chunk * n, h), dtype=torch.float16, device="cuda:0")
+    vbuf = torch.empty_like(kbuf)
+    for b0 in range(0, B, chunk):
+        fq.fq_synth_normal_f16(kbuf, 5, synth.STREAM["aux"] + 30, 1.0, first=b0 * n * h)
+        fq.fq_synth_normal_f16(vbuf, 5, synth.STREAM["aux"] + 31, 1.0, first=b0 * n * h)
+        fq.fq_kv_append(view, kbuf, vbuf, h, b0, chunk, n, 0)
+    qd = torch.empty((B, h), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(qd, 5, synth.STREAM["aux"] + 32, 1.0 / d ** 0.5)
+    out = torch.empty((B, h), dtype=torch.float16, device="cuda:0")
+    fq.fq_decode_attention(qd, view, 0, B, n, out)
+    torch.cuda.synchronize()
+    for b, hh in ((0, 0), (77, 41), (143, 95)):
+        base = (b * n + np.arange(n))[:, None] * h + hh * d + np.arange(d)[None]
+        k = synth.normal_f16(5, synth.STREAM["aux"] + 30, sigma=1.0, index=base.astype(np.uint64).ravel()).reshape(n, d)
+        v = synth.normal_f16(5, synth.STREAM["aux"] + 31, sigma=1.0, index=base.astype(np.uint64).ravel()).reshape(n, d)
+        qi = (b * h + hh * d + np.arange(d)).astype(np.uint64)
+        q = synth.normal_f16(5, synth.STREAM["aux"] + 32, sigma=1.0 / d ** 0.5, index=qi)
+        kh = oracle.dequant_f64(*oracle.quantize(k))[None, None]
+        vh = oracle.dequant_f64(*oracle.quantize(v))[None, None]
+        ref = oracle.attention_decode(q[None, None], kh, vh)[0, 0]
+        got = host(out[b, hh * d:(hh + 1) * d])
+        assert_close(got, ref, rel=2e-3, abs_=4e-3, what=f"full-size b={b} h={hh}")

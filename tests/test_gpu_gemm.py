@@ -1,0 +1,149 @@
+"""Dequant-fused GEMM (4-bit and fp16 weights, every epilogue) against the
+oracle's float64 GEMM on the reconstructed weights."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth.gen import layer_stream
+import oracle
+from tests._util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+fq = pytest.importorskip("bit_weight_kv_amd")
+
+
+def _tol_check(got, ref64, what):
+    """fp16 output of an fp32-accumulated GEMM: within one fp16 rounding plus
+    a small accumulation error of the float64 value."""
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref64)
+    bound = np.abs(ref64) * 2.0 ** -11 + 2e-3 * (np.abs(ref64).max() + 1e-3) * 1e-2 + 1e-6
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} beyond bound, max err {err.max():.3e}"
+
+
+def _run(M, N, K, flags, packed=True, seed=0, qcols=0, f32out=False):
+    a = synth.normal_f16(seed, synth.STREAM["aux"] + 1, (M, K), 1.0)
+    w = synth.normal_f16(seed, synth.STREAM["aux"] + 2, (N, K), 0.02)
+    b = synth.normal_f16(seed, synth.STREAM["aux"] + 3, (N,), 0.1)
+    r = synth.normal_f16(seed, synth.STREAM["aux"] + 4, (M, N), 1.0)
+    if packed:
+        c, m = oracle.quantize(w)
+        wref = oracle.dequant_f16(c, m)
+        W = fq.weight_packed(dev(c), dev(m), N, K)
+        keep = (W,)
+    else:
+        wref = w
+        wd = dev(w)
+        W = fq.weight_f16(wd)
+        keep = (wd,)
+    out = torch.empty((M, N), dtype=torch.float32 if f32out else torch.float16, device="cuda:0")
+    ad, bd, rd = dev(a), dev(b), dev(r)
+    if f32out:
+        flags |= fq.FQ_EPI_F32OUT
+    fq.fq_dequant_gemm(ad, W, out, bias=bd, residual=rd, epilogue=flags, qscale=0.125, qscale_cols=qcols)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(a, wref, b if flags & fq.FQ_EPI_BIAS else None)
+    if flags & fq.FQ_EPI_QSCALE:
+        ref[:, :qcols] *= 0.125
+    if flags & fq.FQ_EPI_RELU:
+        ref = np.maximum(ref, 0)
+    if flags & fq.FQ_EPI_RESIDUAL:
+        ref = ref + r.astype(np.float64)
+    del keep
+    return host(out), ref
+
+
+@pytest.mark.parametrize("M", [1, 8, 37, 64, 144, 300])
+@pytest.mark.parametrize("N,K", [(64, 256), (200, 1024), (768, 256)])
+def test_gemm_packed_shapes(M, N, K):
+    log(f"gemm packed M={M} N={N} K={K}")
+    got, ref = _run(M, N, K, fq.FQ_EPI_BIAS)
+    _tol_check(got, ref, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("flags,qcols", [
+    (fq.FQ_EPI_BIAS | fq.FQ_EPI_QSCALE, 96),
+    (fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU, 0),
+    (fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, 0),
+    (0, 0),
+])
+def test_gemm_epilogues(flags, qcols):
+    for M in (16, 260):
+        got, ref = _run(M, 192, 512, flags, qcols=qcols)
+        _tol_check(got, ref, f"flags={flags} M={M}")
+
+
+@pytest.mark.parametrize("M", [3, 144, 257])
+def test_gemm_fp16_weight_and_f32_out(M):
+    got, ref = _run(M, 328, 256, fq.FQ_EPI_BIAS, packed=False, f32out=True)
+    err = np.abs(got - ref)
+    assert err.max() <= 1e-5 * (np.abs(ref).max() + 1), err.max()
+    got, ref = _run(M, 328, 256, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, packed=False)
+    _tol_check(got, ref, "fp16 weight")
+
+
+def test_gemm_grid_exact_weight_equals_plain_fp16_gemm():
+    """Weights on their own 4-bit grid: the packed GEMM and the fp16-weight GEMM
+    must give identical results (same accumulation order, same inputs)."""
+    rng = np.random.default_rng(0)
+    N, K, M = 128, 512, 70
+    codes = rng.integers(0, 16, (N, K))
+    codes[:, ::64] = 0
+    codes[:, 1::64] = 15
+    mn = -rng.integers(1, 16, (N, K // 64)) / 8.0
+    s = 2.0 ** -rng.integers(3, 7, (N, K // 64))
+    w = (mn.repeat(64, 1) + codes * s.repeat(64, 1)).astype(np.float16)
+    c, m = oracle.quantize(w)
+    assert np.array_equal(oracle.dequant_f16(c, m), w)
+    a = synth.normal_f16(0, 5, (M, K), 1.0)
+    outp = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    outf = torch.empty_like(outp)
+    ad, wd, cd, md = dev(a), dev(w), dev(c), dev(m)
+    fq.fq_dequant_gemm(ad, fq.weight_packed(cd, md, N, K), outp, epilogue=fq.FQ_EPI_F32OUT)
+    fq.fq_dequant_gemm(ad, fq.weight_f16(wd), outf, epilogue=fq.FQ_EPI_F32OUT)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, outf)
+
+
+def test_gemm_empty_m_is_noop():
+    W = fq.weight_f16(torch.zeros((64, 64), dtype=torch.float16, device="cuda:0"))
+    out = torch.full((1, 64), 7.0, dtype=torch.float16, device="cuda:0")
+    a = torch.zeros((1, 64), dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(a[:0], W, out[:0])
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+@pytest.mark.parametrize("M,which", [(144, "w_qkv"), (144, "w_fc2"), (8192, "w_fc1")])
+def test_gemm_full_size_sampled(M, which):
+    """OPT-175B projection shapes (h = 12288, F = 49152) in the launch
+    configuration of the decode (M = 144) and prefill-chunk (M = 8192) steps;
+    weights generated on the GPU and quantised there; sampled outputs against
+    float64 dot products of the oracle's reconstruction of the same rows."""
+    h, F = 12288, 49152
+    N, K = {"w_qkv": (3 * h, h), "w_fc2": (h, F), "w_fc1": (F, h)}[which]
+    log(f"gemm full-size M={M} N={N} K={K}")
+    sw = layer_stream(3, which)
+    w = torch.empty((N, K), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(w, 0, sw, 0.02)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda:0")
+    meta = torch.empty((N, K // 64, 2), dtype=torch.float16, device="cuda:0")
+    fq.fq_quantize(w, codes, meta)
+    del w
+    a = torch.empty((M, K), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(a, 0, synth.STREAM["hidden"], 1.0)
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(a, fq.weight_packed(codes, meta, N, K), out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 10)]))
+    ai = (rows[:, None] * K + np.arange(K)[None]).astype(np.uint64).ravel()
+    wi = (cols[:, None] * K + np.arange(K)[None]).astype(np.uint64).ravel()
+    arows = synth.normal_f16(0, synth.STREAM["hidden"], sigma=1.0, index=ai).reshape(len(rows), K)
+    wrows = synth.normal_f16(0, sw, sigma=0.02, index=wi).reshape(len(cols), K)
+    ref = oracle.gemm(arows, oracle.dequant_f16(*oracle.quantize(wrows)))
+    got = host(out[torch.as_tensor(rows, device="cuda:0")][:, torch.as_tensor(cols, device="cuda:0")])
+    _tol_check(got, ref, f"{which} M={M}")

@@ -1,0 +1,106 @@
+"""fq_layer_step (prefill + decode of one OPT-style layer) against the oracle:
+the tiny configuration in full, the OPT-6.7B-shaped layer on sampled
+sequences, and the packed weights bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from oracle import LayerConfig
+from tests._util import dev, host, bits16, assert_close, log
+
+pytestmark = pytest.mark.gpu
+fq = pytest.importorskip("bit_weight_kv_amd")
+
+NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2", "b_qkv", "b_out", "b_fc1", "b_fc2",
+         "ln1_g", "ln1_b", "ln2_g", "ln2_b")
+
+
+def _check_packed(model, layer, params, cfg):
+    for i, name in enumerate(("w_qkv", "w_out", "w_fc1", "w_fc2")):
+        p = model.packed_weight(layer, i)
+        n, k = p.rows, p.cols
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda:0")
+        meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device="cuda:0")
+        torch.cuda.synchronize()
+        _copy_dev(codes.data_ptr(), p.codes, n * k // 2)
+        _copy_dev(meta.data_ptr(), p.meta, n * (k // 64) * 4)
+        rc, rm = oracle.quantize(params[name], cfg.group)
+        assert np.array_equal(host(codes), rc), name
+        assert np.array_equal(bits16(host(meta)), bits16(rm)), name
+
+
+def _copy_dev(dst, src, nbytes):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    assert hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), ctypes.c_size_t(nbytes), 3) == 0
+
+
+def _layer_case(cfg, B, P, T, seed, bias_sigma, check_seqs=None, chunk=None, via_init=False):
+    h = cfg.hidden
+    model = fq.Model(h, cfg.heads, cfg.ffn, 1, max_tokens=max(B * P if chunk is None else chunk * P, B))
+    params = oracle.layer_params(seed, cfg, 0, bias_sigma)
+    if via_init:
+        model.init_random(seed, bias_sigma)
+    else:
+        model.set_layer(0, {n: dev(params[n]) for n in NAMES})
+    torch.cuda.synchronize()
+    _check_packed(model, 0, params, cfg)
+    kv = fq.KVCache(model, B, P + T)
+    hidden = synth.normal_f16(seed, synth.STREAM["hidden"], (B, P + T, h), 1.0)
+    hd = dev(hidden)
+    x = hd[:, :P].reshape(B * P, h).contiguous()
+    y = torch.empty_like(x)
+    cs = B if chunk is None else chunk
+    for b0 in range(0, B, cs):
+        nb = min(cs, B - b0)
+        fq.fq_layer_step(model, 0, kv, b0, nb, P, 0, x[b0 * P:(b0 + nb) * P], y[b0 * P:(b0 + nb) * P])
+    ys = [host(y).reshape(B, P, h)]
+    for t in range(T):
+        xt = hd[:, P + t].contiguous()
+        yt = torch.empty_like(xt)
+        fq.fq_layer_step(model, 0, kv, 0, B, 1, P + t, xt, yt)
+        ys.append(host(yt).reshape(B, 1, h))
+    torch.cuda.synchronize()
+    # oracle on the checked sequences
+    seqs = list(range(B)) if check_seqs is None else check_seqs
+    packed = oracle.pack_layer(params, cfg)
+    for b in seqs:
+        cache = oracle.new_cache(cfg, 1, P + T)
+        r = oracle.layer_step(hidden[b:b + 1, :P], params, packed, cache, cfg, 0)
+        assert_close(ys[0][b], r["y64"][0], what=f"prefill seq {b}")
+        for t in range(T):
+            r = oracle.layer_step(hidden[b:b + 1, P + t:P + t + 1], params, packed, cache, cfg, P + t)
+            assert_close(ys[1 + t][b], r["y64"][0], what=f"decode step {t} seq {b}")
+    kv.close()
+    model.close()
+
+
+@pytest.mark.parametrize("bias_sigma", [0.0, 0.02])
+def test_layer_tiny_config_full(bias_sigma):
+    """hidden 256, 4 heads x 64, FFN 1024, batch 8, prompt 64, 4 decode steps, seed 0."""
+    log(f"layer tiny bias_sigma={bias_sigma}")
+    _layer_case(LayerConfig(256, 4, 1024), B=8, P=64, T=4, seed=0, bias_sigma=bias_sigma)
+
+
+def test_layer_tiny_via_device_init():
+    """Same layer with weights generated and quantised on the GPU."""
+    _layer_case(LayerConfig(256, 4, 1024), B=8, P=64, T=4, seed=0, bias_sigma=0.0, via_init=True)
+
+
+def test_layer_ragged_shapes():
+    """head_dim 128, prompt not a multiple of the 64-query tile, odd batch, prefill in chunks."""
+    log("layer ragged")
+    _layer_case(LayerConfig(512, 4, 1536), B=5, P=70, T=3, seed=3, bias_sigma=0.02, chunk=2)
+
+
+@pytest.mark.slow
+def test_layer_opt67b_shape_sampled():
+    """One OPT-6.7B-shaped layer (hidden 4096, 32 x 128, FFN 16384), batch 64,
+    prompt 512, 32 decode steps; every sequence runs on the GPU, sequences
+    0 and 45 are checked against the oracle at every position."""
+    log("layer OPT-6.7B shape")
+    _layer_case(LayerConfig(4096, 32, 16384), B=64, P=512, T=32, seed=0, bias_sigma=0.0,
+                check_seqs=[0, 45], chunk=16, via_init=True)
