@@ -1,0 +1,252 @@
+"""Benchmark: generation throughput of the 4-bit weight + 4-bit KV-cache path.
+
+Metric (FlexGen README, "Benchmark Results", Metric bullet): generated tokens
+/ (prompt time + generation time), prompt 512, output 32.  One step = one
+full pass of the path over one batch: prefill of every prompt through every
+layer, then 31 decode steps (quantise-on-append, dequant-fused GEMMs, packed
+KV attention, LM head, greedy argmax).  Inputs are synthetic and already in
+HBM (weights generated and quantised on the device, prompt ids from the
+seeded generator) before the timed region starts.
+
+Default workload: the OPT-175B shape (96 layers, hidden 12288, 96 heads x 128,
+FFN 49152, vocab 50272) with 4-bit group-64 weights and 4-bit KV resident on
+one MI355X, batch 144, prompt 512, gen 32 -- the configuration of the pages'
+"FlexGen with Compression" OPT-175B figure (effective batch 144).
+
+Prints one JSON line.  Also measures, live over the timed region, the
+per-launch device time of every kernel class (HIP events on the launching
+stream) and reports the dominant kernel against its roofline, and times the
+CPU oracle on a bounded sample of the same workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+CONFIGS = {
+    # name: (hidden, heads, ffn, layers, vocab, batch, prompt, gen, compress_weight, streaming knobs)
+    "opt175b-4bit": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=144, prompt=512, gen=32,
+                         compress_weight=True, desc="OPT-175B shape, 4-bit g64 weights + 4-bit KV resident in HBM"),
+    "opt30b-4bit": dict(hidden=7168, heads=56, ffn=28672, layers=48, vocab=50272, batch=256, prompt=512, gen=32,
+                        compress_weight=True, desc="OPT-30B shape, 4-bit g64 weights + 4-bit KV resident in HBM"),
+    "opt175b-fp16-streamed": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=256, prompt=512,
+                                  gen=32, compress_weight=False, resident_layers=0, host_layers=48,
+                                  desc="OPT-175B shape, fp16 weights streamed layer by layer from pinned host memory "
+                                       "(48 distinct host layer blobs, layer l reads blob l mod 48), 4-bit KV"),
+    "tiny-2layer": dict(hidden=256, heads=4, ffn=1024, layers=2, vocab=512, batch=8, prompt=64, gen=5,
+                        compress_weight=True, desc="tiny OPT-style model for smoke benchmarking"),
+}
+METRIC = "generation tokens/s (prompt 512, gen 32) at batch 144-256; % HBM/MFMA roofline"
+PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak (published)
+PAGES_T4_TOKS = {"opt175b-4bit": 1.12}  # FlexGen with Compression, OPT-175B, T4 (context, other hardware)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="opt175b-4bit", choices=sorted(CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--max-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true", help="time only the oracle sample (no GPU)")
+    return ap.parse_args()
+
+
+def roofline(kstats):
+    """Dominant kernel class by device time, against its own roofline."""
+    name, st = max(kstats.items(), key=lambda kv: kv[1]["seconds"])
+    if st["seconds"] <= 0:
+        return None, {}
+    per_launch_s = st["seconds"] / st["launches"]
+    if name.startswith("gemm") or name == "lm_head":
+        achieved = st["flops"] / st["seconds"] / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = st["bytes"] / st["seconds"] / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    r["kernel"] = name
+    r["launches"] = st["launches"]
+    r["avg_launch_ms"] = round(per_launch_s * 1e3, 4)
+    r["work_per_launch"] = (st["flops"] if r["bound"] == "mfma" else st["bytes"]) / st["launches"]
+    return name, r
+
+
+def kernel_table(kstats):
+    out = {}
+    for name, st in kstats.items():
+        if st["launches"] == 0:
+            continue
+        e = {"launches": st["launches"], "seconds": round(st["seconds"], 4),
+             "avg_launch_ms": round(st["seconds"] / st["launches"] * 1e3, 4)}
+        if st["flops"] > 0:
+            e["tflops"] = round(st["flops"] / st["seconds"] / 1e12, 2)
+            e["mfma_frac"] = round(st["flops"] / st["seconds"] / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)
+        if st["bytes"] > 0:
+            e["gbs"] = round(st["bytes"] / st["seconds"] / 1e9, 1)
+            e["hbm_frac"] = round(st["bytes"] / st["seconds"] / 1e9 / PEAK_HBM_GBS, 4)
+        out[name] = e
+    return out
+
+
+def cpu_baseline(cfg, seed):
+    """The CPU oracle on a bounded sample of the same workload: one sequence
+    through one layer of this shape -- prefill of the 512-token prompt, then the
+    31 decode steps -- timed on the host cores, scaled to the full workload
+    (every layer and sequence costs the same): tokens/s = gen / (t * layers)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import synth
+    from synth.gen import layer_stream
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    h, H, F = cfg["hidden"], cfg["heads"], cfg["ffn"]
+    lcfg = oracle.LayerConfig(h, H, F, compress_weight=cfg["compress_weight"])
+    workers = os.cpu_count() or 1
+    t0 = time.time()
+
+    def gen(name, shape, sigma):
+        n = int(np.prod(shape))
+        out = np.empty(n, np.float16)
+        step = max(1 << 22, n // (4 * workers) + 1)
+
+        def part(s):
+            e = min(n, s + step)
+            out[s:e] = synth.normal_f16(seed, layer_stream(0, name), sigma=sigma,
+                                        index=np.arange(s, e, dtype=np.uint64))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(part, range(0, n, step)))
+        return out.reshape(shape)
+
+    params = {"w_qkv": gen("w_qkv", (3 * h, h), 0.02), "w_out": gen("w_out", (h, h), 0.02),
+              "w_fc1": gen("w_fc1", (F, h), 0.02), "w_fc2": gen("w_fc2", (h, F), 0.02)}
+    for name, n in (("b_qkv", 3 * h), ("b_out", h), ("b_fc1", F), ("b_fc2", h)):
+        params[name] = np.zeros(n, np.float16)
+    for name in ("ln1_g", "ln2_g"):
+        params[name] = np.ones(h, np.float16)
+    for name in ("ln1_b", "ln2_b"):
+        params[name] = np.zeros(h, np.float16)
+    # load-time weight packing (not part of the metric), row blocks in parallel
+    packed = {}
+    for name in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+        w = params[name]
+        if not lcfg.compress_weight:
+            packed[name] = w.astype(np.float64)
+            continue
+        out = np.empty(w.shape, np.float64)
+        rows = max(64, w.shape[0] // (4 * workers))
+
+        def part(r0, w=w, out=out):
+            c, m = oracle.quantize(w[r0:r0 + rows])
+            out[r0:r0 + rows] = oracle.dequant_f16(c, m)
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(part, range(0, w.shape[0], rows)))
+        packed[name] = out
+    setup_s = time.time() - t0
+    P, G = cfg["prompt"], cfg["gen"]
+    x = synth.normal_f16(seed, synth.STREAM["hidden"], (1, P + G - 1, h), 1.0)
+    cache = oracle.new_cache(lcfg, 1, P + G)
+    t1 = time.time()
+    oracle.layer_step(x[:, :P], params, packed, cache, lcfg, 0)
+    for t in range(G - 1):
+        oracle.layer_step(x[:, P + t:P + t + 1], params, packed, cache, lcfg, P + t)
+    t_sample = time.time() - t1
+    value = G / (t_sample * cfg["layers"])
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"1 sequence x 1 layer of the {cfg['desc']} shape: prefill of {P} tokens + {G - 1} decode "
+                      f"steps, {t_sample:.1f} s on the host; scaled by {cfg['layers']} layers x batch "
+                      f"(sequences and layers cost the same) to tokens/s = gen/(t*layers); weight generation and "
+                      f"packing ({setup_s:.0f} s, load-time) not timed",
+            "sample_seconds": round(t_sample, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the batch dimension would shard over "
+              f"GPUs with no exchange, which this build does not launch.", file=sys.stderr)
+        sys.exit(2)
+    cfg = CONFIGS[args.config]
+    if args.cpu_baseline_only:
+        print(json.dumps({"cpu_baseline": cpu_baseline(cfg, args.seed)}))
+        return
+    import numpy as np
+    import torch
+
+    import bit_weight_kv_amd as fq
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B, P, G = cfg["batch"], cfg["prompt"], cfg["gen"]
+    t0 = time.time()
+    model = fq.Model(cfg["hidden"], cfg["heads"], cfg["ffn"], cfg["layers"], vocab=cfg["vocab"], max_pos=P + G + 2,
+                     compress_weight=cfg["compress_weight"], resident_layers=cfg.get("resident_layers", -1),
+                     host_layers=cfg.get("host_layers", 0), overlap=True, max_tokens=args.max_tokens)
+    model.init_random(args.seed)
+    kv = fq.KVCache(model, B, P + G)
+    ids = synth.token_ids(args.seed, synth.STREAM["prompt"], (B, P), cfg["vocab"])
+    torch.cuda.synchronize()
+    log(f"[bench] {args.config}: model + cache ready in {time.time() - t0:.1f} s")
+    for w in range(args.warmup):
+        out, st = fq.fq_generate(model, kv, ids, G)
+        log(f"[bench] warmup {w}: {st.tokens_per_s:.2f} tok/s (prefill {st.prefill_s:.2f} s, decode {st.decode_s:.2f} s)")
+    torch.cuda.synchronize()
+    fq.fq_timing_start()
+    stats = []
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        out, st = fq.fq_generate(model, kv, ids, G)
+        stats.append((st.prefill_s, st.decode_s, st.h2d_bytes, st.h2d_s))
+        log(f"[bench] step {s}: {st.tokens_per_s:.2f} tok/s (prefill {st.prefill_s:.2f} s, decode {st.decode_s:.2f} s)")
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    kstats = fq.fq_timing_stop()
+    ms_per_step = t_total / args.steps * 1e3
+    value = B * G * args.steps / t_total
+    _, roof = roofline(kstats)
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 1), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": (round(value / PAGES_T4_TOKS[args.config], 1) if args.config in PAGES_T4_TOKS else None),
+        "dtype": "f16", "data": "synthetic (seeded random-init weights and uniform prompt ids)",
+        "config": {"workload": cfg["desc"], "config": args.config, "layers": cfg["layers"], "hidden": cfg["hidden"],
+                   "heads": cfg["heads"], "ffn": cfg["ffn"], "vocab": cfg["vocab"], "global_batch": B,
+                   "prompt": P, "gen": G, "group": 64, "parallelism": "single GPU"},
+        "phases": {"prefill_s": round(float(np.mean([s[0] for s in stats])), 3),
+                   "decode_s": round(float(np.mean([s[1] for s in stats])), 3),
+                   "h2d_GB": round(float(np.mean([s[2] for s in stats])) / 1e9, 2),
+                   "h2d_busy_s": round(float(np.mean([s[3] for s in stats])), 3)},
+        "roofline": roof,
+        "kernels": kernel_table(kstats),
+    }
+    kv.close()
+    model.close()
+    del kv, model
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle sample")
+        res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

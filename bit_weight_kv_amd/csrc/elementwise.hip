@@ -123,7 +123,12 @@ __global__ __launch_bounds__(256) void synth_normal_kernel(uint16_t* __restrict_
   if (i >= n) return;
   const uint64_t u = mix64(key + (uint64_t)(first + i + 1) * kGamma);
   const int32_t lane_sum = (int32_t)((u & 0xFFFF) + ((u >> 16) & 0xFFFF) + ((u >> 32) & 0xFFFF) + (u >> 48)) - 131070;
-  dst[i] = f2h((float)lane_sum * scale);
+  float prod = (float)lane_sum * scale;
+  // The generator is defined as an fp32 product rounded to fp16 (two
+  // roundings); keep the compiler from fusing the two into one mixed-
+  // precision multiply with a single rounding.
+  asm volatile("" : "+v"(prod));
+  dst[i] = f2h(prod);
 }
 
 __global__ __launch_bounds__(256) void synth_ids_kernel(int32_t* __restrict__ dst, int64_t n, uint64_t key,

@@ -83,16 +83,18 @@ def layer_params(seed: int, cfg: LayerConfig, layer: int, bias_sigma: float = 0.
 
 def pack_layer(params: dict, cfg: LayerConfig) -> dict:
     """Linear weights as used by the GEMMs: dequant_f16(quantize(W)) when weights are
-    compressed, else W itself.  Also returns the packed codes/meta."""
+    compressed, else W itself -- held as float64 (exact copies of the fp16 values)
+    so that every GEMM reads them without a conversion.  Also returns the packed
+    codes/meta."""
     out = {}
     for name in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
         w = params[name]
         if cfg.compress_weight:
             codes, meta = quantize(w, cfg.group)
-            out[name] = dequant_f16(codes, meta, cfg.group)
+            out[name] = dequant_f16(codes, meta, cfg.group).astype(np.float64)
             out[name + ".codes"], out[name + ".meta"] = codes, meta
         else:
-            out[name] = w
+            out[name] = w.astype(np.float64)
     return out
 
 

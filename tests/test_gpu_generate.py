@@ -73,7 +73,9 @@ def test_streamed_fp16_weights_equal_resident():
     assert np.array_equal(a_out, c_out) and np.array_equal(a_lg, c_lg)
     layer_bytes = (4 * H * H + 2 * H * F) * 2
     assert a_st.h2d_bytes == 0
-    assert b_st.h2d_bytes == 3 * layer_bytes * G and b_st.h2d_s > 0
+    # streamed layers 1, 2, 3 use staging slots 1, 0, 1: the first pass copies all
+    # three, later passes find layer 2 still staged in slot 0 and copy two
+    assert b_st.h2d_bytes == (3 + 2 * (G - 1)) * layer_bytes and b_st.h2d_s > 0
 
 
 def test_streamed_shared_host_blobs_match_oracle():

@@ -25,7 +25,9 @@ def _gpu_quant(x16_dev):
 
 
 def test_synth_generator_matches_numpy():
-    for sigma, n, first in ((0.02, 100_003, 0), (1.0, 4096, 12345)):
+    # 4M elements per sigma: a double- versus single-rounding difference in the
+    # fp32 product -> fp16 step shows up about once per 30k elements
+    for sigma, n, first in ((0.02, 4_000_003, 0), (1.0, 4_000_000, 12345)):
         d = torch.empty(n, dtype=torch.float16, device="cuda:0")
         fq.fq_synth_normal_f16(d, 7, 99, sigma, first=first)
         ref = synth.normal_f16(7, 99, sigma=sigma, index=np.arange(first, first + n, dtype=np.uint64))
