@@ -22,6 +22,9 @@
 // with its own L2), so one XCD's L2 serves all re-reads of a weight tile.
 // Split-K (grid.z) writes fp32 partials that a second kernel reduces and
 // passes through the epilogue; used when the M x N grid cannot fill 256 CUs.
+#include <cstdlib>
+#include <type_traits>
+
 #include "common.h"
 
 namespace fq {
@@ -236,6 +239,263 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   }
 }
 
+// ---- large-M kernel ---------------------------------------------------------
+// 256 x 128 block tile, 4 waves in 2 x 2, each wave 128 x 64 (8 x 4 MFMA
+// 16x16x32 tiles, fp32 accumulators in AGPRs).  K step 64.
+//   * Every global operand moves with direct global -> LDS copies
+//     (global_load_lds, 16 bytes per lane, one wave instruction fills 1 KiB of
+//     LDS: lane l -> byte 16 l), so the loop never waits on a VGPR load.
+//   * A (and fp16 B) tiles: a wave instruction covers 8 rows x 8 16-byte
+//     chunks; each lane fetches global chunk c ^ swz(r) of its row so LDS slot
+//     (r, c) holds chunk c ^ swz(r) (conflict-free fragment reads).
+//   * Packed B: the K step's codes (128 rows x 32 B) and {min, scale} land in
+//     one of three code slots; between the MFMAs each thread reconstructs
+//     16 code bytes of one row (two threads per row) into the fp16 B stage.
+//   * Three LDS stages; iteration kt multiplies stage kt, reconstructs the
+//     codes of step kt+2 into stage kt+2, and issues step kt+3's codes and
+//     stage kt+2's A copies; the wait before the single barrier leaves only
+//     this iteration's A (and fp16 B) copies in flight.
+// Rows beyond M (and weight rows beyond N) are clamped to the last valid row:
+// they are read but never stored.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* gbl_void_ptr;
+
+// LDS chunk swizzle.  Measured with the LDS bank-conflict counter on gfx950:
+// chunk c ^ (r & 7) is conflict-free both for the MFMA fragment reads (lane l
+// reads row l & 15, chunk l >> 4) and for the reconstructed-weight stores
+// (lane l writes row l >> 1, chunk (l & 1) * 4 + q), whereas 144-byte padded
+// rows cost ~30 % extra LDS cycles on the reads.
+__device__ inline int swz(int r) { return r & 7; }
+
+template <bool PACKED>
+__global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
+                                                       const uint8_t* __restrict__ codes,
+                                                       const uint16_t* __restrict__ meta,
+                                                       const uint16_t* __restrict__ w16, int64_t N, int64_t K,
+                                                       Epilogue epi) {
+  constexpr int BMx = 256, BNx = 128, TM = 128, TN = 64, FM = 8, FN = 4;
+  constexpr int ROWB = BK * 2;                  // bytes per staged row (128)
+  constexpr int A_BYTES = BMx * ROWB;           // 32 KiB per stage
+  constexpr int B_BYTES = BNx * ROWB;           // 16 KiB per stage
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int CODE_BYTES = BNx * 32 + BNx * 4;  // packed codes + {min, scale} of one K step
+  constexpr int CODE_SLOTS = PACKED ? 3 : 0;
+  constexpr int VM_ISSUE = PACKED ? 8 : 12;     // copies per wave per stage (A, plus fp16 B)
+  // One LDS object per stage and per operand.  The compiler's wait insertion
+  // tracks direct-to-LDS copies per object: an access to an object with no
+  // copy in flight needs no wait, while any access to an object with one
+  // does.  With the loop unrolled by three every stage is a compile-time
+  // object, so reading stage kt never waits for the copies into stage kt+2.
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[A_BYTES], a_lds1[A_BYTES], a_lds2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b_lds0[B_BYTES], b_lds1[B_BYTES], b_lds2[B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t c_lds0[PACKED ? CODE_BYTES : 16], c_lds1[PACKED ? CODE_BYTES : 16],
+      c_lds2[PACKED ? CODE_BYTES : 16];
+  auto a_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? a_lds0 : S == 1 ? a_lds1 : a_lds2;
+  };
+  auto b_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? b_lds0 : S == 1 ? b_lds1 : b_lds2;
+  };
+  auto c_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? c_lds0 : S == 1 ? c_lds1 : c_lds2;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-aware, grouped tile order: the 32 blocks an XCD runs at once cover
+  // 8 M tiles x 4 N tiles, so A and B tiles are re-read from that XCD's L2.
+  // (Tile ids are only remapped within the first 8*floor(n/8) blocks.)
+  const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
+  const int64_t nblk = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  int64_t lid = bid;
+  {
+    const int64_t per_xcd = nblk / 8;
+    if (bid < per_xcd * 8) lid = (bid % 8) * per_xcd + bid / 8;
+  }
+  constexpr int GM = 8;
+  const int64_t group = lid / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t gsize = min((int64_t)GM, tiles_m - first_m);
+  const int64_t in_group = lid - group * GM * tiles_n;
+  const int64_t mt = first_m + in_group % gsize;
+  const int64_t nt = in_group / gsize;
+  const int64_t m0 = mt * BMx, n0 = nt * BNx;
+  const int KT = (int)(K / BK);
+
+  // direct copies of 8-row x 128-byte blocks: lane -> (row, chunk)
+  const int cp_r = lane >> 3, cp_c = lane & 7;
+  const uint16_t* a_src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (4 * i + wave) + cp_r;
+    const int64_t m = min(m0 + r, M - 1);
+    a_src[i] = A + m * lda + (cp_c ^ swz(r)) * 8;
+  }
+  const uint16_t* b_src[PACKED ? 1 : 4];
+  if (!PACKED) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * (4 * i + wave) + cp_r;
+      const int64_t n = min(n0 + r, N - 1);
+      b_src[i] = w16 + n * K + (cp_c ^ swz(r)) * 8;
+    }
+  }
+  auto issue_stage = [&](auto s, int kt) {
+    uint8_t* dst = a_st(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void_ptr)(a_src[i] + (int64_t)kt * BK),
+                                       (lds_void_ptr)(dst + (4 * i + wave) * 1024), 16, 0, 0);
+    if (!PACKED) {
+      uint8_t* bdst = b_st(s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void_ptr)(b_src[i] + (int64_t)kt * BK),
+                                         (lds_void_ptr)(bdst + (4 * i + wave) * 1024), 16, 0, 0);
+    }
+  };
+  // packed codes of one K step: wave w copies rows 32w..32w+31 (two lanes per
+  // row), waves 0 and 1 also copy the meta of rows 64w..64w+63
+  const int code_r = wave * 32 + (lane >> 1);
+  const uint8_t* code_src = PACKED ? codes + min(n0 + code_r, N - 1) * (K / 2) + (lane & 1) * 16 : nullptr;
+  const uint16_t* meta_src = PACKED ? meta + min(n0 + wave * 64 + lane, N - 1) * (K / 64) * 2 : nullptr;
+  auto issue_codes = [&](auto s, int kt) {
+    uint8_t* dst = c_st(s);
+    __builtin_amdgcn_global_load_lds((gbl_void_ptr)(code_src + (int64_t)kt * 32), (lds_void_ptr)(dst + wave * 1024),
+                                     16, 0, 0);
+    if (wave < 2)
+      __builtin_amdgcn_global_load_lds((gbl_void_ptr)(meta_src + (int64_t)kt * 2),
+                                       (lds_void_ptr)(dst + BNx * 32 + wave * 256), 4, 0, 0);
+  };
+  // reconstruction: thread -> (row, 32-wide k half) of the B tile
+  const int b_row = tid >> 1, b_half = tid & 1;
+  uint4 cw = make_uint4(0, 0, 0, 0);
+  uint32_t cm = 0;
+  auto read_codes = [&](auto s) {
+    const uint8_t* src = c_st(s);
+    cw = *reinterpret_cast<const uint4*>(src + b_row * 32 + b_half * 16);
+    cm = *reinterpret_cast<const uint32_t*>(src + BNx * 32 + b_row * 4);
+  };
+  auto store_b_part = [&](auto s, int q) {
+    uint8_t* dst = b_st(s) + b_row * ROWB;
+    const int c = b_half * 4 + q;
+    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm & 0xFFFF));
+    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm >> 16));
+    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+    const uint32_t w = q == 0 ? cw.x : q == 1 ? cw.y : q == 2 ? cw.z : cw.w;
+    uint32_t o[4];
+    dequant8(w, mn2, s2, o);
+    // Written with an explicit ds_write: the compiler cannot tell this store
+    // from the direct copies in flight and would otherwise wait for all of
+    // them here.  It targets a stage with no copy in flight; the barrier's
+    // lgkmcnt(0) wait completes it before any wave reads the stage.
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = {o[0], o[1], o[2], o[3]};
+    const uint32_t addr = (uint32_t)(uintptr_t)(dst + ((c ^ swz(b_row)) * 16));
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+  };
+
+  float4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  // prologue: stages 0 and 1 complete, step 2's codes in slot 2
+  if (PACKED) {
+    if (KT > 0) issue_codes(I0{}, 0);
+    if (KT > 1) issue_codes(I1{}, 1);
+    if (KT > 2) issue_codes(I2{}, 2);
+  }
+  if (KT > 0) issue_stage(I0{}, 0);
+  if (KT > 1) issue_stage(I1{}, 1);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (PACKED) {
+    if (KT > 0) {
+      read_codes(I0{});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_b_part(I0{}, q);
+    }
+    if (KT > 1) {
+      read_codes(I1{});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_b_part(I1{}, q);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const int fr = lane & 15;      // fragment row within a 16-row block
+  const int fk = lane >> 4;      // 8-element k chunk within a 32-wide k slice
+  // Iteration kt (stage S = kt % 3): reconstruct step kt+2's codes (slot
+  // (S+2)%3) into B stage (S+2)%3 between the MFMAs, issue step kt+3's codes
+  // into slot S and stage kt+2's A copies into A stage (S+2)%3.
+  auto iteration = [&](auto s, int kt) {
+    constexpr int S = decltype(s)::value;
+    using S2 = std::integral_constant<int, (S + 2) % 3>;
+    const bool pre = kt + 2 < KT;
+    if (PACKED) read_codes(S2{});  // stale but harmless when kt+2 >= KT
+    if (PACKED && kt + 3 < KT) issue_codes(s, kt + 3);
+    if (pre) issue_stage(S2{}, kt + 2);
+    const uint8_t* As_ = a_st(s);
+    const uint8_t* Bs_ = b_st(s);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kc = ks * 4 + fk;
+      half8_t bf[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 16 + fr;
+        bf[j] = *reinterpret_cast<const half8_t*>(Bs_ + r * ROWB + ((kc ^ swz(r)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 16 + fr;
+        const half8_t af = *reinterpret_cast<const half8_t*>(As_ + r * ROWB + ((kc ^ swz(r)) * 16));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        // unconditional: once no stage is left to fill this rewrites a stage nobody reads
+        if (PACKED && ks == 1 && (i & 1) == 1) store_b_part(S2{}, i >> 1);
+      }
+    }
+    if (pre) {
+      if (VM_ISSUE == 8)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+  for (int kt = 0; kt < KT; kt += 3) {
+    iteration(I0{}, kt);
+    if (kt + 1 < KT) iteration(I1{}, kt + 1);
+    if (kt + 2 < KT) iteration(I2{}, kt + 2);
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * TM + i * 16 + 4 * (lane >> 4) + r;
+        if (m < M && n < N) epilogue_store(epi, m, n, acc[i][j][r]);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
                                                             int64_t N, Epilogue epi) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -306,6 +566,13 @@ fq_status run_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W
 
 using namespace fq;
 
+// Test hook: FQ_GEMM_SMALL_TILES=1 in the environment routes every GEMM to the
+// 128x128 kernel (lets the tests compare the two large-M kernels).
+static const bool g_small_tiles_only = [] {
+  const char* e = getenv("FQ_GEMM_SMALL_TILES");
+  return e && e[0] == '1';
+}();
+
 extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
                                      const uint16_t* bias, const uint16_t* residual, int64_t ldr, uint32_t epilogue,
                                      float qscale, int64_t qscale_cols, void* C, int64_t ldc, void* stream) {
@@ -345,6 +612,13 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
     const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
+  } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !g_small_tiles_only) {
+    const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 128)));
+    if (W->kind == FQ_WEIGHT_PACKED4)
+      gemm_big_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, nullptr, N, K, epi);
+    else
+      gemm_big_kernel<false><<<grid, dim3(256), 0, st>>>(A, M, lda, nullptr, nullptr, W->w16, N, K, epi);
+    r = launch_check("gemm_big_kernel");
   } else {
     const int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
     const int splits = tiles >= 256 ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / tiles));

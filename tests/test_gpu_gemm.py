@@ -107,6 +107,16 @@ def test_gemm_grid_exact_weight_equals_plain_fp16_gemm():
     assert torch.equal(outp, outf)
 
 
+@pytest.mark.parametrize("packed", [True, False])
+def test_gemm_large_tile_kernel_ragged(packed):
+    """M and N not multiples of the 256 x 128 large-M tile, enough tiles to select it."""
+    log(f"gemm large-tile ragged packed={packed}")
+    got, ref = _run(2100, 3900, 256, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, packed=packed)
+    _tol_check(got, ref, "large tile ragged")
+    got, ref = _run(1030, 32776, 128, fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU, packed=packed)
+    _tol_check(got, ref, "large tile ragged 2")
+
+
 def test_gemm_empty_m_is_noop():
     W = fq.weight_f16(torch.zeros((64, 64), dtype=torch.float16, device="cuda:0"))
     out = torch.full((1, 64), 7.0, dtype=torch.float16, device="cuda:0")
