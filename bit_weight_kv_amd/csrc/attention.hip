@@ -17,6 +17,8 @@
 //      lane), 16 positions are in flight per block; each lane accumulates
 //      sum_j (p_j s_jg) c_ji and sum_j p_j min_jg, then the 16 partial sums
 //      are reduced through LDS.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace fq {
@@ -273,6 +275,215 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* 
   }
 }
 
+// ---- causal prefill on the matrix cores ------------------------------------
+// Work-group = 4 waves x 32 queries of one (b, h); keys in chunks of 64.
+// Per chunk the work-group reconstructs K and V of 64 positions into LDS as
+// fp16 (fp16(min + code * s), one rounding), then each wave computes
+//   S^T = K^ Q^T      (v_mfma_f32_16x16x32_f16; lane owns query lane % 16)
+//   online softmax    (per query, reduced over the 4 lane groups)
+//   O^T += V^T P^T    (P taken straight from the S^T registers)
+// Transposing both products keeps every per-query value (scores, running
+// max/sum, output column) in the lanes of that query, so P never moves.
+// V is stored transposed ([d][position]) with the positions of each 32-wide
+// slice in the order {0-3, 16-19, 4-7, 20-23, ...}: the order in which a lane
+// holds its scores, so the V operand is one 16-byte read per lane.
+// LDS rows are 128 bytes with the 16-byte chunk swizzle c ^ (row & 7).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ km,
+    const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vm, int H, int64_t cap, int64_t b0, int T,
+    int64_t pos, uint16_t* __restrict__ out, int64_t ldo) {
+  constexpr int KC = 64;           // positions per chunk
+  constexpr int NKD = D / 32;      // 32-wide d slices
+  constexpr int NDB = D / 16;      // 16-wide d blocks
+  constexpr int G = D / 64;        // quantisation groups per position
+  constexpr int KHALF = D / 64;    // K stored as D/64 arrays of 64 d (128-byte rows)
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[KHALF][KC * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * KC];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int t0 = blockIdx.x * 128 + wave * 32;     // first query of this wave
+  const int64_t row0 = ((b0 + b) * H + h) * cap;   // first cache row of this (b, h)
+  const int64_t nkeys = pos + min(T, (int)(blockIdx.x * 128 + 128));
+  const half2_t neg1024 = {(half_t)-1024.0f, (half_t)-1024.0f};
+
+  // Q^T operand: lane (query l16 of q-block qb, d slice kd, chunk g4)
+  half8_t qf[2][NKD];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int t = min(t0 + qb * 16 + l16, T - 1);
+    const uint16_t* qp = q + ((int64_t)b * T + t) * ldq + (int64_t)h * D;
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) qf[qb][kd] = *reinterpret_cast<const half8_t*>(qp + kd * 32 + g4 * 8);
+  }
+  float4_t oacc[NDB][2];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) oacc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  constexpr float kL2e = 1.4426950408889634f;
+
+  for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
+    __syncthreads();
+    // ---- reconstruct K (threads 0..127) and V (threads 128..255) ----
+    if (tid < 128) {
+      const int key = tid >> 1, hf = tid & 1;  // 2 threads per position, D/2 channels each
+      const int64_t j = min(k0 + key, nkeys - 1);
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(kc + (row0 + j) * (D / 2));
+      const uint32_t* mw = reinterpret_cast<const uint32_t*>(km) + (row0 + j) * G;
+#pragma unroll
+      for (int w = 0; w < D / 16; ++w) {  // 8-channel words of this half
+        const int word = hf * (D / 16) + w;
+        const int d0 = word * 8;
+        const uint32_t mb = mw[d0 / 64];
+        const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
+        const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
+        const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+        const uint32_t code = cw[word];
+        const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
+          const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
+          o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+        }
+        const int arr = d0 / 64, chunk = (d0 % 64) / 8;
+        *reinterpret_cast<uint4*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    } else {
+      // 8 positions (one storage chunk) x 8 channels per thread, transposed
+      const int u = tid - 128;
+      const int pc = u & 7;          // storage chunk: positions 8*pc .. 8*pc+7 in slice order
+      const int dc = u >> 3;         // channels 8*dc .. 8*dc+7 (D/8 <= 16 groups of 8)
+      if (dc < D / 8) {
+        const int sl = pc >> 2, qq = pc & 3;  // 32-wide slice, lane group inside it
+        uint32_t vals[8][4];                  // [position][channel pair]
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
+          const int64_t j = min(k0 + key, nkeys - 1);
+          const uint32_t code = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[dc];
+          const uint32_t mb = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + dc / 8];
+          const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
+          const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
+          const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+          const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
+            const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
+            vals[jj][p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+          }
+        }
+        // channel i of the 8: gather its 8 positions into one 16-byte chunk
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t a = vals[2 * pp][i >> 1], c2 = vals[2 * pp + 1][i >> 1];
+            // low halves (even channel) or high halves (odd channel) of two positions
+            w4[pp] = (i & 1) ? ((a >> 16) | (c2 & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c2 << 16));
+          }
+          const int d = dc * 8 + i;
+          *reinterpret_cast<uint4*>(&v_lds[d * KC + ((pc ^ (d & 7)) * 8)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+      }
+    }
+    __syncthreads();
+    // skip chunks entirely after this wave's last query (causal)
+    if (k0 > pos + t0 + 31) continue;
+    // ---- S^T = K^ Q^T : 4 key blocks x 2 query blocks ----
+    float4_t sacc[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      const int key = kb * 16 + l16;
+#pragma unroll
+      for (int kd = 0; kd < NKD; ++kd) {
+        const int arr = kd / 2, chunk = (kd % 2) * 4 + g4;
+        const half8_t kf = *reinterpret_cast<const half8_t*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
+      }
+    }
+    // ---- online softmax per query (lane l16 of each query block) ----
+    half8_t pf[2][2];  // [query block][32-wide key slice], B operand of O^T
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int64_t qpos = pos + t0 + qb * 16 + l16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t kpos = k0 + kb * 16 + 4 * g4 + r;
+          const float v = (kpos <= qpos && kpos < nkeys) ? sacc[kb][qb][r] * kL2e : -INFINITY;
+          sacc[kb][qb][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun[qb], mx);
+      const float alpha = mnew == -INFINITY ? 1.f : exp2f(mrun[qb] - mnew);
+      float sum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = mnew == -INFINITY ? 0.f : exp2f(sacc[kb][qb][r] - mnew);
+          sacc[kb][qb][r] = e;
+          sum += e;
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      lrun[qb] = lrun[qb] * alpha + sum;
+      mrun[qb] = mnew;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) oacc[i][qb] *= alpha;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pf[qb][sl][r] = (half_t)sacc[2 * sl][qb][r];
+          pf[qb][sl][4 + r] = (half_t)sacc[2 * sl + 1][qb][r];
+        }
+    }
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + l16;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const int chunk = sl * 4 + g4;
+        const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[d * KC + ((chunk ^ (d & 7)) * 8)]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][sl], oacc[db][qb], 0, 0, 0);
+      }
+    }
+  }
+  // ---- normalise and store: lane holds channels db*16 + 4*g4 + r of its query ----
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int t = t0 + qb * 16 + l16;
+    if (t >= T) continue;
+    const float inv = 1.0f / lrun[qb];
+    uint16_t* op = out + ((int64_t)b * T + t) * ldo + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint32_t w0 = (uint32_t)f2h(oacc[db][qb][0] * inv) | ((uint32_t)f2h(oacc[db][qb][1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f2h(oacc[db][qb][2] * inv) | ((uint32_t)f2h(oacc[db][qb][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + db * 16 + 4 * g4) = make_uint2(w0, w1);
+    }
+  }
+}
+
 fq_status check_kv(const fq_kv_layer* kv, const char* who) {
   if (!kv) return fail(FQ_ERR_INVALID, std::string(who) + ": kv is NULL");
   if (kv->group != FQ_GROUP) return fail(FQ_ERR_UNSUPPORTED, std::string(who) + ": only group 64 is implemented");
@@ -287,6 +498,13 @@ fq_status check_kv(const fq_kv_layer* kv, const char* who) {
 }  // namespace fq
 
 using namespace fq;
+
+// Test hook: FQ_PREFILL_VECTOR=1 selects the vector-unit prefill kernel (fp32
+// reconstruction) instead of the matrix-core one.
+static const bool g_prefill_vector_only = [] {
+  const char* e = getenv("FQ_PREFILL_VECTOR");
+  return e && e[0] == '1';
+}();
 
 extern "C" fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
                                          int64_t len, uint16_t* out, int64_t ldo, void* stream) {
@@ -332,18 +550,31 @@ extern "C" fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const 
   if (B == 0 || T == 0) return FQ_OK;
   FQ_CHECK_ARG(q && out && (uintptr_t)q % 16 == 0 && (uintptr_t)out % 16 == 0,
                "fq_prefill_attention: q/out NULL or misaligned");
-  const dim3 grid((unsigned)ceil_div(T, 64), (unsigned)kv->heads, (unsigned)B);
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
-  if (kv->head_dim == 128)
-    prefill_attention_kernel<128><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                              kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
-                                                              out, ldo);
-  else
-    prefill_attention_kernel<64><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                             kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
-                                                             out, ldo);
-  FQ_TRY(launch_check("prefill_attention_kernel"));
+  if (!g_prefill_vector_only) {
+    const dim3 grid((unsigned)ceil_div(T, 128), (unsigned)kv->heads, (unsigned)B);
+    if (kv->head_dim == 128)
+      prefill_attention_mfma_kernel<128><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                                     kv->v_meta, kv->heads, kv->capacity, b0, (int)T,
+                                                                     pos, out, ldo);
+    else
+      prefill_attention_mfma_kernel<64><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                                    kv->v_meta, kv->heads, kv->capacity, b0, (int)T,
+                                                                    pos, out, ldo);
+    FQ_TRY(launch_check("prefill_attention_mfma_kernel"));
+  } else {
+    const dim3 grid((unsigned)ceil_div(T, 64), (unsigned)kv->heads, (unsigned)B);
+    if (kv->head_dim == 128)
+      prefill_attention_kernel<128><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                                kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
+                                                                out, ldo);
+    else
+      prefill_attention_kernel<64><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
+                                                               kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
+                                                               out, ldo);
+    FQ_TRY(launch_check("prefill_attention_kernel"));
+  }
   if (tk >= 0) {
     const double units = (double)B * kv->heads, d = kv->head_dim;
     const double pairs = (double)T * pos + (double)T * (T + 1) / 2.0;  // (query, key) pairs under the causal mask

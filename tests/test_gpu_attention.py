@@ -77,7 +77,8 @@ def test_prefill_attention_causal(d, T, pos):
     for t in range(T):
         ref[:, :, t] = oracle.attention_decode(q4[:, :, t], kh[:, :, :pos + t + 1], vh[:, :, :pos + t + 1])
     ref = ref.transpose(0, 2, 1, 3).reshape(B * T, H * d)
-    assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill d={d} T={T} pos={pos}")
+    r, m = assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill d={d} T={T} pos={pos}")
+    log(f"prefill d={d} T={T} pos={pos}: rel_l2 {r:.2e} max_abs {m:.2e}")
 
 
 def test_decode_full_size_sampled():

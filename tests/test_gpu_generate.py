@@ -29,13 +29,21 @@ def _gpu_generate(L, B, P, G, seed, **model_kw):
     return ids, out, lg, st
 
 
+# Logits come after every layer plus the final LayerNorm: the per-layer bound
+# (relative L2 5e-3) is allowed to compound once more over the stack.
+LOGIT_REL_L2 = 1e-2
+
+
 def _compare(out, lg, ref, what):
     """Logits within tolerance while the token streams agree; a disagreement is
     allowed only at a near-tie of the oracle's logits, and ends the comparison."""
     B, G = out.shape
     for b in range(B):
         for t in range(G):
-            assert_close(lg[t, b], ref["logits"][t][b], rel=5e-3, abs_=3e-2, what=f"{what} logits b={b} t={t}")
+            r, m = assert_close(lg[t, b], ref["logits"][t][b], rel=LOGIT_REL_L2, abs_=3e-2,
+                                what=f"{what} logits b={b} t={t}")
+            if t == 0 and b == 0:
+                log(f"{what}: logits rel_l2 {r:.2e} max_abs {m:.2e}")
             if out[b, t] != ref["tokens"][b, t]:
                 r = ref["logits"][t][b]
                 gap = abs(r[out[b, t]] - r[ref["tokens"][b, t]])
