@@ -312,7 +312,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
   const int wm = wave & 1, wn = wave >> 1;
 
   // XCD-aware, grouped tile order: the 32 blocks an XCD runs at once cover
-  // 8 M tiles x 4 N tiles, so A and B tiles are re-read from that XCD's L2.
+  // 4 M tiles x 8 N tiles, so each activation tile is re-read from that XCD's
+  // L2 by 8 blocks (measured best of 1, 2, 4, 8, 16 M tiles per group).
   // (Tile ids are only remapped within the first 8*floor(n/8) blocks.)
   const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
   const int64_t nblk = tiles_m * tiles_n;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
     const int64_t per_xcd = nblk / 8;
     if (bid < per_xcd * 8) lid = (bid % 8) * per_xcd + bid / 8;
   }
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int64_t group = lid / (GM * tiles_n);
   const int64_t first_m = group * GM;
   const int64_t gsize = min((int64_t)GM, tiles_m - first_m);
@@ -381,10 +382,21 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
   const int b_row = tid >> 1, b_half = tid & 1;
   uint4 cw = make_uint4(0, 0, 0, 0);
   uint32_t cm = 0;
+  // explicit LDS reads (waited inside the asm block): the compiler would
+  // otherwise wait for every direct copy in flight before reading a slot
   auto read_codes = [&](auto s) {
-    const uint8_t* src = c_st(s);
-    cw = *reinterpret_cast<const uint4*>(src + b_row * 32 + b_half * 16);
-    cm = *reinterpret_cast<const uint32_t*>(src + BNx * 32 + b_row * 4);
+    const uint32_t base = (uint32_t)(uintptr_t)c_st(s);
+    const uint32_t ca = base + b_row * 32 + b_half * 16, ma = base + BNx * 32 + b_row * 4;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 v;
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b32 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v), "=&v"(cm)
+        : "v"(ca), "v"(ma)
+        : "memory");
+    cw = make_uint4(v[0], v[1], v[2], v[3]);
   };
   auto store_b_part = [&](auto s, int q) {
     uint8_t* dst = b_st(s) + b_row * ROWB;
@@ -496,6 +508,155 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
   }
 }
 
+// ---- small-M ("decode") kernel ------------------------------------------------
+// For M <= 256 (one decode step of the whole batch) a block owns every row of
+// C and 256 weight rows; each of its 4 waves owns 64 weight rows and all
+// 16*MB rows of A, so the weights are read exactly once per K range and need
+// no LDS: every lane reconstructs its own MFMA operand from 8 code bytes
+// (the 16 k values it contributes to the two 32-wide slices of a K step) in
+// registers.  The A tile of a K step is staged in LDS (double-buffered,
+// swizzled 128-byte rows) and shared by the 4 waves.  Within a K step, slice
+// ks of lane group g covers k chunk 2g+ks (the same mapping on both
+// operands), so a lane's codes for a K step are 8 contiguous bytes.  Split-K
+// across blocks (grid.y) fills the chip; partial sums go through the same
+// reduction kernel as the tiled path.
+template <int MB, bool PACKED>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
+                                                          const uint8_t* __restrict__ codes,
+                                                          const uint16_t* __restrict__ meta,
+                                                          const uint16_t* __restrict__ w16, int64_t N, int64_t K,
+                                                          int k_tiles_per_split, Epilogue epi,
+                                                          float* __restrict__ partial) {
+  constexpr int ROWS = MB * 16;
+  constexpr int CHUNKS = ROWS * 8;               // 16-byte chunks of an A tile
+  constexpr int PER_T = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t n_wave = (int64_t)blockIdx.x * 256 + wave * 64;
+  const int64_t m_base = (int64_t)blockIdx.z * ROWS;  // M beyond 16*MB rows: one block per row group
+  const int KT = (int)(K / BK);
+  const int kt0 = blockIdx.y * k_tiles_per_split;
+  const int kt1 = min(KT, kt0 + k_tiles_per_split);
+
+  // weight rows of this lane: n_wave + 16 j + l16, clamped (never stored beyond N)
+  int64_t wrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wrow[j] = min(n_wave + j * 16 + l16, N - 1);
+
+  uint4 ra[PER_T];
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * 256;
+      ra[i] = make_uint4(0, 0, 0, 0);
+      if (c < CHUNKS) {
+        const int r = c >> 3, ch = c & 7;
+        if (m_base + r < M)
+          ra[i] = *reinterpret_cast<const uint4*>(A + (m_base + r) * lda + (int64_t)kt * BK + ch * 8);
+      }
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = tid + i * 256;
+      if (c < CHUNKS) {
+        const int r = c >> 3, ch = c & 7;
+        *reinterpret_cast<uint4*>(&As[buf][r * 64 + ((ch ^ (r & 7)) * 8)]) = ra[i];
+      }
+    }
+  };
+  // weight operand registers for one K step: 4 rows x (8 bytes of codes + meta) or 4 x 32 bytes fp16
+  uint2 wc[4];
+  uint32_t wm[4];
+  uint4 wf[4][2];
+  auto load_w = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (PACKED) {
+        wc[j] = *reinterpret_cast<const uint2*>(codes + wrow[j] * (K / 2) + (int64_t)kt * 32 + g4 * 8);
+        wm[j] = reinterpret_cast<const uint32_t*>(meta)[wrow[j] * (K / 64) + kt];
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(w16 + wrow[j] * K + (int64_t)kt * BK + g4 * 16);
+        wf[j][0] = src[0];
+        wf[j][1] = src[1];
+      }
+    }
+  };
+
+  float4_t acc[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  if (kt0 < kt1) {
+    load_a(kt0);
+    load_w(kt0);
+    store_a(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const bool more = kt + 1 < kt1;
+      // this step's weight operands
+      half8_t bf[2][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (PACKED) {
+          const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(wm[j] & 0xFFFF));
+          const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(wm[j] >> 16));
+          const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+          uint32_t o[4];
+          dequant8(wc[j].x, mn2, s2, o);
+          bf[0][j] = __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+          dequant8(wc[j].y, mn2, s2, o);
+          bf[1][j] = __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+        } else {
+          bf[0][j] = __builtin_bit_cast(half8_t, wf[j][0]);
+          bf[1][j] = __builtin_bit_cast(half8_t, wf[j][1]);
+        }
+      }
+      if (more) {
+        load_a(kt + 1);
+        load_w(kt + 1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int ch = 2 * g4 + ks;  // k chunk of this lane in slice ks
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = i * 16 + l16;
+          const half8_t af = *reinterpret_cast<const half8_t*>(&As[cur][r * 64 + ((ch ^ (r & 7)) * 8)]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[ks][j], acc[i][j], 0, 0, 0);
+        }
+      }
+      if (more) store_a(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n_wave + j * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m_base + i * 16 + 4 * g4 + r;
+        if (m < M && n < N) {
+          if (partial)
+            partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
+          else
+            epilogue_store(epi, m, n, acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
                                                             int64_t N, Epilogue epi) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -533,6 +694,45 @@ fq_status get_workspace(size_t bytes, float** out) {
   }
   *out = g_ws.ptr;
   return FQ_OK;
+}
+
+template <int MB>
+fq_status run_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi, hipStream_t st) {
+  const int64_t N = W->n;
+  const int KT = (int)(W->k / BK);
+  const int64_t nblk = ceil_div(N, 256) * ceil_div(M, 16 * MB);
+  // aim for ~2 blocks per CU, each split at least 4 K steps long
+  int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, ceil_div(512, nblk)));
+  const int kps = (KT + splits - 1) / splits;
+  splits = (KT + kps - 1) / kps;
+  float* partial = nullptr;
+  if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
+  const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)splits, (unsigned)ceil_div(M, 16 * MB));
+  if (W->kind == FQ_WEIGHT_PACKED4)
+    gemm_skinny_kernel<MB, true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, nullptr, N,
+                                                             W->k, kps, epi, partial);
+  else
+    gemm_skinny_kernel<MB, false><<<grid, dim3(256), 0, st>>>(A, M, lda, nullptr, nullptr, W->w16, N, W->k, kps, epi,
+                                                              partial);
+  FQ_TRY(launch_check("gemm_skinny_kernel"));
+  if (splits > 1) {
+    splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
+    FQ_TRY(launch_check("splitk_reduce_kernel"));
+  }
+  return FQ_OK;
+}
+
+fq_status dispatch_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
+                          hipStream_t st) {
+  const int64_t mb = ceil_div(M, 16);
+  if (mb <= 1) return run_skinny<1>(A, M, lda, W, epi, st);
+  if (mb <= 2) return run_skinny<2>(A, M, lda, W, epi, st);
+  if (mb <= 3) return run_skinny<3>(A, M, lda, W, epi, st);
+  if (mb <= 4) return run_skinny<4>(A, M, lda, W, epi, st);
+  if (mb <= 6) return run_skinny<6>(A, M, lda, W, epi, st);
+  if (mb <= 8) return run_skinny<8>(A, M, lda, W, epi, st);
+  if (mb <= 9) return run_skinny<9>(A, M, lda, W, epi, st);
+  return run_skinny<8>(A, M, lda, W, epi, st);  // 129..256 rows: two row groups of 128
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -573,6 +773,7 @@ static const bool g_small_tiles_only = [] {
   return e && e[0] == '1';
 }();
 
+
 extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
                                      const uint16_t* bias, const uint16_t* residual, int64_t ldr, uint32_t epilogue,
                                      float qscale, int64_t qscale_cols, void* C, int64_t ldc, void* stream) {
@@ -604,7 +805,9 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
   const int KT = (int)(K / 64);
   const int tk = timing_begin(st);
   fq_status r;
-  if (M <= 32) {
+  if (M <= 256 && !g_small_tiles_only) {
+    r = dispatch_skinny(A, M, lda, W, epi, st);
+  } else if (M <= 32) {
     const int64_t tiles = ceil_div(N, 64);
     const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
     r = run_gemm<32, 64, 1, 4>(A, M, lda, W, epi, splits, st);

@@ -55,7 +55,7 @@ def _run(M, N, K, flags, packed=True, seed=0, qcols=0, f32out=False):
     return host(out), ref
 
 
-@pytest.mark.parametrize("M", [1, 8, 37, 64, 144, 300])
+@pytest.mark.parametrize("M", [1, 8, 37, 64, 144, 200, 256, 300])
 @pytest.mark.parametrize("N,K", [(64, 256), (200, 1024), (768, 256)])
 def test_gemm_packed_shapes(M, N, K):
     log(f"gemm packed M={M} N={N} K={K}")
