@@ -60,6 +60,12 @@ def parse():
     ap.add_argument("--max-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true", help="time only the oracle sample (no GPU)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="before the run, copy a BYTES-sized device buffer three times (a plain copy kernel of known "
+                         "size, for scaling hardware byte counters)")
+    ap.add_argument("--kernel-only", choices=["gemm_prefill"], default=None,
+                    help="launch only this kernel class, as one layer of the workload launches it (a short program "
+                         "for hardware-counter passes); prints the launch list instead of the JSON line")
     return ap.parse_args()
 
 
@@ -178,6 +184,44 @@ def cpu_baseline(cfg, seed):
             "sample_seconds": round(t_sample, 2)}
 
 
+def kernel_only(fq, synth, torch, cfg, args):
+    """The prefill GEMMs of one layer, exactly as the prompt pass launches them:
+    the batch's B*P prompt rows in chunks of at most --max-tokens rows, each
+    chunk through the QKV (bias, query scaling), out (bias, residual), FC1
+    (bias, ReLU) and FC2 (bias, residual) products of that layer's packed
+    weights.  Every layer of the workload repeats this launch list."""
+    h, F, B, P = cfg["hidden"], cfg["ffn"], cfg["batch"], cfg["prompt"]
+    model = fq.Model(h, cfg["heads"], F, 1, vocab=cfg["vocab"], max_pos=P + cfg["gen"] + 2,
+                     compress_weight=True, max_tokens=args.max_tokens)
+    model.init_random(args.seed)
+    shapes = {0: (3 * h, h), 1: (h, h), 2: (F, h), 3: (h, F)}
+    W = {i: fq.fq_weight(fq.FQ_WEIGHT_PACKED4, model.packed_weight(0, i), None, n, k)
+         for i, (n, k) in shapes.items()}
+    rows = min(B * P, args.max_tokens)
+    def act(cols, stream):
+        t = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
+        fq.fq_synth_normal_f16(t, args.seed, stream, 1.0)
+        return t
+
+    x, att, x1, h1 = (act(h, synth.STREAM["aux"] + i) for i in range(4))
+    qkv, f = act(3 * h, synth.STREAM["aux"] + 4), act(F, synth.STREAM["aux"] + 5)
+    bias = torch.zeros(max(3 * h, F), dtype=torch.float16, device="cuda")
+    E = fq
+    launches = []
+    for r0 in range(0, B * P, args.max_tokens):
+        M = min(args.max_tokens, B * P - r0)
+        fq.fq_dequant_gemm(h1[:M], W[0], qkv[:M], bias=bias, epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_QSCALE,
+                           qscale=(h // cfg["heads"]) ** -0.5, qscale_cols=h)
+        fq.fq_dequant_gemm(att[:M], W[1], x1[:M], bias=bias, residual=x[:M],
+                           epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_RESIDUAL)
+        fq.fq_dequant_gemm(h1[:M], W[2], f[:M], bias=bias, epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_RELU)
+        fq.fq_dequant_gemm(f[:M], W[3], x[:M], bias=bias, residual=x1[:M], epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_RESIDUAL)
+        launches += [(M, n, k) for n, k in shapes.values()]
+    torch.cuda.synchronize()
+    model.close()
+    print(json.dumps({"kernel_only": args.kernel_only, "launches": [list(t) for t in launches]}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -196,6 +240,19 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # an elementwise kernel: reads and writes BYTES each
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {4 * n} bytes")
+        del src, dst
+        torch.cuda.empty_cache()
+    if args.kernel_only:
+        kernel_only(fq, synth, torch, cfg, args)
+        return
     B, P, G = cfg["batch"], cfg["prompt"], cfg["gen"]
     t0 = time.time()
     model = fq.Model(cfg["hidden"], cfg["heads"], cfg["ffn"], cfg["layers"], vocab=cfg["vocab"], max_pos=P + G + 2,

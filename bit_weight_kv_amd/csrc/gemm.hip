@@ -55,6 +55,61 @@ __device__ inline void epilogue_store(const Epilogue& e, int64_t m, int64_t n, f
     reinterpret_cast<uint16_t*>(e.C)[m * e.ldc + n] = f2h(v);
 }
 
+// Whether epilogue_store8 may use 16-byte accesses for every 8-column chunk
+// that lies inside N (C, residual and bias rows 16-byte aligned).
+__device__ inline bool epilogue_vec_ok(const Epilogue& e) {
+  const bool c_ok = e.ldc % 8 == 0 && (uintptr_t)e.C % 16 == 0;
+  const bool r_ok = !(e.flags & FQ_EPI_RESIDUAL) || (e.ldr % 8 == 0 && (uintptr_t)e.residual % 16 == 0);
+  const bool b_ok = !(e.flags & FQ_EPI_BIAS) || (uintptr_t)e.bias % 16 == 0;
+  return c_ok && r_ok && b_ok;
+}
+
+// epilogue_store of v[0..7] at (m, n..n+7): the same arithmetic per element,
+// with 16-byte loads and stores when `vec` and the chunk lies inside N.
+__device__ inline void epilogue_store8(const Epilogue& e, int64_t m, int64_t n, const float* v, int64_t N,
+                                       bool vec) {
+  if (!vec || n + 8 > N) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (n + k < N) epilogue_store(e, m, n + k, v[k]);
+    return;
+  }
+  float w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = v[k];
+  if (e.flags & FQ_EPI_BIAS) {
+    const uint4 b = *reinterpret_cast<const uint4*>(e.bias + n);
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] += h2f((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));
+  }
+  if (e.flags & FQ_EPI_QSCALE) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (n + k < e.qcols) w[k] *= e.qscale;
+  }
+  if (e.flags & FQ_EPI_RELU) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = fmaxf(w[k], 0.0f);
+  }
+  if (e.flags & FQ_EPI_RESIDUAL) {
+    const uint4 r = *reinterpret_cast<const uint4*>(e.residual + m * e.ldr + n);
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] += h2f((uint16_t)(rw[k >> 1] >> (16 * (k & 1))));
+  }
+  if (e.flags & FQ_EPI_F32OUT) {
+    float4* c = reinterpret_cast<float4*>(reinterpret_cast<float*>(e.C) + m * e.ldc + n);
+    c[0] = make_float4(w[0], w[1], w[2], w[3]);
+    c[1] = make_float4(w[4], w[5], w[6], w[7]);
+  } else {
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = (uint32_t)f2h(w[2 * k]) | (uint32_t)f2h(w[2 * k + 1]) << 16;
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(e.C) + m * e.ldc + n) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 // 8 codes (one 32-bit word, element 2k in the low nibble of byte k) -> 8 fp16
 // values fp16(mn + c*s) in natural order, as 4 packed pairs.
 __device__ inline void dequant8(uint32_t w, half2_t mn2, half2_t s2, uint32_t out[4]) {
@@ -508,6 +563,267 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
   }
 }
 
+// Direct global -> LDS copies written as inline asm.  The compiler then sees
+// no LDS write in flight and inserts no waits of its own for them: the kernel
+// that uses these orders every copy with explicit s_waitcnt + s_barrier.
+// (Through the builtin, the compiler's per-object tracking of such copies
+// falls back to waiting for all of them once a kernel has many copy sites.)
+// M0 holds the wave-uniform LDS base; each lane's data lands at
+// base + lane * size.  One wait state separates the M0 write from the copy.
+__device__ inline void dma_lds16(const void* g, uint32_t lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+__device__ inline void dma_lds4(const void* g, uint32_t lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+// acc += a * b (16x16x32 fp16 MFMA) with the accumulator pinned to AGPRs.
+// Through the builtin, a wave holding 256 accumulators gets part of them
+// assigned to VGPRs and copied around every MFMA.  Consumers of acc after the
+// last call must wait out the MFMA latency themselves.
+__device__ inline void mfma16x16x32_acc(float4_t& acc, const half8_t& a, const half8_t& b) {
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// ---- large-M kernel, 256 x 256 tiles (packed weights) ------------------------
+// 64-byte rows: chunk c of row r sits at slot c ^ swz4(r) (8 consecutive rows
+// read or written at one chunk hit 8 distinct 16-byte bank groups).
+__device__ inline int swz4(int r) { return (r >> 1) & 3; }
+
+// 8 waves in 2 x 4, each 128 x 64 (8 x 4 MFMA 16x16x32 tiles, 128 fp32
+// accumulators pinned to AGPRs): two waves per SIMD, so one wave's LDS
+// latency, reconstruction and barrier waits overlap the other wave's MFMAs.
+// K step 32 (one MFMA k slice).  Per flop this moves half the activation
+// bytes of the 256 x 128 tile.
+//   * A: four LDS stages of 256 rows x 64 bytes; step kt+3's copies are
+//     issued during step kt.  Per step each wave copies 2 KiB of A (two
+//     instructions), half a KiB of codes and 128 bytes of {min, scale} (one
+//     instruction each on lanes 0-31): 4 copies per wave per step, so one
+//     vmcnt value serves every wave.
+//   * codes: four slots of 256 rows x (16 code bytes + 4 {min, scale}
+//     bytes); step kt+4's copies are issued during step kt.  Step kt+1's
+//     codes are reconstructed into the other of two fp16 B stages between the
+//     MFMAs of step kt, half a weight row per thread.
+//   * one barrier per step; the wait before it leaves the copies of this step
+//     and the previous one in flight.
+__global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
+                                                         const uint8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ meta, int64_t N, int64_t K,
+                                                         Epilogue epi) {
+  constexpr int BMx = 256, BNx = 256, TM = 128, TN = 64, FM = 8, FN = 4, BKx = 32;
+  constexpr int ROWB = BKx * 2;                   // 64 bytes per staged row
+  constexpr int A_BYTES = BMx * ROWB;             // 16 KiB
+  constexpr int B_BYTES = BNx * ROWB;             // 16 KiB
+  constexpr int CODE_BYTES = BNx * 16 + BNx * 4;  // 5 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[A_BYTES], a_lds1[A_BYTES], a_lds2[A_BYTES],
+      a_lds3[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b_lds0[B_BYTES], b_lds1[B_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t c_lds[4 * CODE_BYTES];
+  auto a_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? a_lds0 : S == 1 ? a_lds1 : S == 2 ? a_lds2 : a_lds3;
+  };
+  auto b_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? b_lds0 : b_lds1;
+  };
+  auto c_st = [&](auto s) -> uint8_t* { return c_lds + decltype(s)::value * CODE_BYTES; };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 4 M
+  // tiles x 8 N tiles
+  const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
+  const int64_t nblk = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  int64_t lid = bid;
+  {
+    const int64_t per_xcd = nblk / 8;
+    if (bid < per_xcd * 8) lid = (bid % 8) * per_xcd + bid / 8;
+  }
+  constexpr int GM = 4;
+  const int64_t group = lid / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t gsize = min((int64_t)GM, tiles_m - first_m);
+  const int64_t in_group = lid - group * GM * tiles_n;
+  const int64_t m0 = (first_m + in_group % gsize) * BMx, n0 = (in_group / gsize) * BNx;
+  const int KT = (int)(K / BKx);
+
+  // A copies: instruction q (0..15) fills rows 16q..16q+15 (lane -> row
+  // lane >> 2, slot lane & 3, fetching chunk slot ^ swz4(row)); wave w
+  // issues q = w and q = w + 8
+  const int cp_r = lane >> 2, cp_c = lane & 3;
+  const uint16_t* a_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (8 * i + wave) + cp_r;
+    a_src[i] = A + min(m0 + r, M - 1) * lda + (cp_c ^ swz4(r)) * 8;
+  }
+  auto issue_a = [&](auto s, int kt) {
+    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_lds16(a_src[i] + (int64_t)kt * BKx, dst + i * 8192);
+  };
+  // codes: wave w copies rows 32w..32w+31 on lanes 0-31
+  const int64_t code_row = min(n0 + wave * 32 + (lane & 31), N - 1);
+  const uint8_t* code_src = codes + code_row * (K / 2);
+  const uint16_t* meta_src = meta + code_row * (K / 64) * 2;
+  auto issue_codes = [&](auto s, int kt) {
+    const uint32_t dst = (uint32_t)(uintptr_t)c_st(s);
+    if (lane < 32) {
+      dma_lds16(code_src + (int64_t)kt * 16, dst + wave * 512);
+      dma_lds4(meta_src + (int64_t)(kt >> 1) * 2, dst + BNx * 16 + wave * 128);
+    }
+  };
+  // reconstruction: thread -> (row tid / 2, chunks 2 (tid & 1) and +1)
+  const int b_row = tid >> 1, b_half = tid & 1;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 cw = {0, 0};
+  uint32_t cm = 0;
+  auto read_codes = [&](auto s) {
+    const uint32_t base = (uint32_t)(uintptr_t)c_st(s);
+    const uint32_t ca = base + b_row * 16 + b_half * 8, ma = base + BNx * 16 + b_row * 4;
+    u32x2 v;
+    uint32_t mv;
+    asm volatile(
+        "ds_read_b64 %0, %2\n\t"
+        "ds_read_b32 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v), "=&v"(mv)
+        : "v"(ca), "v"(ma)
+        : "memory");
+    cw = v;
+    cm = mv;
+  };
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  auto store_b = [&](auto s, int q) {
+    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm & 0xFFFF));
+    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm >> 16));
+    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+    uint32_t o[4];
+    dequant8(cw[q], mn2, s2, o);
+    const u32x4 v = {o[0], o[1], o[2], o[3]};
+    const int c = b_half * 2 + q;
+    const uint32_t addr = (uint32_t)(uintptr_t)(b_st(s) + b_row * ROWB + ((c ^ swz4(b_row)) * 16));
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+  };
+
+  float4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  // prologue (K is a multiple of 128: KT >= 4 and a multiple of 4)
+  issue_codes(I0{}, 0);
+  issue_codes(I1{}, 1);
+  issue_codes(I2{}, 2);
+  issue_codes(I3{}, 3);
+  issue_a(I0{}, 0);
+  issue_a(I1{}, 1);
+  issue_a(I2{}, 2);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  read_codes(I0{});
+  store_b(I0{}, 0);
+  store_b(I0{}, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const int fr = lane & 15, fk = lane >> 4;
+  // step kt: A stage and code slot kt % 4 (S), B stage kt % 2.  Mode 0
+  // (every step but the last four): issue step kt+4's codes and step kt+3's
+  // A, leave this step's and the previous step's copies in flight (8 per
+  // wave).  Mode 1 (step KT-4): issue step KT-1's A only.  Mode 2: issue
+  // nothing.  Modes 1 and 2 wait for every copy.
+  auto step = [&](auto s, int kt, auto mode) {
+    constexpr int S = decltype(s)::value;
+    constexpr int MODE = decltype(mode)::value;
+    using SB = std::integral_constant<int, S % 2>;
+    using SB1 = std::integral_constant<int, (S + 1) % 2>;
+    using S1 = std::integral_constant<int, (S + 1) % 4>;
+    using S3 = std::integral_constant<int, (S + 3) % 4>;
+    read_codes(S1{});  // step kt+1 (stale but harmless past the last step)
+    if constexpr (MODE == 0) issue_codes(s, kt + 4);
+    if constexpr (MODE <= 1) issue_a(S3{}, kt + 3);
+    const uint8_t* As_ = a_st(s);
+    const uint8_t* Bs_ = b_st(SB{});
+    half8_t bf[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * TN + j * 16 + fr;
+      bf[j] = *reinterpret_cast<const half8_t*>(Bs_ + r * ROWB + ((fk ^ swz4(r)) * 16));
+    }
+    auto a_frag = [&](int i) {
+      const int r = wm * TM + i * 16 + fr;
+      return *reinterpret_cast<const half8_t*>(As_ + r * ROWB + ((fk ^ swz4(r)) * 16));
+    };
+    half8_t af = a_frag(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const half8_t an = a_frag(i + 1 < FM ? i + 1 : i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma16x16x32_acc(acc[i][j], af, bf[j]);
+      // past the last step this rewrites a stage nobody reads
+      if ((i & 3) == 3) store_b(SB1{}, i >> 2);
+      af = an;
+    }
+    if constexpr (MODE == 0)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  int kt = 0;
+  for (; kt + 4 < KT; kt += 4) {
+    step(I0{}, kt, M0{});
+    step(I1{}, kt + 1, M0{});
+    step(I2{}, kt + 2, M0{});
+    step(I3{}, kt + 3, M0{});
+  }
+  step(I0{}, kt, M1{});
+  step(I1{}, kt + 1, M2{});
+  step(I2{}, kt + 2, M2{});
+  step(I3{}, kt + 3, M2{});
+  // the last MFMAs' results are read by VALU instructions below: wait out
+  // the MFMA write -> VALU read latency the compiler cannot see
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // epilogue staged through LDS, 16 rows x 64 columns per wave at a time
+  // (row stride 68 floats), wave w in half (w & 1) of A stage w / 2
+  {
+    constexpr int SROW = 68;
+    uint8_t* region = (wave >> 1) == 0 ? a_lds0 : (wave >> 1) == 1 ? a_lds1 : (wave >> 1) == 2 ? a_lds2 : a_lds3;
+    float* stg = reinterpret_cast<float*>(region + (wave & 1) * 8192);
+    const bool vec = epilogue_vec_ok(epi);
+    const int rr = lane >> 2, cs = (lane & 3) * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(4 * (lane >> 4) + r) * SROW + j * 16 + (lane & 15)] = acc[i][j][r];
+      __syncthreads();
+      const int64_t m = m0 + wm * TM + i * 16 + rr;
+      if (m < M) {
+        for (int c = 0; c < 16; c += 8) {
+          const float4 lo = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c);
+          const float4 hi = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c + 4);
+          const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          epilogue_store8(epi, m, n0 + wn * TN + cs + c, v, N, vec);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ---- small-M ("decode") kernel ------------------------------------------------
 // For M <= 256 (one decode step of the whole batch) a block owns every row of
 // C and 256 weight rows; each of its 4 waves owns 64 weight rows and all
@@ -815,6 +1131,11 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
     const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
+  } else if (M >= 1024 && N >= 1024 && K % 128 == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 128 &&
+             !g_small_tiles_only && W->kind == FQ_WEIGHT_PACKED4) {
+    const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
+    gemm_wide8_kernel<<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi);
+    r = launch_check("gemm_wide8_kernel");
   } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !g_small_tiles_only) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 128)));
     if (W->kind == FQ_WEIGHT_PACKED4)

@@ -109,12 +109,32 @@ def test_gemm_grid_exact_weight_equals_plain_fp16_gemm():
 
 @pytest.mark.parametrize("packed", [True, False])
 def test_gemm_large_tile_kernel_ragged(packed):
-    """M and N not multiples of the 256 x 128 large-M tile, enough tiles to select it."""
+    """M and N not multiples of the large-M tiles, enough tiles to select them
+    (4-bit weights: the 256 x 256 kernel; fp16 weights: the 256 x 128 one);
+    N = 3900 takes the element-wise epilogue, N = 32776 the 8-wide one with
+    a last tile 8 columns wide."""
     log(f"gemm large-tile ragged packed={packed}")
     got, ref = _run(2100, 3900, 256, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, packed=packed)
     _tol_check(got, ref, "large tile ragged")
     got, ref = _run(1030, 32776, 128, fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU, packed=packed)
     _tol_check(got, ref, "large tile ragged 2")
+
+
+def test_gemm_large_tile_vector_epilogue():
+    """256 x 256 kernel, 8-wide epilogue with bias + residual, and with the
+    query scaling boundary inside an 8-column chunk and fp32 output."""
+    log("gemm large-tile vector epilogue")
+    got, ref = _run(2100, 4096, 256, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL)
+    _tol_check(got, ref, "vector epilogue")
+    got, ref = _run(2100, 4104, 384, fq.FQ_EPI_BIAS | fq.FQ_EPI_QSCALE, qcols=1000, f32out=True)
+    _tol_check(got, ref, "vector epilogue qscale f32")
+
+
+def test_gemm_packed_256x128_kernel():
+    """4-bit weights with K not a multiple of 128 take the 256 x 128 kernel."""
+    log("gemm packed 256x128 K=192")
+    got, ref = _run(2100, 4000, 192, fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU)
+    _tol_check(got, ref, "packed 256x128")
 
 
 def test_gemm_empty_m_is_noop():
