@@ -585,6 +585,12 @@ __device__ inline void dma_lds4(const void* g, uint32_t lds_base) {
 __device__ inline void mfma16x16x32_acc(float4_t& acc, const half8_t& a, const half8_t& b) {
   asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// The same, kept in program order relative to every other ordered MFMA (the
+// compiler's scheduler would otherwise reorder them and wait for all
+// fragment reads before the first one).
+__device__ inline void mfma16x16x32_acc_ordered(float4_t& acc, const half8_t& a, const half8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
 // ---- large-M kernel, 256 x 256 tiles (packed weights) ------------------------
 // 64-byte rows: chunk c of row r sits at slot c ^ swz4(r) (8 consecutive rows
@@ -973,6 +979,166 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
   }
 }
 
+// ---- 4-bit decode GEMM (M <= 256) --------------------------------------------
+// A block owns 256 weight rows (64 per wave) and every row of A (16*MB).
+// The weight stream is the traffic, so it is kept deep in flight: per K step
+// (64 = one quantisation group) the block copies the step's A tile (swizzled
+// 128-byte rows), its codes (256 rows x 32 B) and {min, scale} (256 x 4 B)
+// global -> LDS with direct copies into a ring of S stages, issued S-1 steps
+// ahead (every wave issues the same PER copies per step: its share of the A
+// tile, and the codes/meta of its own 64 rows).  Each lane reconstructs its
+// own MFMA B operand from 8 code bytes per weight row (the 16 k values it
+// contributes to the step's two 32-wide slices, chunk 2g+ks of lane group g),
+// one step ahead: step kt+1's operand is rebuilt between step kt's MFMAs.
+// One barrier per step; the wait before it leaves S-3 steps of copies in
+// flight.  Split-K across blocks (grid.y) with fp32 partials as before.
+template <int MB>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
+                                                          const uint8_t* __restrict__ codes,
+                                                          const uint16_t* __restrict__ meta, int64_t N, int64_t K,
+                                                          int k_tiles_per_split, Epilogue epi,
+                                                          float* __restrict__ partial) {
+  constexpr int ROWS = MB * 16, ROWS_PAD = (ROWS + 31) / 32 * 32;
+  constexpr int A_INSTR = ROWS_PAD / 32;  // A copies per wave per step (8 rows of 128 B each)
+  constexpr int PER = A_INSTR + 3;        // + two codes copies + one {min, scale} copy
+  constexpr int A_BYTES = ROWS_PAD * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
+  constexpr int S = 5;
+  static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
+  static_assert((S - 3) * PER <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t n_blk = (int64_t)blockIdx.x * 256;
+  const int64_t m_base = (int64_t)blockIdx.z * ROWS;
+  const int KT = (int)(K / BK);
+  const int kt0 = blockIdx.y * k_tiles_per_split;
+  const int kt1 = min(KT, kt0 + k_tiles_per_split);
+
+  // A copies: instruction q = wave + 4t fills rows 8q..8q+7 (lane -> row
+  // 8q + lane / 8, slot lane % 8 holding chunk slot ^ (row % 8)); rows past M
+  // are clamped (read, never stored)
+  const uint16_t* a_src[A_INSTR];
+#pragma unroll
+  for (int t = 0; t < A_INSTR; ++t) {
+    const int r = 8 * (wave + 4 * t) + (lane >> 3);
+    a_src[t] = A + min(m_base + r, M - 1) * lda + ((lane & 7) ^ (r & 7)) * 8;
+  }
+  const uint8_t* c_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    c_src[i] = codes + min(n_blk + wave * 64 + i * 32 + (lane >> 1), N - 1) * (K / 2) + (lane & 1) * 16;
+  const uint16_t* m_src = meta + min(n_blk + wave * 64 + lane, N - 1) * (K / 64) * 2;
+  auto issue = [&](int kt, int slot) {
+    const uint32_t st = lds_base + slot * STAGE;
+#pragma unroll
+    for (int t = 0; t < A_INSTR; ++t) dma_lds16(a_src[t] + (int64_t)kt * BK, st + (wave + 4 * t) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_lds16(c_src[i] + (int64_t)kt * 32, st + A_BYTES + (wave * 64 + i * 32) * 32);
+    dma_lds4(m_src + (int64_t)kt * 2, st + A_BYTES + C_BYTES + wave * 256);
+  };
+  // this lane's weight rows: wave * 64 + 16 j + l16
+  uint2 cw[4];
+  uint32_t cm[4];
+  auto read_codes = [&](int slot) {
+    const uint8_t* st = lds + slot * STAGE + A_BYTES;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wave * 64 + j * 16 + l16;
+      cw[j] = *reinterpret_cast<const uint2*>(st + row * 32 + g4 * 8);
+      cm[j] = *reinterpret_cast<const uint32_t*>(st + C_BYTES + row * 4);
+    }
+  };
+  auto rebuild = [&](int e, half8_t (&b)[2][4]) {  // e = 4 * word + row
+    const int j = e & 3, w = e >> 2;
+    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
+    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
+    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+    uint32_t o[4];
+    dequant8(w ? cw[j].y : cw[j].x, mn2, s2, o);
+    b[w][j] = __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+
+  float4_t acc[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  if (kt0 < kt1) {
+    for (int t = 0; t < S - 1 && kt0 + t < kt1; ++t) issue(kt0 + t, t);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    half8_t bcur[2][4], bnxt[2][4];
+    read_codes(0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rebuild(e, bcur);
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int it = kt - kt0, slot = it % S;
+      if (kt > kt0) {
+        // steps kt and kt+1 complete in every wave; step kt-1's slot free
+        if (kt + S - 2 < kt1)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
+      const bool ahead = kt + 1 < kt1;
+      if (ahead) read_codes((it + 1) % S);
+      const uint8_t* As_ = lds + slot * STAGE;
+      // every A fragment of the step requested up front, in the order the
+      // MFMAs use them (LDS reads complete in order, so each MFMA group waits
+      // only for its own fragment)
+      half8_t af[2][MB];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = i * 16 + l16, ch = 2 * g4 + ks;
+          af[ks][i] = *reinterpret_cast<const half8_t*>(As_ + r * 128 + ((ch ^ (r & 7)) * 16));
+          __builtin_amdgcn_sched_barrier(0);  // issue in use order
+        }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mfma16x16x32_acc_ordered(acc[i][j], af[ks][i], bcur[ks][j]);
+          const int e = ks * MB + i;
+          if (e < 8 && ahead) rebuild(e, bnxt);
+        }
+      }
+#pragma unroll
+      for (int e = 2 * MB; e < 8; ++e)
+        if (ahead) rebuild(e, bnxt);
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bcur[w][j] = bnxt[w][j];
+    }
+    // the last MFMAs' results are read by VALU instructions below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  }
+
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n_blk + wave * 64 + j * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m_base + i * 16 + 4 * g4 + r;
+        if (m < M && n < N) {
+          if (partial)
+            partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
+          else
+            epilogue_store(epi, m, n, acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
                                                             int64_t N, Epilogue epi) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1038,9 +1204,62 @@ fq_status run_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
   return FQ_OK;
 }
 
+// Split count for the 4-bit decode GEMM: blocks run one per CU (the LDS ring
+// takes most of a CU's LDS), so pick the split that minimises rounds of 256
+// blocks x (K steps per block + ring fill), plus the fp32 partial traffic
+// (written and read back by the reduction) priced at 4 TB/s.
+int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB) {
+  const double step_us = std::max(0.15, 0.06 * MB);
+  int best = 1;
+  double best_t = 1e30;
+  for (int s = 1; s <= std::min(16, std::max(1, KT / 4)); ++s) {
+    const int kps = (KT + s - 1) / s;
+    const int splits = (KT + kps - 1) / kps;
+    const double rounds = (double)ceil_div(nblk * splits, 256);
+    const double t = rounds * (kps + 6) * step_us + (splits > 1 ? splits * (double)M * N * 8.0 / 4e6 : 0.0);
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
+}
+
+template <int MB>
+fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
+                     hipStream_t st) {
+  const int64_t N = W->n;
+  const int KT = (int)(W->k / BK);
+  const int64_t zb = ceil_div(M, 16 * MB);
+  int splits = decode_splits(ceil_div(N, 256) * zb, KT, M, N, MB);
+  const int kps = (KT + splits - 1) / splits;
+  splits = (KT + kps - 1) / kps;
+  float* partial = nullptr;
+  if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
+  const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)splits, (unsigned)zb);
+  gemm_decode_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps, epi,
+                                                     partial);
+  FQ_TRY(launch_check("gemm_decode_kernel"));
+  if (splits > 1) {
+    splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
+    FQ_TRY(launch_check("splitk_reduce_kernel"));
+  }
+  return FQ_OK;
+}
+
 fq_status dispatch_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
                           hipStream_t st) {
   const int64_t mb = ceil_div(M, 16);
+  if (W->kind == FQ_WEIGHT_PACKED4) {
+    if (mb <= 1) return run_decode<1>(A, M, lda, W, epi, st);
+    if (mb <= 2) return run_decode<2>(A, M, lda, W, epi, st);
+    if (mb <= 3) return run_decode<3>(A, M, lda, W, epi, st);
+    if (mb <= 4) return run_decode<4>(A, M, lda, W, epi, st);
+    if (mb <= 6) return run_decode<6>(A, M, lda, W, epi, st);
+    if (mb <= 8) return run_decode<8>(A, M, lda, W, epi, st);
+    if (mb <= 9) return run_decode<9>(A, M, lda, W, epi, st);
+    return run_decode<8>(A, M, lda, W, epi, st);  // 129..256 rows: two row groups of 128
+  }
   if (mb <= 1) return run_skinny<1>(A, M, lda, W, epi, st);
   if (mb <= 2) return run_skinny<2>(A, M, lda, W, epi, st);
   if (mb <= 3) return run_skinny<3>(A, M, lda, W, epi, st);
