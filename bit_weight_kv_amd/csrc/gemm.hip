@@ -592,6 +592,60 @@ __device__ inline void mfma16x16x32_acc_ordered(float4_t& acc, const half8_t& a,
   asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Four MFMAs (acc_j += a * b_j) with the reconstruction of one 8-code word
+// interleaved between them: a wave's VALU work overlaps its own MFMAs only
+// when the two are interleaved finely (measured: 8 MFMAs + 16 independent
+// VALU ops cost 162 cycles interleaved, 213 back to back, 147 for the MFMAs
+// alone).  The VALU part is dequant8 instruction for instruction: nibbles to
+// bytes (and, shift, and), byte permutes into {c, 0x00} pairs, exponent OR
+// (1024 + c), exact fp16 subtract of 1024, one packed fp16 FMA c*s + min with
+// {min, scale} taken from the halves of `ms`.  Its outputs are consumed by
+// later MFMAs only, never inside this block.
+__device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
+                                     const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
+                                     uint32_t w, uint32_t ms, half8_t& out) {
+  // separate volatile statements keep their order; one accumulator per MFMA
+  // statement keeps every accumulator in place (a statement binding several
+  // makes the register allocator copy them around)
+  uint32_t o0, o1, o2, o3, lo, hi;
+  mfma16x16x32_acc_ordered(c0, a, b0);
+  asm volatile(
+      "v_and_b32 %0, 0x0f0f0f0f, %4\n\t"
+      "v_lshrrev_b32 %1, 4, %4\n\t"
+      "v_and_b32 %1, 0x0f0f0f0f, %1\n\t"
+      "v_perm_b32 %2, %1, %0, %5\n\t"
+      "v_perm_b32 %3, %1, %0, %6"
+      : "=&v"(lo), "=&v"(hi), "=&v"(o0), "=&v"(o1)
+      : "v"(w), "s"(0x0C040C00u), "s"(0x0C050C01u));
+  mfma16x16x32_acc_ordered(c1, a, b1);
+  asm volatile(
+      "v_perm_b32 %0, %5, %4, %6\n\t"
+      "v_perm_b32 %1, %5, %4, %7\n\t"
+      "v_or_b32 %2, 0x64006400, %2\n\t"
+      "v_or_b32 %3, 0x64006400, %3\n\t"
+      "v_or_b32 %0, 0x64006400, %0"
+      : "=&v"(o2), "=&v"(o3), "+v"(o0), "+v"(o1)
+      : "v"(lo), "v"(hi), "s"(0x0C060C02u), "s"(0x0C070C03u));
+  mfma16x16x32_acc_ordered(c2, a, b2);
+  asm volatile(
+      "v_or_b32 %3, 0x64006400, %3\n\t"
+      "v_pk_add_f16 %0, %0, %4\n\t"
+      "v_pk_add_f16 %1, %1, %4\n\t"
+      "v_pk_add_f16 %2, %2, %4\n\t"
+      "v_pk_add_f16 %3, %3, %4"
+      : "+v"(o0), "+v"(o1), "+v"(o2), "+v"(o3)
+      : "s"(0xE400E400u));
+  mfma16x16x32_acc_ordered(c3, a, b3);
+  asm volatile(
+      "v_pk_fma_f16 %0, %0, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
+      "v_pk_fma_f16 %1, %1, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
+      "v_pk_fma_f16 %2, %2, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
+      "v_pk_fma_f16 %3, %3, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]"
+      : "+v"(o0), "+v"(o1), "+v"(o2), "+v"(o3)
+      : "v"(ms));
+  out = __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
+}
+
 // ---- large-M kernel, 256 x 256 tiles (packed weights) ------------------------
 // 64-byte rows: chunk c of row r sits at slot c ^ swz4(r) (8 consecutive rows
 // read or written at one chunk hit 8 distinct 16-byte bank groups).
@@ -708,16 +762,18 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
     cm = mv;
   };
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  auto store_b_word = [&](auto s, int q, const half8_t& v) {
+    const int c = b_half * 2 + q;
+    const uint32_t addr = (uint32_t)(uintptr_t)(b_st(s) + b_row * ROWB + ((c ^ swz4(b_row)) * 16));
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+  };
   auto store_b = [&](auto s, int q) {
     const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm & 0xFFFF));
     const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm >> 16));
     const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
     uint32_t o[4];
     dequant8(cw[q], mn2, s2, o);
-    const u32x4 v = {o[0], o[1], o[2], o[3]};
-    const int c = b_half * 2 + q;
-    const uint32_t addr = (uint32_t)(uintptr_t)(b_st(s) + b_row * ROWB + ((c ^ swz4(b_row)) * 16));
-    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+    store_b_word(s, q, __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3])));
   };
 
   float4_t acc[FM][FN];
@@ -741,21 +797,22 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   const int fr = lane & 15, fk = lane >> 4;
-  // step kt: A stage and code slot kt % 4 (S), B stage kt % 2.  Mode 0
-  // (every step but the last four): issue step kt+4's codes and step kt+3's
-  // A, leave this step's and the previous step's copies in flight (8 per
-  // wave).  Mode 1 (step KT-4): issue step KT-1's A only.  Mode 2: issue
-  // nothing.  Modes 1 and 2 wait for every copy.
-  auto step = [&](auto s, int kt, auto mode) {
+  // step kt: A stage and code slot kt % 4 (S), B stage kt % 2.  Every step
+  // but the last four issues step kt+4's codes and step kt+3's A and leaves
+  // this step's and the previous step's copies in flight (8 per wave); step
+  // KT-4 issues step KT-1's A only; the last four wait for every copy.  The
+  // conditions are run-time branches around the copies and waits only: the
+  // MFMA chain is the same code in every step (a branch around MFMAs makes
+  // the register allocator copy accumulators at the join).
+  auto step = [&](auto s, int kt) {
     constexpr int S = decltype(s)::value;
-    constexpr int MODE = decltype(mode)::value;
     using SB = std::integral_constant<int, S % 2>;
     using SB1 = std::integral_constant<int, (S + 1) % 2>;
     using S1 = std::integral_constant<int, (S + 1) % 4>;
     using S3 = std::integral_constant<int, (S + 3) % 4>;
     read_codes(S1{});  // step kt+1 (stale but harmless past the last step)
-    if constexpr (MODE == 0) issue_codes(s, kt + 4);
-    if constexpr (MODE <= 1) issue_a(S3{}, kt + 3);
+    if (kt + 4 < KT) issue_codes(s, kt + 4);
+    if (kt + 3 < KT) issue_a(S3{}, kt + 3);
     const uint8_t* As_ = a_st(s);
     const uint8_t* Bs_ = b_st(SB{});
     half8_t bf[FN];
@@ -772,31 +829,30 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const half8_t an = a_frag(i + 1 < FM ? i + 1 : i);
+      if ((i & 3) == 1) {
+        // the MFMAs of this row block carry the reconstruction of code word
+        // q; past the last step it rewrites a stage nobody reads
+        const int q = i >> 2;
+        half8_t nb;
+        mfma4_rebuild(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, bf[0], bf[1], bf[2], bf[3], cw[q], cm, nb);
+        store_b_word(SB1{}, q, nb);
+      } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) mfma16x16x32_acc(acc[i][j], af, bf[j]);
-      // past the last step this rewrites a stage nobody reads
-      if ((i & 3) == 3) store_b(SB1{}, i >> 2);
+        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bf[j]);
+      }
       af = an;
     }
-    if constexpr (MODE == 0)
+    if (kt + 4 < KT)
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  using M0 = std::integral_constant<int, 0>;
-  using M1 = std::integral_constant<int, 1>;
-  using M2 = std::integral_constant<int, 2>;
-  int kt = 0;
-  for (; kt + 4 < KT; kt += 4) {
-    step(I0{}, kt, M0{});
-    step(I1{}, kt + 1, M0{});
-    step(I2{}, kt + 2, M0{});
-    step(I3{}, kt + 3, M0{});
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    step(I2{}, kt + 2);
+    step(I3{}, kt + 3);
   }
-  step(I0{}, kt, M1{});
-  step(I1{}, kt + 1, M2{});
-  step(I2{}, kt + 2, M2{});
-  step(I3{}, kt + 3, M2{});
   // the last MFMAs' results are read by VALU instructions below: wait out
   // the MFMA write -> VALU read latency the compiler cannot see
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1004,6 +1060,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __rest
   constexpr int A_BYTES = ROWS_PAD * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
   constexpr int S = 5;
   static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
+  static_assert(MB >= 4, "at least 8 MFMA groups per step carry the 8 reconstructions");
   static_assert((S - 3) * PER <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
@@ -1069,11 +1126,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __rest
   if (kt0 < kt1) {
     for (int t = 0; t < S - 1 && kt0 + t < kt1; ++t) issue(kt0 + t, t);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    half8_t bcur[2][4], bnxt[2][4];
+    half8_t bA[2][4], bB[2][4];
     read_codes(0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rebuild(e, bcur);
-    for (int kt = kt0; kt < kt1; ++kt) {
+    for (int e = 0; e < 8; ++e) rebuild(e, bA);
+    // One K step: MFMAs on `bcur`, step kt+1's operand rebuilt into `bnxt`
+    // (interleaved with the MFMAs: reconstruction d goes with MFMA group
+    // d * 2MB / 8 of the 2MB groups).  Steps alternate the
+    // two operand buffers, so no register copy sits before an MFMA.
+    auto step = [&](int kt, half8_t (&bcur)[2][4], half8_t (&bnxt)[2][4]) {
       const int it = kt - kt0, slot = it % S;
       if (kt > kt0) {
         // steps kt and kt+1 complete in every wave; step kt-1's slot free
@@ -1086,35 +1147,45 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __rest
       const bool ahead = kt + 1 < kt1;
       if (ahead) read_codes((it + 1) % S);
       const uint8_t* As_ = lds + slot * STAGE;
-      // every A fragment of the step requested up front, in the order the
-      // MFMAs use them (LDS reads complete in order, so each MFMA group waits
-      // only for its own fragment)
-      half8_t af[2][MB];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) {
+        // the slice's A fragments requested up front, in the order the MFMAs
+        // use them (LDS reads complete in order, so each MFMA group waits
+        // only for its own fragment)
+        half8_t af[MB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int r = i * 16 + l16, ch = 2 * g4 + ks;
-          af[ks][i] = *reinterpret_cast<const half8_t*>(As_ + r * 128 + ((ch ^ (r & 7)) * 16));
+          af[i] = *reinterpret_cast<const half8_t*>(As_ + r * 128 + ((ch ^ (r & 7)) * 16));
           __builtin_amdgcn_sched_barrier(0);  // issue in use order
         }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
         for (int i = 0; i < MB; ++i) {
+          const int g = ks * MB + i;
+          int d = -1;  // the reconstruction carried by group g, if any
 #pragma unroll
-          for (int j = 0; j < 4; ++j) mfma16x16x32_acc_ordered(acc[i][j], af[ks][i], bcur[ks][j]);
-          const int e = ks * MB + i;
-          if (e < 8 && ahead) rebuild(e, bnxt);
+          for (int e = 0; e < 8; ++e)
+            if (e * 2 * MB / 8 == g) d = e;
+          // (past the last step this rebuilds stale codes into an unused
+          // buffer: a runtime condition here would split the MFMA chain)
+          if (d >= 0) {
+            const int j = d & 3, w = d >> 2;
+            mfma4_rebuild(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af[i], bcur[ks][0], bcur[ks][1], bcur[ks][2],
+                          bcur[ks][3], w ? cw[j].y : cw[j].x, cm[j], bnxt[w][j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mfma16x16x32_acc_ordered(acc[i][j], af[i], bcur[ks][j]);
+          }
         }
       }
-#pragma unroll
-      for (int e = 2 * MB; e < 8; ++e)
-        if (ahead) rebuild(e, bnxt);
-#pragma unroll
-      for (int w = 0; w < 2; ++w)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bcur[w][j] = bnxt[w][j];
+    };
+    // pairs of steps: every split has an even number of steps (the host
+    // guarantees it), so the MFMA chain is one piece of code -- a separate
+    // odd last step makes the register allocator move the accumulators
+    // through VGPRs next to MFMAs it cannot see
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      step(kt, bA, bB);
+      step(kt + 1, bB, bA);
     }
     // the last MFMAs' results are read by VALU instructions below
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1232,7 +1303,8 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
   const int KT = (int)(W->k / BK);
   const int64_t zb = ceil_div(M, 16 * MB);
   int splits = decode_splits(ceil_div(N, 256) * zb, KT, M, N, MB);
-  const int kps = (KT + splits - 1) / splits;
+  // the kernel runs K steps in pairs: even steps per split (KT is even here)
+  const int kps = ((KT + splits - 1) / splits + 1) & ~1;
   splits = (KT + kps - 1) / kps;
   float* partial = nullptr;
   if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
@@ -1250,10 +1322,9 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
 fq_status dispatch_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
                           hipStream_t st) {
   const int64_t mb = ceil_div(M, 16);
-  if (W->kind == FQ_WEIGHT_PACKED4) {
-    if (mb <= 1) return run_decode<1>(A, M, lda, W, epi, st);
-    if (mb <= 2) return run_decode<2>(A, M, lda, W, epi, st);
-    if (mb <= 3) return run_decode<3>(A, M, lda, W, epi, st);
+  // the streaming decode kernel for 4-bit weights from 49 rows up (at least
+  // 8 MFMA groups per K step to carry the reconstructions) and even K steps
+  if (W->kind == FQ_WEIGHT_PACKED4 && (W->k / BK) % 2 == 0 && mb >= 4) {
     if (mb <= 4) return run_decode<4>(A, M, lda, W, epi, st);
     if (mb <= 6) return run_decode<6>(A, M, lda, W, epi, st);
     if (mb <= 8) return run_decode<8>(A, M, lda, W, epi, st);
