@@ -77,7 +77,10 @@ def test_inline_asm_mfma_kernels_keep_accumulators_in_place(gemm_asm):
         guards = [i for i, l in enumerate(lines) if re.match(r"\s*s_nop 7\s*$", l) and i > first]
         assert guards, f"{name}: no s_nop 7 guard after the MFMAs"
         region = lines[first:guards[0]]
-        bad = [l.strip() for l in region if re.search(r"v_accvgpr_(read|write|mov)", l)]
+        # zero initialisation of the accumulators (a constant write the
+        # compiler may lay out after the loop in text order) is not traffic
+        bad = [l.strip() for l in region if re.search(r"v_accvgpr_(read|write|mov)", l)
+               and not re.search(r"v_accvgpr_write_b32 a\d+, 0\s*$", l)]
         assert not bad, f"{name}: accumulator traffic between inline-asm MFMAs: {bad[:4]}"
         assert "scratch_" not in body, f"{name}: spills to scratch"
     # the 4-bit prefill kernel and every decode instantiation are covered
