@@ -34,9 +34,10 @@ CONFIGS = {
     "opt30b-4bit": dict(hidden=7168, heads=56, ffn=28672, layers=48, vocab=50272, batch=256, prompt=512, gen=32,
                         compress_weight=True, desc="OPT-30B shape, 4-bit g64 weights + 4-bit KV resident in HBM"),
     "opt175b-fp16-streamed": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=256, prompt=512,
-                                  gen=32, compress_weight=False, resident_layers=0, host_layers=48,
+                                  gen=32, compress_weight=False, resident_layers=0, host_layers=12,
                                   desc="OPT-175B shape, fp16 weights streamed layer by layer from pinned host memory "
-                                       "(48 distinct host layer blobs, layer l reads blob l mod 48), 4-bit KV"),
+                                       "(12 distinct host layer blobs, layer l reads blob l mod 12: the GPU host "
+                                       "allows ~58 GB of pinned memory per process), 4-bit KV"),
     "tiny-2layer": dict(hidden=256, heads=4, ffn=1024, layers=2, vocab=512, batch=8, prompt=64, gen=5,
                         compress_weight=True, desc="tiny OPT-style model for smoke benchmarking"),
 }
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the run, copy a BYTES-sized device buffer three times (a plain copy kernel of known "
                          "size, for scaling hardware byte counters)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure this GPU's practical ceilings (HBM copy stream, pinned host<->device copies, "
+                         "the vendor library's fp16 GEMM at the prefill shape) and print them as one JSON line")
     ap.add_argument("--kernel-only", choices=["gemm_prefill"], default=None,
                     help="launch only this kernel class, as one layer of the workload launches it (a short program "
                          "for hardware-counter passes); prints the launch list instead of the JSON line")
@@ -210,6 +214,43 @@ def cpu_baseline(cfg, seed):
             "sample_seconds": round(t_sample, 2)}
 
 
+def ceilings(torch):
+    """Practical ceilings of this GPU, measured with plain torch operations
+    (reference points for the roofline fractions; not part of the path)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    out = {}
+    n = 1 << 30  # 4 GiB of int32, far above the 256 MB MALL
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: torch.neg(src, out=dst), 5)
+    out["hbm_copy_GBs"] = round(2 * 4 * n / t / 1e9, 1)  # read + write
+    del src, dst
+    torch.cuda.empty_cache()
+    host = torch.empty(1 << 28, dtype=torch.int32, pin_memory=True)  # 1 GiB pinned
+    dev = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    out["h2d_pinned_GBs"] = round(4 * (1 << 28) / timed(lambda: dev.copy_(host, non_blocking=True), 5) / 1e9, 1)
+    out["d2h_pinned_GBs"] = round(4 * (1 << 28) / timed(lambda: host.copy_(dev, non_blocking=True), 5) / 1e9, 1)
+    del host, dev
+    M, N, K = 16384, 49152, 12288
+    a = torch.randn((M, K), dtype=torch.float16, device="cuda")
+    b = torch.randn((K, N), dtype=torch.float16, device="cuda")
+    c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    t = timed(lambda: torch.matmul(a, b, out=c), 5)
+    out["library_fp16_gemm_TFLOPs"] = round(2.0 * M * N * K / t / 1e12, 1)
+    out["library_fp16_gemm_shape"] = [M, N, K]
+    return out
+
+
 def kernel_only(fq, synth, torch, cfg, args):
     """The prefill GEMMs of one layer, exactly as the prompt pass launches them:
     the batch's B*P prompt rows in chunks of at most --max-tokens rows, each
@@ -276,6 +317,9 @@ def main():
         log(f"[bench] copy calibration: 3 copies of {4 * n} bytes")
         del src, dst
         torch.cuda.empty_cache()
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(torch)}), flush=True)
+        return
     if args.kernel_only:
         kernel_only(fq, synth, torch, cfg, args)
         return
@@ -286,6 +330,14 @@ def main():
                      host_layers=cfg.get("host_layers", 0), overlap=True, max_tokens=args.max_tokens)
     model.init_random(args.seed)
     kv = fq.KVCache(model, B, P + G)
+    last = [time.time()]
+
+    def progress(done, total):  # generations of several minutes report each completed token every ~20 s
+        if time.time() - last[0] > 20 or done == 1 and time.time() - last[0] > 5:
+            log(f"[bench] token {done}/{total} done")
+            last[0] = time.time()
+
+    fq.fq_set_progress(progress)
     ids = synth.token_ids(args.seed, synth.STREAM["prompt"], (B, P), cfg["vocab"])
     torch.cuda.synchronize()
     log(f"[bench] {args.config}: model + cache ready in {time.time() - t0:.1f} s")

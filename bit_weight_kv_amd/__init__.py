@@ -99,6 +99,7 @@ _SIGS = {
     "fq_generate": (c_i32, [c_vp, c_vp, _P(c_i32), c_i64, c_i64, c_i64, _P(c_i32), c_vp, _P(fq_gen_stats), c_vp]),
     "fq_synth_normal_f16": (c_i32, [c_vp, c_i64, c_u64, c_u64, c_i64, c_f64, c_vp]),
     "fq_synth_token_ids": (c_i32, [c_vp, c_i64, c_u64, c_u64, c_i32, c_vp]),
+    "fq_set_progress": (None, [c_vp, c_vp]),
     "fq_timing_start": (c_i32, []),
     "fq_timing_stop": (c_i32, [_P(fq_kernel_stats)]),
 }
@@ -291,6 +292,22 @@ class KVCache:
 
 def fq_layer_step(model, layer, kv, b0, B, T, pos, x, y, stream=None):
     _check(_lib.fq_layer_step(model.handle, layer, kv.handle, b0, B, T, pos, _ptr(x), _ptr(y), _stream(stream)))
+
+
+_PROGRESS_FN = ctypes.CFUNCTYPE(None, c_i64, c_i64, c_vp)
+_progress_keep = None
+
+
+def fq_set_progress(fn):
+    """fn(done, total) is called as each generated token's step finishes on
+    the device during fq_generate; None disables it."""
+    global _progress_keep
+    if fn is None:
+        _progress_keep = None
+        _lib.fq_set_progress(None, None)
+        return
+    _progress_keep = _PROGRESS_FN(lambda done, total, user: fn(done, total))
+    _lib.fq_set_progress(ctypes.cast(_progress_keep, c_vp), None)
 
 
 def fq_generate(model, kv, prompt_ids, gen_len, logits=None, stream=None):

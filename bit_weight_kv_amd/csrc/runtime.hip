@@ -583,6 +583,16 @@ extern "C" fq_status fq_layer_step(fq_model* m, int32_t layer, fq_kv* kv, int64_
   return layer_compute(m, layer, v, b0, B, T, pos, x, y, nullptr, st);
 }
 
+namespace {
+fq_progress_fn g_progress = nullptr;
+void* g_progress_user = nullptr;
+}  // namespace
+
+extern "C" void fq_set_progress(fq_progress_fn fn, void* user) {
+  g_progress = fn;
+  g_progress_user = user;
+}
+
 extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_ids, int64_t B, int64_t P,
                                  int64_t gen_len, int32_t* out_ids, float* logits, fq_gen_stats* stats, void* stream) {
   clear_error();
@@ -610,6 +620,14 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
 
   hipEvent_t ev[3];
   for (int i = 0; i < 3; ++i) FQ_HIP(hipEventCreate(&ev[i]));
+  const fq_progress_fn progress = g_progress;
+  void* const progress_user = g_progress_user;
+  std::vector<hipEvent_t> step_ev;
+  int64_t reported = 0;  // steps reported to `progress`
+  if (progress) {
+    step_ev.resize(gen_len);
+    for (auto& e : step_ev) FQ_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
   auto run = [&]() -> fq_status {
     FQ_HIP(hipEventRecord(ev[0], st));
     FQ_HIP(hipMemcpyAsync(d_prompt, prompt_ids, (size_t)B * P * 4, hipMemcpyHostToDevice, st));
@@ -634,12 +652,25 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
       FQ_TRY(fq_dequant_gemm(m->h1, B, h, &head, nullptr, nullptr, 0, FQ_EPI_F32OUT, 1.f, 0, lg, V, (void*)st));
       FQ_TRY(launch_argmax(lg, B, V, V, d_out + step * B, st));
       if (step == 0) FQ_HIP(hipEventRecord(ev[1], st));
+      if (progress) {
+        FQ_HIP(hipEventRecord(step_ev[step], st));
+        // queueing is paced by the device once its queue is full: report the
+        // steps already finished (non-blocking query, in order)
+        while (reported < step && hipEventQuery(step_ev[reported]) == hipSuccess) {
+          ++reported;
+          progress(reported, gen_len, progress_user);
+        }
+      }
       if (step + 1 == gen_len) break;
       const int64_t pos = P + step;  // position of the token just generated
       FQ_TRY(launch_embed(d_out + step * B, B, 1, pos, m->embed, m->pos, h, x, st));
       FQ_TRY(run_layers(m, kv, B, 1, pos, x, B, st));
     }
     FQ_HIP(hipEventRecord(ev[2], st));
+    for (; progress && reported < gen_len; ++reported) {
+      FQ_HIP(hipEventSynchronize(step_ev[reported]));
+      progress(reported + 1, gen_len, progress_user);
+    }
     FQ_HIP(hipEventSynchronize(ev[2]));
     FQ_TRY(stream_collect(m));
     // d_out is [gen_len, B]; out_ids is [B, gen_len]
@@ -661,5 +692,6 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
   };
   fq_status s = run();
   for (int i = 0; i < 3; ++i) (void)hipEventDestroy(ev[i]);
+  for (auto& e : step_ev) (void)hipEventDestroy(e);
   return s;
 }

@@ -284,6 +284,17 @@ typedef struct {
 fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_ids, int64_t B, int64_t P, int64_t gen_len,
                       int32_t* out_ids, float* logits, fq_gen_stats* stats, void* stream);
 
+/* Optional progress report for long generations: fq_generate calls
+ * fn(done, gen_len, user) once per generated token, in order
+ * (done = 1..gen_len), from the calling thread, after that token's step has
+ * finished on the device -- while it queues later steps (a non-blocking
+ * query between steps) and, once everything is queued, by waiting for the
+ * remaining steps in order.  NULL disables it (the default).  Process-wide;
+ * not synchronised with concurrent fq_generate calls.  The device timing is
+ * unchanged. */
+typedef void (*fq_progress_fn)(int64_t done, int64_t total, void* user);
+void fq_set_progress(fq_progress_fn fn, void* user);
+
 /* ------------------------------------------------------------------------ */
 /* Per-launch device timing (HIP events on the launching stream), grouped by
  * kernel class, with each launch's algorithmic work: flops of the

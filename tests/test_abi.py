@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "fq.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:fq_status|const char\*)\s+(fq_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:fq_status|const char\*|void)\s+(fq_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_five_calls():

@@ -96,3 +96,17 @@ def test_streamed_shared_host_blobs_match_oracle():
     lps = [oracle.layer_params(3, cfg, l % 2) for l in range(L)]
     ref = oracle.generate(ids, G, 3, mcfg, layers_params=lps)
     _compare(out, lg, ref, "streamed fp16")
+
+
+def test_progress_callback_reports_every_token_in_order():
+    L, B, P, G = 2, 2, 8, 5
+    seen = []
+    fq.fq_set_progress(lambda done, total: seen.append((done, total)))
+    try:
+        ids, out, lg, _ = _gpu_generate(L, B, P, G, seed=3)
+    finally:
+        fq.fq_set_progress(None)
+    assert seen == [(t, G) for t in range(1, G + 1)]
+    # the report changes nothing: same tokens and logits without it
+    _, out2, lg2, _ = _gpu_generate(L, B, P, G, seed=3)
+    assert np.array_equal(out, out2) and np.array_equal(lg, lg2)
