@@ -38,6 +38,11 @@ CONFIGS = {
                                   desc="OPT-175B shape, fp16 weights streamed layer by layer from pinned host memory "
                                        "(12 distinct host layer blobs, layer l reads blob l mod 12: the GPU host "
                                        "allows ~58 GB of pinned memory per process), 4-bit KV"),
+    "opt175b-4bit-b256-offload": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=256, prompt=512,
+                                      gen=32, compress_weight=True, resident_layers=78,
+                                      desc="OPT-175B shape, batch 256: the 4-bit KV cache (184 GB) leaves HBM for 78 "
+                                           "layers of 4-bit weights; the other 18 stream from pinned host memory in "
+                                           "packed form (0.5625 byte per weight) every pass"),
     "tiny-2layer": dict(hidden=256, heads=4, ffn=1024, layers=2, vocab=512, batch=8, prompt=64, gen=5,
                         compress_weight=True, desc="tiny OPT-style model for smoke benchmarking"),
 }

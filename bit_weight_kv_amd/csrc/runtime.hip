@@ -13,10 +13,12 @@
 //
 // Schedule.  Prefill is layer-major: each layer is applied to every chunk of
 // sequences before the next layer starts, so a streamed layer is copied once
-// per pass and serves the whole batch (the block schedule).  Streamed fp16
-// weights use two device staging buffers: a copy stream fills buffer
-// (l+1)%2 while the compute stream runs layer l from buffer l%2; events
-// copied[s] and consumed[s] order the two streams (no host waits).
+// per pass and serves the whole batch (the block schedule).  Streamed layers
+// (fp16, or packed 4-bit codes + {min, scale} when weights are compressed:
+// 3.56x fewer bytes over the host link) use two device staging buffers: a
+// copy stream fills buffer (l+1)%2 while the compute stream runs layer l from
+// buffer l%2; events copied[s] and consumed[s] order the two streams (no
+// host waits).
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -56,8 +58,8 @@ struct fq_model {
   int64_t max_tokens = 0;
   uint16_t *h1 = nullptr, *qkv = nullptr, *att = nullptr, *x1 = nullptr, *f = nullptr;
   // streaming
-  std::vector<uint16_t*> host_blobs;  // pinned host, one layer each
-  uint16_t* stage[2] = {nullptr, nullptr};
+  std::vector<uint8_t*> host_blobs;  // pinned host, one layer each (fp16 or packed)
+  uint8_t* stage[2] = {nullptr, nullptr};
   hipStream_t copy_stream = nullptr;
   hipEvent_t copied[2] = {nullptr, nullptr};
   hipEvent_t consumed[2] = {nullptr, nullptr};
@@ -79,7 +81,13 @@ struct fq_model {
   int64_t d() const { return cfg.hidden / cfg.heads; }
   int64_t layer_elems() const { return 4 * h() * h() + 2 * h() * F(); }
   int64_t small_elems() const { return 3 * h() + h() + F() + h() + 4 * h(); }
-  bool streamed(int l) const { return !pol.compress_weight && layers[l].host_blob >= 0; }
+  // bytes of one layer's weights as stored in a host blob / staging buffer:
+  // fp16, or packed codes + {min, scale} (0.5625 byte per weight)
+  size_t blob_bytes() const {
+    return pol.compress_weight ? (size_t)layer_elems() / 2 + (size_t)layer_elems() / 64 * 4
+                               : (size_t)layer_elems() * 2;
+  }
+  bool streamed(int l) const { return layers[l].host_blob >= 0; }
 };
 
 struct fq_kv {
@@ -114,6 +122,26 @@ void blob_slices(const fq_model* m, uint16_t* base, uint16_t* w[4]) {
   w[3] = w[2] + F * h;
 }
 
+void weight_shape(const fq_model* m, int which, int64_t* n, int64_t* k);
+
+// Packed weights of one layer inside a blob [codes qkv | meta qkv | codes out
+// | meta out | codes fc1 | meta fc1 | codes fc2 | meta fc2] (every part a
+// multiple of 256 bytes, so each keeps the GEMM's 16-byte alignment).
+void packed_slices(const fq_model* m, uint8_t* base, fq_packed w[4]) {
+  uint8_t* cur = base;
+  for (int k = 0; k < 4; ++k) {
+    int64_t n, kk;
+    weight_shape(m, k, &n, &kk);
+    w[k].rows = n;
+    w[k].cols = kk;
+    w[k].group = FQ_GROUP;
+    w[k].codes = cur;
+    cur += (size_t)n * kk / 2;
+    w[k].meta = reinterpret_cast<uint16_t*>(cur);
+    cur += (size_t)n * (kk / 64) * 4;
+  }
+}
+
 void weight_shape(const fq_model* m, int which, int64_t* n, int64_t* k) {
   const int64_t h = m->h(), F = m->F();
   const int64_t N[4] = {3 * h, h, F, h}, K[4] = {h, h, h, F};
@@ -121,29 +149,42 @@ void weight_shape(const fq_model* m, int which, int64_t* n, int64_t* k) {
   *k = K[which];
 }
 
-// Device weight operand of layer l (after any staging).
-fq_weight layer_weight(const fq_model* m, int l, int which, uint16_t* const staged16[4]) {
+// Device weight operand of layer l: its resident copy, or the slice of the
+// staging buffer its host blob was copied into.
+fq_weight layer_weight(const fq_model* m, int l, int which, uint8_t* staged) {
   fq_weight w{};
   weight_shape(m, which, &w.n, &w.k);
   if (m->pol.compress_weight) {
     w.kind = FQ_WEIGHT_PACKED4;
-    w.packed = m->layers[l].w[which];
+    if (staged) {
+      fq_packed p[4];
+      packed_slices(m, staged, p);
+      w.packed = p[which];
+    } else {
+      w.packed = m->layers[l].w[which];
+    }
   } else {
     w.kind = FQ_WEIGHT_F16;
-    w.w16 = staged16 ? staged16[which] : m->layers[l].w16[which];
+    if (staged) {
+      uint16_t* p[4];
+      blob_slices(m, reinterpret_cast<uint16_t*>(staged), p);
+      w.w16 = p[which];
+    } else {
+      w.w16 = m->layers[l].w16[which];
+    }
   }
   return w;
 }
 
 // The core of one decoder layer over M = B*T rows (see fq_layer_step).
 fq_status layer_compute(fq_model* m, int l, const fq_kv_layer& kv, int64_t b0, int64_t B, int64_t T, int64_t pos,
-                        const uint16_t* x, uint16_t* y, uint16_t* const staged16[4], hipStream_t st) {
+                        const uint16_t* x, uint16_t* y, uint8_t* staged, hipStream_t st) {
   const int64_t h = m->h(), F = m->F(), M = B * T;
   const uint16_t* sp = m->layers[l].small;
   const uint16_t *b_qkv = sp, *b_out = sp + 3 * h, *b_fc1 = b_out + h, *b_fc2 = b_fc1 + F;
   const uint16_t *ln1g = b_fc2 + h, *ln1b = ln1g + h, *ln2g = ln1b + h, *ln2b = ln2g + h;
-  const fq_weight wq = layer_weight(m, l, 0, staged16), wo = layer_weight(m, l, 1, staged16),
-                  w1 = layer_weight(m, l, 2, staged16), w2 = layer_weight(m, l, 3, staged16);
+  const fq_weight wq = layer_weight(m, l, 0, staged), wo = layer_weight(m, l, 1, staged),
+                  w1 = layer_weight(m, l, 2, staged), w2 = layer_weight(m, l, 3, staged);
   void* s = (void*)st;
   FQ_TRY(fq_layernorm(x, M, h, h, ln1g, ln1b, 1e-5f, m->h1, h, s));
   const float qscale = 1.0f / std::sqrt((float)m->d());
@@ -167,7 +208,7 @@ fq_status layer_compute(fq_model* m, int l, const fq_kv_layer& kv, int64_t b0, i
 fq_status stream_issue(fq_model* m, int l) {
   const int slot = l & 1;
   if (m->staged[slot] == l) return FQ_OK;
-  const size_t bytes = (size_t)m->layer_elems() * 2;
+  const size_t bytes = m->blob_bytes();
   if (m->n_copies == m->copy_ev.size()) {
     hipEvent_t a, b;
     FQ_HIP(hipEventCreate(&a));
@@ -206,14 +247,12 @@ fq_status run_layers(fq_model* m, fq_kv* kv, int64_t B, int64_t T, int64_t pos, 
   const int L = m->cfg.layers;
   const int64_t h = m->h();
   for (int l = 0; l < L; ++l) {
-    uint16_t* staged16[4] = {nullptr, nullptr, nullptr, nullptr};
-    uint16_t* const* sp = nullptr;
+    uint8_t* sp = nullptr;
     if (m->streamed(l)) {
       const int slot = l & 1;
       FQ_TRY(stream_issue(m, l));  // no-op when prefetched during layer l-1
       FQ_HIP(hipStreamWaitEvent(st, m->copied[slot], 0));
-      blob_slices(m, m->stage[slot], staged16);
-      sp = staged16;
+      sp = m->stage[slot];
     }
     // prefetch layer l+1 into the other slot while layer l computes
     if (m->pol.overlap && l + 1 < L && m->streamed(l + 1)) FQ_TRY(stream_issue(m, l + 1));
@@ -277,32 +316,22 @@ extern "C" fq_status fq_model_create(const fq_model_config* cfg, const fq_policy
   const int L = cfg->layers;
   const int64_t h = m->h(), F = m->F();
   m->layers.resize(L);
-  const int resident = (policy->compress_weight || policy->resident_layers < 0) ? L
-                                                                                : std::min(L, policy->resident_layers);
+  const int resident = policy->resident_layers < 0 ? L : std::min(L, policy->resident_layers);
   const int streamed = L - resident;
   const int nblobs = streamed == 0 ? 0 : (policy->host_layers > 0 ? std::min(streamed, policy->host_layers) : streamed);
   for (int l = 0; l < L; ++l) {
     LayerStore& ls = m->layers[l];
     fq_status s;
-    for (int w = 0; w < 4; ++w) {
-      int64_t n, k;
-      weight_shape(m, w, &n, &k);
-      if (policy->compress_weight) {
-        ls.w[w].rows = n;
-        ls.w[w].cols = k;
-        ls.w[w].group = FQ_GROUP;
-        if ((s = dmalloc(m, (void**)&ls.w[w].codes, (size_t)n * k / 2, "packed codes")) != FQ_OK) return bail(s);
-        if ((s = dmalloc(m, (void**)&ls.w[w].meta, (size_t)n * (k / 64) * 4, "packed meta")) != FQ_OK) return bail(s);
-      }
-    }
-    if (!policy->compress_weight) {
-      if (l < resident) {
-        uint16_t* blob = nullptr;
-        if ((s = dmalloc(m, (void**)&blob, (size_t)m->layer_elems() * 2, "fp16 layer")) != FQ_OK) return bail(s);
-        blob_slices(m, blob, ls.w16);
-      } else {
-        ls.host_blob = (l - resident) % nblobs;
-      }
+    if (l >= resident) {
+      ls.host_blob = (l - resident) % nblobs;
+    } else if (policy->compress_weight) {
+      uint8_t* blob = nullptr;
+      if ((s = dmalloc(m, (void**)&blob, m->blob_bytes(), "packed layer")) != FQ_OK) return bail(s);
+      packed_slices(m, blob, ls.w);
+    } else {
+      uint16_t* blob = nullptr;
+      if ((s = dmalloc(m, (void**)&blob, m->blob_bytes(), "fp16 layer")) != FQ_OK) return bail(s);
+      blob_slices(m, blob, ls.w16);
     }
     if ((s = dmalloc(m, (void**)&ls.small, (size_t)m->small_elems() * 2, "layer vectors")) != FQ_OK) return bail(s);
   }
@@ -321,7 +350,7 @@ extern "C" fq_status fq_model_create(const fq_model_config* cfg, const fq_policy
   if (nblobs > 0) {
     m->host_blobs.assign(nblobs, nullptr);
     for (int i = 0; i < nblobs; ++i) {
-      hipError_t e = hipHostMalloc((void**)&m->host_blobs[i], (size_t)m->layer_elems() * 2, hipHostMallocDefault);
+      hipError_t e = hipHostMalloc((void**)&m->host_blobs[i], m->blob_bytes(), hipHostMallocDefault);
       if (e != hipSuccess) {
         (void)hipGetLastError();
         m->host_blobs[i] = nullptr;
@@ -329,7 +358,7 @@ extern "C" fq_status fq_model_create(const fq_model_config* cfg, const fq_policy
       }
     }
     for (int k = 0; k < 2; ++k) {
-      if ((s = dmalloc(m, (void**)&m->stage[k], (size_t)m->layer_elems() * 2, "staging")) != FQ_OK) return bail(s);
+      if ((s = dmalloc(m, (void**)&m->stage[k], m->blob_bytes(), "staging")) != FQ_OK) return bail(s);
       if (hipEventCreateWithFlags(&m->copied[k], hipEventDisableTiming) != hipSuccess ||
           hipEventCreateWithFlags(&m->consumed[k], hipEventDisableTiming) != hipSuccess)
         return bail(fail(FQ_ERR_HIP, "fq_model_create: event creation failed"));
@@ -345,7 +374,7 @@ extern "C" fq_status fq_model_destroy(fq_model* m) {
   if (!m) return FQ_OK;
   (void)hipDeviceSynchronize();
   for (void* p : m->allocs) (void)hipFree(p);
-  for (uint16_t* p : m->host_blobs)
+  for (uint8_t* p : m->host_blobs)
     if (p) (void)hipHostFree(p);
   for (int k = 0; k < 2; ++k) {
     if (m->copied[k]) (void)hipEventDestroy(m->copied[k]);
@@ -367,19 +396,29 @@ fq_status set_layer(fq_model* m, int l, const fq_layer_weights* w, hipStream_t s
   const int64_t h = m->h(), F = m->F();
   LayerStore& ls = m->layers[l];
   const uint16_t* src[4] = {w->w_qkv, w->w_out, w->w_fc1, w->w_fc2};
+  fq_packed staged[4];
+  if (m->pol.compress_weight && ls.host_blob >= 0) {
+    // quantise into staging slot 0 (no generation is running), then copy the
+    // packed layer to its host blob
+    FQ_HIP(hipDeviceSynchronize());
+    packed_slices(m, m->stage[0], staged);
+    m->staged[0] = -1;
+  }
   for (int k = 0; k < 4; ++k) {
     int64_t n, kk;
     weight_shape(m, k, &n, &kk);
     if (m->pol.compress_weight) {
-      FQ_TRY(fq_quantize(src[k], n, kk, kk, &ls.w[k], (void*)st));
+      FQ_TRY(fq_quantize(src[k], n, kk, kk, ls.host_blob >= 0 ? &staged[k] : &ls.w[k], (void*)st));
     } else if (ls.host_blob < 0) {
       FQ_HIP(hipMemcpyAsync(ls.w16[k], src[k], (size_t)n * kk * 2, hipMemcpyDeviceToDevice, st));
     } else {
       uint16_t* hw[4];
-      blob_slices(m, m->host_blobs[ls.host_blob], hw);
+      blob_slices(m, reinterpret_cast<uint16_t*>(m->host_blobs[ls.host_blob]), hw);
       FQ_HIP(hipMemcpyAsync(hw[k], src[k], (size_t)n * kk * 2, hipMemcpyDeviceToHost, st));
     }
   }
+  if (m->pol.compress_weight && ls.host_blob >= 0)
+    FQ_HIP(hipMemcpyAsync(m->host_blobs[ls.host_blob], m->stage[0], m->blob_bytes(), hipMemcpyDeviceToHost, st));
   const uint16_t* vec[8] = {w->b_qkv, w->b_out, w->b_fc1, w->b_fc2, w->ln1_g, w->ln1_b, w->ln2_g, w->ln2_b};
   const int64_t len[8] = {3 * h, h, F, h, h, h, h, h};
   uint16_t* dst = ls.small;
@@ -401,7 +440,7 @@ extern "C" fq_status fq_model_set_layer(fq_model* m, int32_t layer, const fq_lay
                "fq_model_set_layer: NULL parameter");
   hipStream_t st = as_stream(stream);
   FQ_TRY(set_layer(m, layer, w, st));
-  if (!m->pol.compress_weight && m->layers[layer].host_blob >= 0) FQ_HIP(hipStreamSynchronize(st));
+  if (m->layers[layer].host_blob >= 0) FQ_HIP(hipStreamSynchronize(st));
   return FQ_OK;
 }
 
@@ -500,6 +539,8 @@ extern "C" fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, in
   FQ_CHECK_ARG(m && out, "fq_model_packed_weight: NULL argument");
   FQ_CHECK_ARG(layer >= 0 && layer < m->cfg.layers && which >= 0 && which < 4, "fq_model_packed_weight: bad index");
   if (!m->pol.compress_weight) return fail(FQ_ERR_INVALID, "fq_model_packed_weight: weights are not compressed");
+  if (m->layers[layer].host_blob >= 0)
+    return fail(FQ_ERR_INVALID, "fq_model_packed_weight: layer is streamed from host memory");
   *out = m->layers[layer].w[which];
   return FQ_OK;
 }
@@ -573,12 +614,10 @@ extern "C" fq_status fq_layer_step(fq_model* m, int32_t layer, fq_kv* kv, int64_
   hipStream_t st = as_stream(stream);
   if (m->streamed(layer)) {
     // synchronous staging of a host-resident layer into slot 0
-    const size_t bytes = (size_t)m->layer_elems() * 2;
-    FQ_HIP(hipMemcpyAsync(m->stage[0], m->host_blobs[m->layers[layer].host_blob], bytes, hipMemcpyHostToDevice, st));
+    FQ_HIP(hipMemcpyAsync(m->stage[0], m->host_blobs[m->layers[layer].host_blob], m->blob_bytes(),
+                          hipMemcpyHostToDevice, st));
     m->staged[0] = -1;
-    uint16_t* staged16[4];
-    blob_slices(m, m->stage[0], staged16);
-    return layer_compute(m, layer, v, b0, B, T, pos, x, y, staged16, st);
+    return layer_compute(m, layer, v, b0, B, T, pos, x, y, m->stage[0], st);
   }
   return layer_compute(m, layer, v, b0, B, T, pos, x, y, nullptr, st);
 }

@@ -192,12 +192,14 @@ typedef struct {
 /* Placement policy (FlexGen README, "Get Started": --percent places weights
  * and cache; "Handle Out-of-memory": --compress-weight, --pin-weight). */
 typedef struct {
-  int32_t compress_weight; /* 1: 4-bit packed weights resident in HBM; 0: fp16 weights */
+  int32_t compress_weight; /* 1: 4-bit packed weights (group 64); 0: fp16 weights */
   int32_t compress_cache;  /* must be 1 (4-bit KV cache) */
-  int32_t resident_layers; /* fp16 weights only: layers kept in HBM, the rest live in
-                              pinned host memory and are streamed; -1 = all resident */
-  int32_t host_layers;     /* fp16 streamed weights: distinct host layer blobs; layer l
-                              reads blob (l - resident_layers) % host_layers; 0 = one per layer */
+  int32_t resident_layers; /* layers 0..resident_layers-1 are kept in HBM; the rest live in
+                              pinned host memory -- packed (0.5625 byte per weight) when
+                              compress_weight, else fp16 -- and are streamed through two
+                              device staging buffers; -1 = all resident */
+  int32_t host_layers;     /* streamed layers: distinct host layer blobs; layer l reads blob
+                              (l - resident_layers) % host_layers; 0 = one per layer */
   int32_t overlap;         /* 1: prefetch layer l+1 on a copy stream while layer l computes */
   int64_t max_tokens;      /* rows of the per-call activation workspace (0: default 16384) */
 } fq_policy;

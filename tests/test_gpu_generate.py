@@ -98,6 +98,46 @@ def test_streamed_shared_host_blobs_match_oracle():
     _compare(out, lg, ref, "streamed fp16")
 
 
+def test_streamed_packed_weights_equal_resident():
+    """4-bit weights: all resident vs. layers 1..3 streamed in packed form
+    (codes + {min, scale}, 0.5625 byte per weight) from pinned host memory,
+    with and without overlap: identical tokens and logits."""
+    L, B, P, G = 4, 2, 10, 4
+    log("packed streaming equivalence")
+    _, a_out, a_lg, a_st = _gpu_generate(L, B, P, G, seed=2)
+    _, b_out, b_lg, b_st = _gpu_generate(L, B, P, G, seed=2, resident_layers=1)
+    _, c_out, c_lg, c_st = _gpu_generate(L, B, P, G, seed=2, resident_layers=1, overlap=False)
+    assert np.array_equal(a_out, b_out) and np.array_equal(a_lg, b_lg)
+    assert np.array_equal(a_out, c_out) and np.array_equal(a_lg, c_lg)
+    elems = 4 * H * H + 2 * H * F
+    layer_bytes = elems // 2 + elems // 64 * 4
+    assert a_st.h2d_bytes == 0
+    assert b_st.h2d_bytes == (3 + 2 * (G - 1)) * layer_bytes and b_st.h2d_s > 0
+
+
+def test_streamed_packed_shared_host_blobs_match_oracle():
+    """4 layers of 4-bit weights all streamed from 2 packed host blobs: layer l
+    holds the weights generated for layer l % 2; the oracle runs the same
+    tied-weight model."""
+    L, B, P, G = 4, 2, 8, 4
+    ids, out, lg, st = _gpu_generate(L, B, P, G, seed=4, resident_layers=0, host_layers=2)
+    cfg = LayerConfig(H, NH, F)
+    mcfg = ModelConfig(cfg, L, V, P + G + 2)
+    lps = [oracle.layer_params(4, cfg, l % 2) for l in range(L)]
+    ref = oracle.generate(ids, G, 4, mcfg, layers_params=lps)
+    _compare(out, lg, ref, "streamed 4-bit")
+
+
+def test_packed_weight_of_streamed_layer_is_rejected():
+    model = fq.Model(H, NH, F, 2, vocab=V, max_pos=16, resident_layers=1)
+    try:
+        model.packed_weight(0, 0)
+        with pytest.raises(fq.FqError):
+            model.packed_weight(1, 0)
+    finally:
+        model.close()
+
+
 def test_progress_callback_reports_every_token_in_order():
     L, B, P, G = 2, 2, 8, 5
     seen = []
