@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--ceilings", action="store_true",
                     help="measure this GPU's practical ceilings (HBM copy stream, pinned host<->device copies, "
                          "the vendor library's fp16 GEMM at the prefill shape) and print them as one JSON line")
-    ap.add_argument("--kernel-only", choices=["gemm_prefill"], default=None,
+    ap.add_argument("--kernel-only", choices=["gemm_prefill", "gemm_decode", "decode_attention"], default=None,
                     help="launch only this kernel class, as one layer of the workload launches it (a short program "
                          "for hardware-counter passes); prints the launch list instead of the JSON line")
     return ap.parse_args()
@@ -84,7 +84,10 @@ def measured_traffic(kernel):
     since the counters were taken."""
     import hashlib
     import re
-    summary = {"gemm_prefill": ("profiles/gemm_prefill_opt175b_4bit_b144.md", "bit_weight_kv_amd/csrc/gemm.hip")}
+    summary = {"gemm_prefill": ("profiles/gemm_prefill_opt175b_4bit_b144.md", "bit_weight_kv_amd/csrc/gemm.hip"),
+               "gemm_decode": ("profiles/gemm_decode_opt175b_4bit_b144.md", "bit_weight_kv_amd/csrc/gemm.hip"),
+               "decode_attention": ("profiles/decode_attention_opt175b_4bit_b144.md",
+                                    "bit_weight_kv_amd/csrc/attention.hip")}
     if kernel not in summary:
         return None
     md, src = (os.path.join(ROOT, f) for f in summary[kernel])
@@ -123,7 +126,7 @@ def roofline(kstats, config):
     return name, r
 
 
-def kernel_table(kstats):
+def kernel_table(kstats, config):
     out = {}
     for name, st in kstats.items():
         if st["launches"] == 0:
@@ -136,6 +139,10 @@ def kernel_table(kstats):
         if st["bytes"] > 0:
             e["gbs"] = round(st["bytes"] / st["seconds"] / 1e9, 1)
             e["hbm_frac"] = round(st["bytes"] / st["seconds"] / 1e9 / PEAK_HBM_GBS, 4)
+        if config == "opt175b-4bit":
+            t = measured_traffic(name)
+            if t is not None:
+                e["traffic_per_launch"] = t
         out[name] = e
     return out
 
@@ -257,11 +264,45 @@ def ceilings(torch):
 
 
 def kernel_only(fq, synth, torch, cfg, args):
-    """The prefill GEMMs of one layer, exactly as the prompt pass launches them:
-    the batch's B*P prompt rows in chunks of at most --max-tokens rows, each
-    chunk through the QKV (bias, query scaling), out (bias, residual), FC1
-    (bias, ReLU) and FC2 (bias, residual) products of that layer's packed
-    weights.  Every layer of the workload repeats this launch list."""
+    if args.kernel_only == "gemm_prefill":
+        return kernel_only_gemm(fq, synth, torch, cfg, args, prefill=True)
+    if args.kernel_only == "gemm_decode":
+        return kernel_only_gemm(fq, synth, torch, cfg, args, prefill=False)
+    return kernel_only_decode_attention(fq, synth, torch, cfg, args)
+
+
+def kernel_only_decode_attention(fq, synth, torch, cfg, args):
+    """Decode attention of one layer at three cache lengths of the workload's
+    decode steps (first, middle, last): B sequences x H heads over a packed
+    cache of capacity P + G - 1 (contents are seeded random codes and
+    {min, scale} pairs; the traffic does not depend on them)."""
+    h, H, B, P, G = cfg["hidden"], cfg["heads"], cfg["batch"], cfg["prompt"], cfg["gen"]
+    d, S = h // H, P + G - 1
+    gen = torch.Generator(device="cuda").manual_seed(args.seed)
+    kc = torch.randint(0, 256, (B, H, S, d // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    vc = torch.randint(0, 256, (B, H, S, d // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    km = torch.empty((B, H, S, d // 64, 2), dtype=torch.float16, device="cuda")
+    km[..., 0], km[..., 1] = -0.05, 0.006
+    vm = km.clone()
+    kv = fq.kv_layer_view(kc, km.view(torch.int16), vc, vm.view(torch.int16))
+    q = torch.empty((B, 3 * h), dtype=torch.float16, device="cuda")
+    fq.fq_synth_normal_f16(q, args.seed, synth.STREAM["aux"], 1.0)
+    out = torch.empty((B, h), dtype=torch.float16, device="cuda")
+    launches = []
+    for length in (P + 1, P + G // 2, P + G - 1):
+        fq.fq_decode_attention(q, kv, 0, B, length, out, ldq=3 * h)
+        launches.append([B, H, length, d])
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": args.kernel_only, "launches": launches}), flush=True)
+
+
+def kernel_only_gemm(fq, synth, torch, cfg, args, prefill):
+    """The projection GEMMs of one layer, exactly as the prompt pass (prefill)
+    or one decode step launches them: the batch's B*P prompt rows in chunks of
+    at most --max-tokens rows (or the B rows of a decode step), each chunk
+    through the QKV (bias, query scaling), out (bias, residual), FC1 (bias,
+    ReLU) and FC2 (bias, residual) products of that layer's packed weights.
+    Every layer of the workload repeats this launch list."""
     h, F, B, P = cfg["hidden"], cfg["ffn"], cfg["batch"], cfg["prompt"]
     model = fq.Model(h, cfg["heads"], F, 1, vocab=cfg["vocab"], max_pos=P + cfg["gen"] + 2,
                      compress_weight=True, max_tokens=args.max_tokens)
@@ -269,7 +310,8 @@ def kernel_only(fq, synth, torch, cfg, args):
     shapes = {0: (3 * h, h), 1: (h, h), 2: (F, h), 3: (h, F)}
     W = {i: fq.fq_weight(fq.FQ_WEIGHT_PACKED4, model.packed_weight(0, i), None, n, k)
          for i, (n, k) in shapes.items()}
-    rows = min(B * P, args.max_tokens)
+    total = B * P if prefill else B  # a decode step runs every sequence's one new row
+    rows = min(total, args.max_tokens)
     def act(cols, stream):
         t = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
         fq.fq_synth_normal_f16(t, args.seed, stream, 1.0)
@@ -280,8 +322,8 @@ def kernel_only(fq, synth, torch, cfg, args):
     bias = torch.zeros(max(3 * h, F), dtype=torch.float16, device="cuda")
     E = fq
     launches = []
-    for r0 in range(0, B * P, args.max_tokens):
-        M = min(args.max_tokens, B * P - r0)
+    for r0 in range(0, total, args.max_tokens):
+        M = min(args.max_tokens, total - r0)
         fq.fq_dequant_gemm(h1[:M], W[0], qkv[:M], bias=bias, epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_QSCALE,
                            qscale=(h // cfg["heads"]) ** -0.5, qscale_cols=h)
         fq.fq_dequant_gemm(att[:M], W[1], x1[:M], bias=bias, residual=x[:M],
@@ -376,7 +418,7 @@ def main():
                    "h2d_GB": round(float(np.mean([s[2] for s in stats])) / 1e9, 2),
                    "h2d_busy_s": round(float(np.mean([s[3] for s in stats])), 3)},
         "roofline": roof,
-        "kernels": kernel_table(kstats),
+        "kernels": kernel_table(kstats, args.config),
     }
     kv.close()
     model.close()
