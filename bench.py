@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 CONFIGS = {
-    # name: (hidden, heads, ffn, layers, vocab, batch, prompt, gen, compress_weight, streaming knobs)
+    # name: (hidden, heads, ffn, layers, vocab, batch, prompt, gen, compression switches, streaming knobs)
     "opt175b-4bit": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=144, prompt=512, gen=32,
                          compress_weight=True, desc="OPT-175B shape, 4-bit g64 weights + 4-bit KV resident in HBM"),
     "opt30b-4bit": dict(hidden=7168, heads=56, ffn=28672, layers=48, vocab=50272, batch=256, prompt=512, gen=32,
@@ -43,6 +43,10 @@ CONFIGS = {
                                       desc="OPT-175B shape, batch 256: the 4-bit KV cache (184 GB) leaves HBM for 78 "
                                            "layers of 4-bit weights; the other 18 stream from pinned host memory in "
                                            "packed form (0.5625 byte per weight) every pass"),
+    "opt175b-4bit-weights-f16-cache": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=48,
+                                           prompt=512, gen=32, compress_weight=True, compress_cache=False,
+                                           desc="OPT-175B shape, weight-only compression: 4-bit g64 weights, fp16 KV "
+                                                "cache (2 bytes per element: 123 GB at batch 48), all in HBM"),
     "tiny-2layer": dict(hidden=256, heads=4, ffn=1024, layers=2, vocab=512, batch=8, prompt=64, gen=5,
                         compress_weight=True, desc="tiny OPT-style model for smoke benchmarking"),
 }
@@ -166,7 +170,8 @@ def cpu_baseline(cfg, seed):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     h, H, F = cfg["hidden"], cfg["heads"], cfg["ffn"]
-    lcfg = oracle.LayerConfig(h, H, F, compress_weight=cfg["compress_weight"])
+    lcfg = oracle.LayerConfig(h, H, F, compress_weight=cfg["compress_weight"],
+                              compress_cache=cfg.get("compress_cache", True))
     workers = os.cpu_count() or 1
     t0 = time.time()
 
@@ -374,7 +379,8 @@ def main():
     t0 = time.time()
     model = fq.Model(cfg["hidden"], cfg["heads"], cfg["ffn"], cfg["layers"], vocab=cfg["vocab"], max_pos=P + G + 2,
                      compress_weight=cfg["compress_weight"], resident_layers=cfg.get("resident_layers", -1),
-                     host_layers=cfg.get("host_layers", 0), overlap=True, max_tokens=args.max_tokens)
+                     host_layers=cfg.get("host_layers", 0), overlap=True, max_tokens=args.max_tokens,
+                     compress_cache=cfg.get("compress_cache", True))
     model.init_random(args.seed)
     kv = fq.KVCache(model, B, P + G)
     last = [time.time()]

@@ -43,7 +43,8 @@ class fq_weight(ctypes.Structure):
 
 class fq_kv_layer(ctypes.Structure):
     _fields_ = [("k_codes", c_vp), ("k_meta", c_vp), ("v_codes", c_vp), ("v_meta", c_vp), ("batch", c_i64),
-                ("heads", c_i32), ("head_dim", c_i32), ("capacity", c_i64), ("group", c_i32)]
+                ("heads", c_i32), ("head_dim", c_i32), ("capacity", c_i64), ("group", c_i32), ("bits", c_i32),
+                ("k16", c_vp), ("v16", c_vp)]
 
 
 class fq_model_config(ctypes.Structure):
@@ -178,8 +179,15 @@ def kv_layer_view(k_codes, k_meta, v_codes, v_meta):
     """fq_kv_layer over torch tensors: codes uint8 [B, H, S, d/2], meta int16 [B, H, S, d/64, 2]."""
     B, H, S, half = k_codes.shape
     v = fq_kv_layer(c_vp(k_codes.data_ptr()), c_vp(k_meta.data_ptr()), c_vp(v_codes.data_ptr()),
-                    c_vp(v_meta.data_ptr()), B, H, half * 2, S, FQ_GROUP)
+                    c_vp(v_meta.data_ptr()), B, H, half * 2, S, FQ_GROUP, 4, None, None)
     return _keep(v, k_codes, k_meta, v_codes, v_meta)
+
+
+def kv_layer_view_f16(k16, v16):
+    """fq_kv_layer (bits 16) over torch fp16 tensors k16, v16 [B, H, S, d]."""
+    B, H, S, d = k16.shape
+    v = fq_kv_layer(None, None, None, None, B, H, d, S, FQ_GROUP, 16, c_vp(k16.data_ptr()), c_vp(v16.data_ptr()))
+    return _keep(v, k16, v16)
 
 
 def fq_kv_append(kv, k, v, ld, b0, B, T, pos, stream=None):
@@ -228,9 +236,10 @@ class Model:
     """Owner of an fq_model handle (fq_model_create / fq_model_destroy)."""
 
     def __init__(self, hidden, heads, ffn, layers, vocab=0, max_pos=0, compress_weight=True, resident_layers=-1,
-                 host_layers=0, overlap=True, max_tokens=16384):
+                 host_layers=0, overlap=True, max_tokens=16384, compress_cache=True):
         self.cfg = fq_model_config(hidden, heads, ffn, layers, vocab, max_pos)
-        self.pol = fq_policy(int(compress_weight), 1, resident_layers, host_layers, int(overlap), max_tokens)
+        self.pol = fq_policy(int(compress_weight), int(compress_cache), resident_layers, host_layers, int(overlap),
+                             max_tokens)
         h = c_vp()
         _check(_lib.fq_model_create(ctypes.byref(self.cfg), ctypes.byref(self.pol), ctypes.byref(h)))
         self.handle = h

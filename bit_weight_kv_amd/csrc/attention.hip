@@ -1,4 +1,4 @@
-// Attention over the 4-bit KV cache: the decode kernel (K3, one new query
+// Attention over the KV cache: the decode kernel (K3, one new query
 // per sequence) and the causal prefill kernel (K5, T new queries).
 //
 // Cache format (FlexGen README, "Extreme Compression": the attention cache is
@@ -17,7 +17,12 @@
 //      lane), 16 positions are in flight per block; each lane accumulates
 //      sum_j (p_j s_jg) c_ji and sum_j p_j min_jg, then the 16 partial sums
 //      are reduced through LDS.
+//
+// The fp16 cache (cache compression off, weights possibly still compressed)
+// goes through the same kernels instantiated with F16 = true: keys and values
+// are read as stored (2 bytes per cached element) instead of reconstructed.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.h"
 
@@ -58,14 +63,18 @@ __device__ inline void codes8_f16(uint32_t w, half2_t out[4]) {
   }
 }
 
-template <int D>
+// F16 selects the fp16 cache (k16/v16): each position is then covered by D/8
+// lanes in both passes, 16 bytes per lane, and the scores are reduced across
+// those lanes with xor shuffles.
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
                                                                const uint8_t* __restrict__ kc,
                                                                const uint16_t* __restrict__ km,
                                                                const uint8_t* __restrict__ vc,
                                                                const uint16_t* __restrict__ vm, int H, int64_t cap,
                                                                int64_t b0, int len, uint16_t* __restrict__ out,
-                                                               int64_t ldo) {
+                                                               int64_t ldo, const uint16_t* __restrict__ k16,
+                                                               const uint16_t* __restrict__ v16) {
   constexpr int G = D / 64;       // groups per head
   constexpr int WORDS = D / 8;    // 32-bit code words per position
   constexpr int LPP = WORDS;      // lanes per position in the value pass
@@ -76,9 +85,62 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   const int b = blockIdx.y, h = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t row0 = ((b0 + b) * H + h) * cap;  // first cache row of this (b, h)
+  const uint16_t* qp = q + (int64_t)b * ldq + (int64_t)h * D;
+  float* p = smem;
+  const int slot = tid / LPP, wl = tid % LPP;  // wl: 8-channel chunk of this lane in the per-position passes
+
+  if constexpr (F16) {
+    // ---- scores: D/8 lanes per position ----
+    const uint4 qr = *reinterpret_cast<const uint4*>(qp + wl * 8);
+    const half2_t q2[4] = {__builtin_bit_cast(half2_t, qr.x), __builtin_bit_cast(half2_t, qr.y),
+                           __builtin_bit_cast(half2_t, qr.z), __builtin_bit_cast(half2_t, qr.w)};
+    float lmax = -INFINITY;
+    for (int j = slot; j < len; j += SLOTS) {
+      const uint4 kr = *reinterpret_cast<const uint4*>(k16 + (row0 + j) * D + wl * 8);
+      float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kr.x), q2[0], 0.f, false);
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kr.y), q2[1], s, false);
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kr.z), q2[2], s, false);
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kr.w), q2[3], s, false);
+#pragma unroll
+      for (int o = 1; o < LPP; o <<= 1) s += __shfl_xor(s, o);  // the LPP lanes of one position
+      s *= kLog2e;
+      if (wl == 0) p[j] = s;
+      lmax = fmaxf(lmax, s);
+    }
+    const float mx = block_max256(lmax, red);  // also orders the p[] writes before the reads below
+    float lsum = 0.f;
+    for (int j = tid; j < len; j += 256) {
+      const float e = exp2f(p[j] - mx);
+      p[j] = e;
+      lsum += e;
+    }
+    const float inv = 1.0f / block_sum256(lsum, red);
+    // ---- values ----
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = slot; j < len; j += SLOTS) {
+      const uint4 vr = *reinterpret_cast<const uint4*>(v16 + (row0 + j) * D + wl * 8);
+      const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+      const float pj = p[j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += pj * h2f((uint16_t)(w[k] & 0xFFFF));
+        acc[2 * k + 1] += pj * h2f((uint16_t)(w[k] >> 16));
+      }
+    }
+    float* part = smem + ((len + 3) & ~3);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[slot * D + wl * 8 + k] = acc[k];
+    __syncthreads();
+    if (tid < D) {
+      float o = 0.f;
+#pragma unroll 4
+      for (int s2 = 0; s2 < SLOTS; ++s2) o += part[s2 * D + tid];
+      out[(int64_t)b * ldo + (int64_t)h * D + tid] = f2h(o * inv);
+    }
+    return;
+  }
 
   // ---- query: fp16 pairs in registers, per-group sums of q ----
-  const uint16_t* qp = q + (int64_t)b * ldq + (int64_t)h * D;
   half2_t qv[D / 2];
 #pragma unroll
   for (int i = 0; i < D / 8; ++i) {
@@ -98,7 +160,6 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   }
 
   // ---- scores ----
-  float* p = smem;
   float lmax = -INFINITY;
   for (int j = tid; j < len; j += 256) {
     const uint4* crow = reinterpret_cast<const uint4*>(kc + (row0 + j) * (D / 2));
@@ -137,8 +198,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   const float inv = 1.0f / block_sum256(lsum, red);  // also orders the p[] writes before the reads below
 
   // ---- values ----
-  const int slot = tid / LPP, wl = tid % LPP;  // wl: code word (8 channels) of this lane
-  const int g = wl / 8;                        // group of those channels
+  const int g = wl / 8;  // group of this lane's 8 channels
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float bsum = 0.f;
   for (int j = slot; j < len; j += SLOTS) {
@@ -166,14 +226,16 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
 // Block = 64 queries of one (b, h); 4 lanes per query, each owning D/4
 // channels.  Keys/values are reconstructed chunk by chunk (64 positions) into
 // LDS as fp32 and read back as broadcasts.
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
                                                                 const uint8_t* __restrict__ kc,
                                                                 const uint16_t* __restrict__ km,
                                                                 const uint8_t* __restrict__ vc,
                                                                 const uint16_t* __restrict__ vm, int H, int64_t cap,
                                                                 int64_t b0, int T, int64_t pos,
-                                                                uint16_t* __restrict__ out, int64_t ldo) {
+                                                                uint16_t* __restrict__ out, int64_t ldo,
+                                                                const uint16_t* __restrict__ k16,
+                                                                const uint16_t* __restrict__ v16) {
   constexpr int QT = 64, KC = 64, PART = D / 4, G = D / 64;
   __shared__ __attribute__((aligned(16))) float Ks[KC][D + 4];
   __shared__ __attribute__((aligned(16))) float Vs[KC][D + 4];
@@ -216,7 +278,20 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* 
       const int r = (wi / (D / 8)) % KC, w8 = wi % (D / 8);
       const int64_t j = k0 + r;
       float* dst = which ? &Vs[r][w8 * 8] : &Ks[r][w8 * 8];
-      if (j < nkeys) {
+      if constexpr (F16) {
+        if (j < nkeys) {
+          const uint4 r4 = *reinterpret_cast<const uint4*>((which ? v16 : k16) + (row0 + j) * D + w8 * 8);
+          const uint32_t w[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            dst[2 * k] = h2f((uint16_t)(w[k] & 0xFFFF));
+            dst[2 * k + 1] = h2f((uint16_t)(w[k] >> 16));
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dst[k] = 0.f;
+        }
+      } else if (j < nkeys) {
         const uint8_t* cbase = which ? vc : kc;
         const uint16_t* mbase = which ? vm : km;
         const uint32_t w = reinterpret_cast<const uint32_t*>(cbase + (row0 + j) * (D / 2))[w8];
@@ -288,11 +363,12 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* 
 // slice in the order {0-3, 16-19, 4-7, 20-23, ...}: the order in which a lane
 // holds its scores, so the V operand is one 16-byte read per lane.
 // LDS rows are 128 bytes with the 16-byte chunk swizzle c ^ (row & 7).
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ km,
     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vm, int H, int64_t cap, int64_t b0, int T,
-    int64_t pos, uint16_t* __restrict__ out, int64_t ldo) {
+    int64_t pos, uint16_t* __restrict__ out, int64_t ldo, const uint16_t* __restrict__ k16,
+    const uint16_t* __restrict__ v16) {
   constexpr int KC = 64;           // positions per chunk
   constexpr int NKD = D / 32;      // 32-wide d slices
   constexpr int NDB = D / 16;      // 16-wide d blocks
@@ -338,18 +414,23 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       for (int w = 0; w < D / 16; ++w) {  // 8-channel words of this half
         const int word = hf * (D / 16) + w;
         const int d0 = word * 8;
-        const uint32_t mb = mw[d0 / 64];
-        const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
-        const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
-        const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-        const uint32_t code = cw[word];
-        const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
         uint32_t o[4];
+        if constexpr (F16) {
+          const uint4 r4 = *reinterpret_cast<const uint4*>(k16 + (row0 + j) * D + d0);
+          o[0] = r4.x, o[1] = r4.y, o[2] = r4.z, o[3] = r4.w;
+        } else {
+          const uint32_t mb = mw[d0 / 64];
+          const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
+          const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
+          const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+          const uint32_t code = cw[word];
+          const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
-          const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
-          o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
+            const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
+            o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+          }
         }
         const int arr = d0 / 64, chunk = (d0 % 64) / 8;
         *reinterpret_cast<uint4*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -366,17 +447,22 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
         for (int jj = 0; jj < 8; ++jj) {
           const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
           const int64_t j = min(k0 + key, nkeys - 1);
-          const uint32_t code = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[dc];
-          const uint32_t mb = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + dc / 8];
-          const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
-          const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
-          const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-          const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
+          if constexpr (F16) {
+            const uint4 r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + j) * D + dc * 8);
+            vals[jj][0] = r4.x, vals[jj][1] = r4.y, vals[jj][2] = r4.z, vals[jj][3] = r4.w;
+          } else {
+            const uint32_t code = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[dc];
+            const uint32_t mb = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + dc / 8];
+            const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
+            const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
+            const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+            const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
-            const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
-            vals[jj][p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
+              const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
+              vals[jj][p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
+            }
           }
         }
         // channel i of the 8: gather its 8 positions into one 16-byte chunk
@@ -489,9 +575,28 @@ fq_status check_kv(const fq_kv_layer* kv, const char* who) {
   if (kv->group != FQ_GROUP) return fail(FQ_ERR_UNSUPPORTED, std::string(who) + ": only group 64 is implemented");
   if (kv->head_dim != 64 && kv->head_dim != 128)
     return fail(FQ_ERR_UNSUPPORTED, std::string(who) + ": head_dim must be 64 or 128");
-  if (!kv->k_codes || !kv->k_meta || !kv->v_codes || !kv->v_meta)
+  if (!kv_bits_valid(*kv)) return fail(FQ_ERR_INVALID, std::string(who) + ": bits must be 4 or 16");
+  if (kv_is_f16(*kv)) {
+    if (!kv->k16 || !kv->v16) return fail(FQ_ERR_INVALID, std::string(who) + ": NULL cache buffer");
+    if ((uintptr_t)kv->k16 % 16 || (uintptr_t)kv->v16 % 16)
+      return fail(FQ_ERR_INVALID, std::string(who) + ": fp16 cache must be 16-byte aligned");
+  } else if (!kv->k_codes || !kv->k_meta || !kv->v_codes || !kv->v_meta) {
     return fail(FQ_ERR_INVALID, std::string(who) + ": NULL cache buffer");
+  }
   return FQ_OK;
+}
+
+// Kernel instantiation for (head_dim, cache format); F(D, F16) launches.
+template <typename F>
+void by_format(const fq_kv_layer& kv, F&& launch) {
+  const bool f16 = kv_is_f16(kv);
+  if (kv.head_dim == 128) {
+    if (f16) launch(std::integral_constant<int, 128>{}, std::true_type{});
+    else launch(std::integral_constant<int, 128>{}, std::false_type{});
+  } else {
+    if (f16) launch(std::integral_constant<int, 64>{}, std::true_type{});
+    else launch(std::integral_constant<int, 64>{}, std::false_type{});
+  }
 }
 
 }  // namespace
@@ -499,12 +604,13 @@ fq_status check_kv(const fq_kv_layer* kv, const char* who) {
 
 using namespace fq;
 
-// Test hook: FQ_PREFILL_VECTOR=1 selects the vector-unit prefill kernel (fp32
-// reconstruction) instead of the matrix-core one.
-static const bool g_prefill_vector_only = [] {
+// Test hook: FQ_PREFILL_VECTOR=1 in the environment at the time of the call
+// selects the vector-unit prefill kernel (fp32 reconstruction) instead of the
+// matrix-core one.
+static bool prefill_vector_only() {
   const char* e = getenv("FQ_PREFILL_VECTOR");
   return e && e[0] == '1';
-}();
+}
 
 extern "C" fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
                                          int64_t len, uint16_t* out, int64_t ldo, void* stream) {
@@ -522,18 +628,15 @@ extern "C" fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const f
   const dim3 grid((unsigned)kv->heads, (unsigned)B);
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
-  if (D == 128)
-    decode_attention_kernel<128><<<grid, dim3(256), lds, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                               kv->v_meta, kv->heads, kv->capacity, b0, (int)len,
-                                                               out, ldo);
-  else
-    decode_attention_kernel<64><<<grid, dim3(256), lds, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                              kv->v_meta, kv->heads, kv->capacity, b0, (int)len, out,
-                                                              ldo);
+  by_format(*kv, [&](auto d, auto f16) {
+    decode_attention_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), lds, st>>>(
+        q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)len, out, ldo,
+        kv->k16, kv->v16);
+  });
   FQ_TRY(launch_check("decode_attention_kernel"));
   if (tk >= 0) {
-    const double units = (double)B * kv->heads;
-    timing_end(tk, FQ_KC_DECODE_ATTN, units * 4.0 * len * D, units * (2.0 * len * D * 0.5625 + 4.0 * D), st);
+    const double units = (double)B * kv->heads, epb = kv_is_f16(*kv) ? 2.0 : 0.5625;  // cache bytes per element
+    timing_end(tk, FQ_KC_DECODE_ATTN, units * 4.0 * len * D, units * (2.0 * len * D * epb + 4.0 * D), st);
   }
   return FQ_OK;
 }
@@ -552,34 +655,28 @@ extern "C" fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const 
                "fq_prefill_attention: q/out NULL or misaligned");
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
-  if (!g_prefill_vector_only) {
+  if (!prefill_vector_only()) {
     const dim3 grid((unsigned)ceil_div(T, 128), (unsigned)kv->heads, (unsigned)B);
-    if (kv->head_dim == 128)
-      prefill_attention_mfma_kernel<128><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                                     kv->v_meta, kv->heads, kv->capacity, b0, (int)T,
-                                                                     pos, out, ldo);
-    else
-      prefill_attention_mfma_kernel<64><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                                    kv->v_meta, kv->heads, kv->capacity, b0, (int)T,
-                                                                    pos, out, ldo);
+    by_format(*kv, [&](auto d, auto f16) {
+      prefill_attention_mfma_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), 0, st>>>(
+          q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos, out,
+          ldo, kv->k16, kv->v16);
+    });
     FQ_TRY(launch_check("prefill_attention_mfma_kernel"));
   } else {
     const dim3 grid((unsigned)ceil_div(T, 64), (unsigned)kv->heads, (unsigned)B);
-    if (kv->head_dim == 128)
-      prefill_attention_kernel<128><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                                kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
-                                                                out, ldo);
-    else
-      prefill_attention_kernel<64><<<grid, dim3(256), 0, st>>>(q, ldq, kv->k_codes, kv->k_meta, kv->v_codes,
-                                                               kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos,
-                                                               out, ldo);
+    by_format(*kv, [&](auto d, auto f16) {
+      prefill_attention_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), 0, st>>>(
+          q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos, out,
+          ldo, kv->k16, kv->v16);
+    });
     FQ_TRY(launch_check("prefill_attention_kernel"));
   }
   if (tk >= 0) {
-    const double units = (double)B * kv->heads, d = kv->head_dim;
+    const double units = (double)B * kv->heads, d = kv->head_dim, epb = kv_is_f16(*kv) ? 2.0 : 0.5625;
     const double pairs = (double)T * pos + (double)T * (T + 1) / 2.0;  // (query, key) pairs under the causal mask
-    timing_end(tk, FQ_KC_PREFILL_ATTN, units * 4.0 * pairs * d,
-               units * (4.0 * T * d + 2.0 * (pos + T) * d * 0.5625), st);
+    timing_end(tk, FQ_KC_PREFILL_ATTN, units * 4.0 * pairs * d, units * (4.0 * T * d + 2.0 * (pos + T) * d * epb),
+               st);
   }
   return FQ_OK;
 }

@@ -44,6 +44,11 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Storage format of a KV-cache layer view: true for the fp16 cache, false for
+// the 4-bit one (bits 4, or 0 in a zero-initialised view).
+inline bool kv_is_f16(const fq_kv_layer& kv) { return kv.bits == 16; }
+inline bool kv_bits_valid(const fq_kv_layer& kv) { return kv.bits == 0 || kv.bits == 4 || kv.bits == 16; }
+
 // ---- device vector types ---------------------------------------------------
 typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -129,6 +129,32 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restri
   }
 }
 
+// fp16 cache: K/V of T new tokens copied unchanged to positions pos..pos+T-1.
+// Items enumerate (b, t, which, head, 8-channel chunk) with the chunk fastest,
+// one 16-byte store per thread.
+template <bool ALIGNED>
+__global__ __launch_bounds__(256) void kv_append_f16_kernel(const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v, int64_t ld,
+                                                            int64_t n_items, int T, int H, int cpd, int64_t b0,
+                                                            int64_t cap, int64_t pos, uint16_t* __restrict__ k16,
+                                                            uint16_t* __restrict__ v16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_items) return;
+  int64_t rest = i;
+  const int c = (int)(rest % cpd);
+  rest /= cpd;
+  const int head = (int)(rest % H);
+  rest /= H;
+  const int which = (int)(rest & 1);
+  rest >>= 1;
+  const int tok = (int)(rest % T);
+  const int64_t b = rest / T;
+  const int d = cpd * 8;
+  const uint4 raw = load8((which ? v : k) + (b * T + tok) * ld + (int64_t)head * d + c * 8, ALIGNED);
+  const int64_t row = ((b0 + b) * H + head) * cap + pos + tok;
+  reinterpret_cast<uint4*>((which ? v16 : k16) + row * d)[c] = raw;
+}
+
 // y = fp16(min + code * s) with one rounding (fused fp16 multiply-add).
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ meta, int64_t n8,
@@ -216,13 +242,32 @@ extern "C" fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, cons
   FQ_CHECK_ARG(b0 + B <= kv->batch, "fq_kv_append: sequence range exceeds the cache batch");
   FQ_CHECK_ARG(pos + T <= kv->capacity, "fq_kv_append: positions exceed the cache capacity");
   FQ_CHECK_ARG(ld >= (int64_t)kv->heads * kv->head_dim, "fq_kv_append: ld < heads*head_dim");
+  FQ_CHECK_ARG(kv_bits_valid(*kv), "fq_kv_append: bits must be 4 or 16");
   if (B == 0 || T == 0) return FQ_OK;
+  const bool aligned = ((uintptr_t)k % 16 == 0) && ((uintptr_t)v % 16 == 0) && (ld % 8 == 0);
+  hipStream_t st = as_stream(stream);
+  if (kv_is_f16(*kv)) {
+    FQ_CHECK_ARG(k && v && kv->k16 && kv->v16, "fq_kv_append: NULL buffer");
+    FQ_CHECK_ARG((uintptr_t)kv->k16 % 16 == 0 && (uintptr_t)kv->v16 % 16 == 0,
+                 "fq_kv_append: fp16 cache must be 16-byte aligned");
+    const int cpd = kv->head_dim / 8;
+    const int64_t n_items = B * T * 2 * kv->heads * cpd;
+    const dim3 grid((unsigned)ceil_div(n_items, 256));
+    const int tk = timing_begin(st);
+    if (aligned)
+      kv_append_f16_kernel<true><<<grid, dim3(256), 0, st>>>(k, v, ld, n_items, (int)T, kv->heads, cpd, b0,
+                                                             kv->capacity, pos, kv->k16, kv->v16);
+    else
+      kv_append_f16_kernel<false><<<grid, dim3(256), 0, st>>>(k, v, ld, n_items, (int)T, kv->heads, cpd, b0,
+                                                              kv->capacity, pos, kv->k16, kv->v16);
+    FQ_TRY(launch_check("kv_append_f16_kernel"));
+    timing_end(tk, FQ_KC_KV_APPEND, 0.0, (double)n_items * 8 * 4.0, st);
+    return FQ_OK;
+  }
   FQ_CHECK_ARG(k && v && kv->k_codes && kv->k_meta && kv->v_codes && kv->v_meta, "fq_kv_append: NULL buffer");
   const int gpd = kv->head_dim / 64;
   const int64_t n_groups = B * T * 2 * kv->heads * gpd;
-  const bool aligned = ((uintptr_t)k % 16 == 0) && ((uintptr_t)v % 16 == 0) && (ld % 8 == 0);
   const dim3 grid((unsigned)ceil_div(n_groups * 8, 256));
-  hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
   if (aligned)
     kv_append_kernel<true><<<grid, dim3(256), 0, st>>>(k, v, ld, n_groups, (int)T, kv->heads, gpd, b0, kv->capacity,

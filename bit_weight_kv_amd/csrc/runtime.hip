@@ -294,7 +294,6 @@ extern "C" fq_status fq_model_create(const fq_model_config* cfg, const fq_policy
   if (d != 64 && d != 128) return fail(FQ_ERR_UNSUPPORTED, "fq_model_create: head_dim must be 64 or 128");
   FQ_CHECK_ARG(cfg->hidden % 64 == 0 && cfg->ffn % 64 == 0, "fq_model_create: hidden and ffn must be multiples of 64");
   FQ_CHECK_ARG(cfg->vocab >= 0 && (cfg->vocab == 0 || cfg->max_pos > 2), "fq_model_create: bad vocab/max_pos");
-  if (!policy->compress_cache) return fail(FQ_ERR_UNSUPPORTED, "fq_model_create: only the 4-bit KV cache is implemented");
   FQ_CHECK_ARG(policy->resident_layers >= -1, "fq_model_create: bad resident_layers");
   FQ_CHECK_ARG(policy->host_layers >= 0, "fq_model_create: bad host_layers");
 
@@ -556,11 +555,13 @@ extern "C" fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capa
   kv->device = m->device;
   const int H = m->cfg.heads;
   const int64_t d = m->d();
+  const bool f16 = !m->pol.compress_cache;
   const size_t codes = (size_t)batch * H * capacity * d / 2;
   const size_t meta = (size_t)batch * H * capacity * (d / 64) * 4;
+  const size_t elems = (size_t)batch * H * capacity * d;  // fp16 cache: elements per tensor
   for (int l = 0; l < kv->layers; ++l) {
     uint8_t* base = nullptr;
-    hipError_t e = hipMalloc(&base, 2 * (codes + meta));
+    hipError_t e = hipMalloc(&base, f16 ? 2 * elems * 2 : 2 * (codes + meta));
     if (e != hipSuccess) {
       (void)hipGetLastError();
       fq_kv_destroy(kv);
@@ -568,10 +569,17 @@ extern "C" fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capa
     }
     kv->allocs.push_back(base);
     fq_kv_layer v{};
-    v.k_codes = base;
-    v.v_codes = base + codes;
-    v.k_meta = reinterpret_cast<uint16_t*>(base + 2 * codes);
-    v.v_meta = reinterpret_cast<uint16_t*>(base + 2 * codes + meta);
+    if (f16) {
+      v.bits = 16;
+      v.k16 = reinterpret_cast<uint16_t*>(base);
+      v.v16 = reinterpret_cast<uint16_t*>(base) + elems;
+    } else {
+      v.bits = 4;
+      v.k_codes = base;
+      v.v_codes = base + codes;
+      v.k_meta = reinterpret_cast<uint16_t*>(base + 2 * codes);
+      v.v_meta = reinterpret_cast<uint16_t*>(base + 2 * codes + meta);
+    }
     v.batch = batch;
     v.heads = H;
     v.head_dim = (int32_t)d;

@@ -128,11 +128,19 @@ fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_we
                           int64_t qscale_cols, void* C, int64_t ldc, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* One layer of 4-bit KV cache (device memory; caller- or handle-owned):
+/* One layer of KV cache (device memory; caller- or handle-owned).
+ * 4-bit cache (bits 4, or 0 in a zero-initialised struct):
  *   k_codes, v_codes: uint8  [batch, heads, capacity, head_dim/2]
  *   k_meta,  v_meta:  uint16 [batch, heads, capacity, head_dim/64, 2]
  * One group = 64 consecutive head-dim channels of one token and head, so a
- * group never spans two tokens.  head_dim % 64 == 0. */
+ * group never spans two tokens.  head_dim % 64 == 0.
+ * fp16 cache (bits 16; cache compression switched off while weights may still
+ * be compressed -- FlexGen README, "Handle Out-of-memory", where weight
+ * compression is a flag of its own, and the Manning "FlexGen technique" page,
+ * "Configuring an OPT model", where the policy sets weight and cache
+ * compression separately):
+ *   k16, v16: fp16 [batch, heads, capacity, head_dim]; the codes/meta
+ *   pointers are unused. */
 typedef struct {
   uint8_t* k_codes;
   uint16_t* k_meta;
@@ -143,11 +151,14 @@ typedef struct {
   int32_t head_dim;
   int64_t capacity;
   int32_t group; /* must be 64 */
+  int32_t bits;  /* 4 (or 0): packed codes + meta;  16: fp16 entries in k16 / v16 */
+  uint16_t* k16;
+  uint16_t* v16;
 } fq_kv_layer;
 
 /* Quantise-on-append: the new tokens' K and V (fp16) become 4-bit cache
  * entries (FlexGen README, "Extreme Compression": the attention cache is
- * stored in 4 bits).
+ * stored in 4 bits); with bits == 16 they are copied unchanged.
  *   k, v: device fp16; row r = b*T + t holds heads*head_dim values of token
  *         t of sequence b; row stride ld elements (e.g. the K and V column
  *         blocks of a fused QKV activation with ld = 3*hidden)
@@ -156,9 +167,10 @@ typedef struct {
 fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, const uint16_t* v, int64_t ld, int64_t b0,
                        int64_t B, int64_t T, int64_t pos, void* stream);
 
-/* Decode attention over the packed cache: for each sequence b and head h,
+/* Decode attention over the cache: for each sequence b and head h,
  * s_j = q . k^_j for j < len, p = softmax(s), o = sum_j p_j v^_j, with k^, v^
- * reconstructed in registers in fp32 (min + code * s).
+ * reconstructed in registers in fp32 (min + code * s) from a 4-bit cache, or
+ * read as stored from an fp16 cache.
  *   q:   device fp16 [B, heads*head_dim] row stride ldq, already scaled by
  *        head_dim^-1/2
  *   out: device fp16 [B, heads*head_dim] row stride ldo
@@ -193,7 +205,7 @@ typedef struct {
  * and cache; "Handle Out-of-memory": --compress-weight, --pin-weight). */
 typedef struct {
   int32_t compress_weight; /* 1: 4-bit packed weights (group 64); 0: fp16 weights */
-  int32_t compress_cache;  /* must be 1 (4-bit KV cache) */
+  int32_t compress_cache;  /* 1: 4-bit KV cache (group 64); 0: fp16 KV cache */
   int32_t resident_layers; /* layers 0..resident_layers-1 are kept in HBM; the rest live in
                               pinned host memory -- packed (0.5625 byte per weight) when
                               compress_weight, else fp16 -- and are streamed through two
@@ -248,14 +260,16 @@ fq_status fq_model_init_random(fq_model* m, uint64_t seed, double bias_sigma, vo
 /* Device view of one layer's packed weight (which: 0 qkv, 1 out, 2 fc1, 3 fc2). */
 fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, int32_t which, fq_packed* out);
 
-/* KV cache for `batch` sequences of up to `capacity` positions, all layers. */
+/* KV cache for `batch` sequences of up to `capacity` positions, all layers:
+ * 4-bit (0.5625 byte per cached element) when the policy compresses the
+ * cache, else fp16 (2 bytes). */
 fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capacity, fq_kv** out);
 fq_status fq_kv_destroy(fq_kv* kv);
 fq_status fq_kv_layer_view(const fq_kv* kv, int32_t layer, fq_kv_layer* out);
 
 /* One decoder layer over T new tokens of sequences b0..b0+B-1 at positions
  * pos..pos+T-1: LN1, QKV projection (+bias, query scaling), quantise-on-
- * append of K/V, attention over the packed cache (causal for T > 1), output
+ * append of K/V (or fp16 append), attention over the cache (causal for T > 1), output
  * projection (+bias, +residual), LN2, FC1 (+bias, ReLU), FC2 (+bias,
  * +residual).  fp16 storage points as in the header of the oracle's layer.
  *   x, y: device fp16 [B*T, h] (may be the same buffer).

@@ -14,8 +14,10 @@ round-to-nearest-even, from its float64 value; everything between them is
 float64):
   h1 = LN1(x)[16]
   q  = ((h1 Wq^T + bq) * d^-1/2)[16];  k = (h1 Wk^T + bk)[16];  v = (h1 Wv^T + bv)[16]
-  k, v appended to the cache as 4-bit groups (quant.quantize), then
-  o  = attention(q, dequant(K cache), dequant(V cache))[16]
+  k, v appended to the cache as 4-bit groups (quant.quantize), or kept as
+  fp16 when cache compression is off, then
+  o  = attention(q, dequant(K cache), dequant(V cache))[16]  (the fp16 cache
+       is read as stored)
   x1 = (x + o Wo^T + bo)[16]
   h2 = LN2(x1)[16]
   f  = relu(h2 W1^T + b1)[16]
@@ -23,6 +25,10 @@ float64):
 W^ is dequant_f16 of the packed weight (or the fp16 weight itself when
 weights are not compressed).  The new token's K/V enter the cache before
 attention, so the query always attends over the reconstructed cache.
+Weight and cache compression are separate switches (README, "Handle
+Out-of-memory": --compress-weight; Manning "FlexGen technique" page,
+"Configuring an OPT model": the policy enables weight and cache compression
+separately).
 """
 from dataclasses import dataclass
 
@@ -175,7 +181,8 @@ def layer_step(x16: np.ndarray, params: dict, packed: dict, cache: dict, cfg: La
     y64 = x1.astype(np.float64) + gemm(f, packed["w_fc2"], params["b_fc2"])
     r["y"] = y64.astype(np.float16).reshape(B, T, h)
     r["y64"] = y64.reshape(B, T, h)
-    local = {"h1": h1, "q": q, "k": k, "v": v, "o": o, "o64": o64, "x1": x1, "x1_64": x1_64,
+    local = {"h1": h1, "q": q, "k": k, "v": v, "k64": qkv[:, h:2 * h], "v64": qkv[:, 2 * h:],
+             "o": o, "o64": o64, "x1": x1, "x1_64": x1_64,
              "h2": h2, "f": f}
     for name in want:
         r[name] = local[name]

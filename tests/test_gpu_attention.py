@@ -1,7 +1,8 @@
 """Decode attention (one query per sequence) and causal prefill attention over
-the packed cache, against the oracle's float64 softmax attention on the same
-cache contents.  The GPU fills its cache with its own quantise-on-append from
-the same fp16 K/V (bit-exactness of that step is tested separately)."""
+the packed 4-bit cache and over the fp16 cache, against the oracle's float64
+softmax attention on the same cache contents.  The GPU fills its cache with its
+own append (quantise-on-append for the 4-bit cache) from the same fp16 K/V
+(bit-exactness of that step is tested separately)."""
 import numpy as np
 import pytest
 import torch
@@ -14,43 +15,54 @@ pytestmark = pytest.mark.gpu
 fq = pytest.importorskip("bit_weight_kv_amd")
 
 
-def _cache(B, H, d, n, cap, seed, b_off=0):
-    """fp16 K/V [B, n, H*d] from the generator -> GPU cache (appended) and oracle cache."""
+def _cache(B, H, d, n, cap, seed, b_off=0, fmt="q4"):
+    """fp16 K/V [B, n, H*d] from the generator -> GPU cache (appended) and the
+    oracle's reading of the same cache (fmt "q4": 4-bit, "f16": fp16)."""
     h = H * d
     k = synth.normal_f16(seed, synth.STREAM["aux"] + 20, (B * n, h), 1.0)
     v = synth.normal_f16(seed, synth.STREAM["aux"] + 21, (B * n, h), 1.0)
-    kc = torch.zeros((B + b_off, H, cap, d // 2), dtype=torch.uint8, device="cuda:0")
-    km = torch.zeros((B + b_off, H, cap, d // 64, 2), dtype=torch.float16, device="cuda:0")
-    vc, vm = torch.zeros_like(kc), torch.zeros_like(km)
-    view = fq.kv_layer_view(kc, km, vc, vm)
+    if fmt == "q4":
+        kc = torch.zeros((B + b_off, H, cap, d // 2), dtype=torch.uint8, device="cuda:0")
+        km = torch.zeros((B + b_off, H, cap, d // 64, 2), dtype=torch.float16, device="cuda:0")
+        vc, vm = torch.zeros_like(kc), torch.zeros_like(km)
+        view, keep = fq.kv_layer_view(kc, km, vc, vm), (kc, km, vc, vm)
+    else:
+        k16 = torch.zeros((B + b_off, H, cap, d), dtype=torch.float16, device="cuda:0")
+        v16 = torch.zeros_like(k16)
+        view, keep = fq.kv_layer_view_f16(k16, v16), (k16, v16)
     kd, vd = dev(k), dev(v)
     fq.fq_kv_append(view, kd, vd, h, b_off, B, n, 0)
     torch.cuda.synchronize()
     to4 = lambda a: np.ascontiguousarray(a.reshape(B, n, H, d).transpose(0, 2, 1, 3))
-    kh = oracle.dequant_f64(*oracle.quantize(to4(k)))
-    vh = oracle.dequant_f64(*oracle.quantize(to4(v)))
-    return view, (kc, km, vc, vm), kh, vh
+    if fmt == "q4":
+        kh = oracle.dequant_f64(*oracle.quantize(to4(k)))
+        vh = oracle.dequant_f64(*oracle.quantize(to4(v)))
+    else:
+        kh, vh = to4(k).astype(np.float64), to4(v).astype(np.float64)
+    return view, keep, kh, vh
 
 
+@pytest.mark.parametrize("fmt", ["q4", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("length", [1, 2, 63, 64, 65, 300, 543])
-def test_decode_attention(d, length):
+def test_decode_attention(d, length, fmt):
     B, H = 3, 4
-    log(f"decode attention d={d} len={length}")
-    view, keep, kh, vh = _cache(B, H, d, length, length + 3, seed=d + length, b_off=1)
+    log(f"decode attention {fmt} d={d} len={length}")
+    view, keep, kh, vh = _cache(B, H, d, length, length + 3, seed=d + length, b_off=1, fmt=fmt)
     q = (synth.normal_f16(0, synth.STREAM["aux"] + 22, (B, H * d), 1.0).astype(np.float32)
          * d ** -0.5).astype(np.float16)
     out = torch.empty((B, H * d), dtype=torch.float16, device="cuda:0")
     fq.fq_decode_attention(dev(q), view, 1, B, length, out)
     torch.cuda.synchronize()
     ref = oracle.attention_decode(q.reshape(B, H, d), kh, vh).reshape(B, H * d)
-    assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"decode d={d} len={length}")
+    assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"decode {fmt} d={d} len={length}")
 
 
-def test_decode_attention_long_and_peaked():
+@pytest.mark.parametrize("fmt", ["q4", "f16"])
+def test_decode_attention_long_and_peaked(fmt):
     """A long cache (4000 positions) and a query aligned with one key (peaked softmax)."""
     B, H, d, n = 2, 2, 128, 4000
-    view, keep, kh, vh = _cache(B, H, d, n, n, seed=9)
+    view, keep, kh, vh = _cache(B, H, d, n, n, seed=9, fmt=fmt)
     q = np.zeros((B, H, d), np.float16)
     q[:, :, :] = (kh[:, :, 1234, :] * 0.3).astype(np.float16)
     out = torch.empty((B, H * d), dtype=torch.float16, device="cuda:0")
@@ -60,13 +72,17 @@ def test_decode_attention_long_and_peaked():
     assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what="long/peaked")
 
 
+@pytest.mark.parametrize("kernel", ["mfma", "vector"])
+@pytest.mark.parametrize("fmt", ["q4", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T,pos", [(1, 0), (5, 0), (64, 0), (65, 0), (130, 0), (9, 7)])
-def test_prefill_attention_causal(d, T, pos):
+def test_prefill_attention_causal(d, T, pos, fmt, kernel, monkeypatch):
     B, H = 2, 3
-    log(f"prefill attention d={d} T={T} pos={pos}")
+    log(f"prefill attention {kernel} {fmt} d={d} T={T} pos={pos}")
+    if kernel == "vector":
+        monkeypatch.setenv("FQ_PREFILL_VECTOR", "1")  # read by the library at each call
     n = pos + T
-    view, keep, kh, vh = _cache(B, H, d, n, n + 1, seed=T + pos)
+    view, keep, kh, vh = _cache(B, H, d, n, n + 1, seed=T + pos, fmt=fmt)
     q = (synth.normal_f16(1, synth.STREAM["aux"] + 23, (B * T, H * d), 1.0).astype(np.float32)
          * d ** -0.5).astype(np.float16)
     out = torch.empty((B * T, H * d), dtype=torch.float16, device="cuda:0")
@@ -77,8 +93,8 @@ def test_prefill_attention_causal(d, T, pos):
     for t in range(T):
         ref[:, :, t] = oracle.attention_decode(q4[:, :, t], kh[:, :, :pos + t + 1], vh[:, :, :pos + t + 1])
     ref = ref.transpose(0, 2, 1, 3).reshape(B * T, H * d)
-    r, m = assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill d={d} T={T} pos={pos}")
-    log(f"prefill d={d} T={T} pos={pos}: rel_l2 {r:.2e} max_abs {m:.2e}")
+    r, m = assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill {kernel} {fmt} d={d} T={T} pos={pos}")
+    log(f"prefill {kernel} {fmt} d={d} T={T} pos={pos}: rel_l2 {r:.2e} max_abs {m:.2e}")
 
 
 def test_decode_full_size_sampled():

@@ -62,6 +62,18 @@ def test_generate_matches_oracle():
     assert abs(st.tokens_per_s - B * G / (st.prefill_s + st.decode_s)) < 1e-6 * st.tokens_per_s
 
 
+@pytest.mark.parametrize("weight,cache", [(True, False), (False, False)])
+def test_generate_compression_toggles_match_oracle(weight, cache):
+    """Weight-only compression (fp16 KV cache) and no compression, against the
+    oracle's generation with the same switches."""
+    L, B, P, G = 2, 4, 16, 6
+    log(f"generate compress_weight={weight} compress_cache={cache}")
+    ids, out, lg, st = _gpu_generate(L, B, P, G, seed=4, compress_weight=weight, compress_cache=cache)
+    mcfg = ModelConfig(LayerConfig(H, NH, F, compress_weight=weight, compress_cache=cache), L, V, P + G + 2)
+    ref = oracle.generate(ids, G, 4, mcfg)
+    _compare(out, lg, ref, f"weight={weight} cache={cache}")
+
+
 def test_generate_deterministic_and_batch_independent():
     L, B, P, G = 2, 3, 12, 4
     ids, out1, lg1, _ = _gpu_generate(L, B, P, G, seed=1)

@@ -113,6 +113,41 @@ def test_kv_append_bit_exact(H, d, B, T, pos):
     assert not host(kc)[0].any() and not host(kc)[1:, :, :pos].any()
 
 
+@pytest.mark.parametrize("H,d,B,T,pos,shift", [(4, 64, 3, 5, 0, 0), (4, 128, 2, 1, 9, 0), (3, 128, 2, 7, 3, 1)])
+def test_kv_append_f16_copies_exactly(H, d, B, T, pos, shift):
+    """fp16 cache: the new K/V land unchanged at positions pos..pos+T-1 (shift 1
+    offsets the source by one element, taking the unaligned path)."""
+    h = H * d
+    cap = pos + T + 2
+    qkv = synth.normal_f16(3, 95 + H, (B * T, 3 * h + shift), 1.0)
+    qd = dev(qkv)
+    k16 = torch.zeros((B + 1, H, cap, d), dtype=torch.float16, device="cuda:0")
+    v16 = torch.zeros_like(k16)
+    view = fq.kv_layer_view_f16(k16, v16)
+    fq.fq_kv_append(view, qd[:, shift + h:], qd[:, shift + 2 * h:], 3 * h + shift, 1, B, T, pos)
+    torch.cuda.synchronize()
+    k = qkv[:, shift + h:shift + 2 * h].reshape(B, T, H, d).transpose(0, 2, 1, 3)
+    v = qkv[:, shift + 2 * h:].reshape(B, T, H, d).transpose(0, 2, 1, 3)
+    assert np.array_equal(bits16(host(k16)[1:, :, pos:pos + T]), bits16(k))
+    assert np.array_equal(bits16(host(v16)[1:, :, pos:pos + T]), bits16(v))
+    assert not host(k16)[0].any() and not host(k16)[1:, :, :pos].any() and not host(v16)[1:, :, pos + T:].any()
+
+
+def test_kv_view_format_errors():
+    k16 = torch.zeros((1, 2, 4, 64), dtype=torch.float16, device="cuda:0")
+    bad = fq.kv_layer_view_f16(k16, torch.zeros_like(k16))
+    bad.bits = 7
+    x = torch.zeros((1, 3 * 128), dtype=torch.float16, device="cuda:0")
+    with pytest.raises(fq.FqError):
+        fq.fq_kv_append(bad, x[:, 128:], x[:, 256:], 384, 0, 1, 1, 0)
+    with pytest.raises(fq.FqError):
+        fq.fq_decode_attention(x, bad, 0, 1, 1, torch.zeros((1, 128), dtype=torch.float16, device="cuda:0"))
+    missing = fq.kv_layer_view_f16(k16, torch.zeros_like(k16))
+    missing.v16 = None
+    with pytest.raises(fq.FqError):
+        fq.fq_prefill_attention(x, missing, 0, 1, 1, 0, torch.zeros((1, 128), dtype=torch.float16, device="cuda:0"))
+
+
 def test_quantize_full_size_weight_sampled_rows():
     """FC1 weight of the OPT-175B shape (49152 x 12288), generated on the GPU;
     sampled rows checked bit-exactly against the oracle on the same inputs."""

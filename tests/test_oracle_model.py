@@ -1,7 +1,9 @@
 """Pins of the oracle's layer step and generation loop: causal consistency
 (prefill of P+1 tokens == prefill of P then one decode step, exact because a
 quantisation group never spans two tokens), a zero-weight layer that reduces
-to its residual path in closed form, and greedy-generation consistency."""
+to its residual path in closed form, the fp16-cache variant against torch's
+causal attention, the 4-bit and fp16 caches agreeing where quantisation is
+lossless, and greedy-generation consistency."""
 import numpy as np
 
 import synth
@@ -67,6 +69,54 @@ def test_uncompressed_weights_and_cache_variant_runs_and_is_consistent():
     layer_step(x[:, :5], p, pk, c, cfg, 0)
     b = layer_step(x[:, 5:], p, pk, c, cfg, 5)["y"]
     assert np.array_equal(a[:, 5:].view(np.uint16), b.view(np.uint16))
+
+
+def test_fp16_cache_layer_attention_against_torch_sdpa():
+    """Cache compression off: the cache holds the rounded K/V as they are, and
+    the attention output of a prefill followed by two decode steps equals
+    torch's causal scaled-dot-product attention (float64) over those values."""
+    import torch
+    cfg = LayerConfig(hidden=256, heads=4, ffn=512, compress_weight=True, compress_cache=False)
+    p = layer_params(5, cfg, 0, bias_sigma=0.02)
+    pk = pack_layer(p, cfg)
+    B, P, T, H, d = 2, 5, 2, 4, 64
+    x = _x(B, P + T, 256, seed=5)
+    c = new_cache(cfg, B, P + T + 1)
+    want = ("q", "k", "v", "o64")
+    rs = [layer_step(x[:, :P], p, pk, c, cfg, 0, want=want)]
+    for t in range(T):
+        rs.append(layer_step(x[:, P + t:P + t + 1], p, pk, c, cfg, P + t, want=want))
+    bhtd = lambda a, n: torch.from_numpy(a.reshape(B, n, H, d).transpose(0, 2, 1, 3).astype(np.float64))
+    q = torch.cat([bhtd(r["q"], r["q"].shape[0] // B) for r in rs], 2)
+    k = torch.cat([bhtd(r["k"], r["k"].shape[0] // B) for r in rs], 2)
+    v = torch.cat([bhtd(r["v"], r["v"].shape[0] // B) for r in rs], 2)
+    assert np.array_equal(c["k"][:, :, :P + T].view(np.uint16), k.numpy().astype(np.float16).view(np.uint16))
+    assert np.array_equal(c["v"][:, :, :P + T].view(np.uint16), v.numpy().astype(np.float16).view(np.uint16))
+    assert not c["k"][:, :, P + T:].any()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=1.0).numpy()
+    got = np.concatenate([r["o64"] for r in rs], 2)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_cache_toggle_agrees_on_grid_exact_keys_and_values():
+    """With zero weights every token's K and V are the biases; biases chosen on
+    their own 4-bit grid (both extremes present, power-of-two step) quantise
+    losslessly, so the 4-bit and fp16 caches give bit-identical layer outputs."""
+    outs = []
+    for cc in (True, False):
+        cfg = LayerConfig(hidden=256, heads=4, ffn=512, compress_cache=cc)
+        p = layer_params(6, cfg, 0, bias_sigma=0.02)
+        for w in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
+            p[w] = np.zeros_like(p[w])
+        codes = np.arange(3 * 256) % 16
+        p["b_qkv"] = (-0.5 + codes * 2.0 ** -4).astype(np.float16)
+        pk = pack_layer(p, cfg)
+        c = new_cache(cfg, 2, 6)
+        outs.append(layer_step(_x(2, 6, 256, seed=6), p, pk, c, cfg, 0, want=("o",)))
+        if not cc:
+            assert np.array_equal(c["v"][:, :, :6].reshape(2, 4, 6, 64)[0, 1, 3], p["b_qkv"][512 + 64:512 + 128])
+    assert np.array_equal(outs[0]["y"].view(np.uint16), outs[1]["y"].view(np.uint16))
+    assert np.array_equal(outs[0]["o"].view(np.uint16), outs[1]["o"].view(np.uint16))
 
 
 def test_argmax_ties_lowest_index():
