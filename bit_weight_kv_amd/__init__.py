@@ -86,6 +86,8 @@ _SIGS = {
     "fq_kv_append": (c_i32, [_P(fq_kv_layer), c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "fq_decode_attention": (c_i32, [c_vp, c_i64, _P(fq_kv_layer), c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "fq_prefill_attention": (c_i32, [c_vp, c_i64, _P(fq_kv_layer), c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "fq_qkv_gemm_append": (c_i32, [c_vp, c_i64, c_i64, _P(fq_weight), c_vp, c_f32, _P(fq_kv_layer), c_i64, c_i64,
+                                   c_i64, c_i64, c_vp, c_i64, c_vp]),
     "fq_layernorm": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_f32, c_vp, c_i64, c_vp]),
     "fq_model_create": (c_i32, [_P(fq_model_config), _P(fq_policy), _P(c_vp)]),
     "fq_model_destroy": (c_i32, [c_vp]),
@@ -194,6 +196,12 @@ def fq_kv_append(kv, k, v, ld, b0, B, T, pos, stream=None):
     _check(_lib.fq_kv_append(ctypes.byref(kv), _ptr(k) if isinstance(k, torch.Tensor) else c_vp(k),
                              _ptr(v) if isinstance(v, torch.Tensor) else c_vp(v), ld, b0, B, T, pos,
                              _stream(stream)))
+
+
+def fq_qkv_gemm_append(A, W, bias, qscale, kv, b0, B, T, pos, C, stream=None):
+    """QKV projection (+bias, q scaled) with the K/V append fused: q -> C[:, :h], K/V -> cache."""
+    _check(_lib.fq_qkv_gemm_append(_ptr(A), A.shape[0], A.stride(0), ctypes.byref(W), _ptr(bias), qscale,
+                                   ctypes.byref(kv), b0, B, T, pos, _ptr(C), C.stride(0), _stream(stream)))
 
 
 def fq_decode_attention(q, kv, b0, B, length, out, ldq=None, ldo=None, stream=None):

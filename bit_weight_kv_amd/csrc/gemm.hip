@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "quant_group.h"
 
 namespace fq {
 namespace {
@@ -54,6 +55,21 @@ __device__ inline void epilogue_store(const Epilogue& e, int64_t m, int64_t n, f
   else
     reinterpret_cast<uint16_t*>(e.C)[m * e.ldc + n] = f2h(v);
 }
+
+// K/V append fused into the epilogue of the QKV projection: columns
+// [h, 2h) are keys and [2h, 3h) values; row m is token m % T of sequence
+// b0 + m / T and lands at cache position pos + m % T.  fp16 storage (f16) or
+// 4-bit groups of 64 channels, quantised exactly as the append kernel does.
+struct KvAppend {
+  uint8_t* kc;
+  uint16_t* km;
+  uint8_t* vc;
+  uint16_t* vm;
+  uint16_t* k16;
+  uint16_t* v16;
+  int64_t h, cap, b0, pos;
+  int T, H, d, f16;
+};
 
 // Whether epilogue_store8 may use 16-byte accesses for every 8-column chunk
 // that lies inside N (C, residual and bias rows 16-byte aligned).
@@ -646,6 +662,55 @@ __device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, f
   out = __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
 }
 
+// One row's 16 accumulators of a K or V group (columns nw + cs .. nw + cs + 15
+// of the 64-column group starting at nw): bias, one rounding to fp16 (the
+// value the unfused path stores in C), then the fp16 cache store or the 4-bit
+// group quantisation across the 4 lanes (cs = 0, 16, 32, 48) holding the row.
+__device__ inline void kv_append_epilogue(const Epilogue& e, const KvAppend& kv, const float* src, int64_t m,
+                                          int64_t nw, int cs) {
+  float v[16];
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(src + c);
+    v[c] = x.x, v[c + 1] = x.y, v[c + 2] = x.z, v[c + 3] = x.w;
+  }
+  if (e.flags & FQ_EPI_BIAS) {
+#pragma unroll
+    for (int c = 0; c < 16; c += 8) {
+      const uint4 b = *reinterpret_cast<const uint4*>(e.bias + nw + cs + c);
+      const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[c + k] += h2f((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));
+    }
+  }
+  uint32_t hw[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) hw[k] = (uint32_t)f2h(v[2 * k]) | (uint32_t)f2h(v[2 * k + 1]) << 16;
+  const int64_t col = nw - kv.h;
+  const bool is_v = col >= kv.h;
+  const int64_t c2 = is_v ? col - kv.h : col;
+  const int head = (int)(c2 / kv.d), ch = (int)(c2 % kv.d);  // ch: first channel of the group
+  const int64_t b = m / kv.T, t = m - b * kv.T;
+  const int64_t row = ((kv.b0 + b) * kv.H + head) * kv.cap + kv.pos + t;
+  if (kv.f16) {
+    uint4* dst = reinterpret_cast<uint4*>((is_v ? kv.v16 : kv.k16) + row * kv.d + ch + cs);
+    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    return;
+  }
+  float f[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    f[2 * k] = h2f((uint16_t)(hw[k] & 0xFFFF));
+    f[2 * k + 1] = h2f((uint16_t)(hw[k] >> 16));
+  }
+  uint32_t packed[2], mb;
+  quant_group<16, 4>(f, packed, mb);
+  *reinterpret_cast<uint2*>((is_v ? kv.vc : kv.kc) + row * (kv.d / 2) + ch / 2 + cs / 2) =
+      make_uint2(packed[0], packed[1]);
+  if (cs == 0) reinterpret_cast<uint32_t*>(is_v ? kv.vm : kv.km)[row * (kv.d / 64) + ch / 64] = mb;
+}
+
 // ---- large-M kernel, 256 x 256 tiles (packed weights) ------------------------
 // 64-byte rows: chunk c of row r sits at slot c ^ swz4(r) (8 consecutive rows
 // read or written at one chunk hit 8 distinct 16-byte bank groups).
@@ -667,10 +732,12 @@ __device__ inline int swz4(int r) { return (r >> 1) & 3; }
 //     MFMAs of step kt, half a weight row per thread.
 //   * one barrier per step; the wait before it leaves the copies of this step
 //     and the previous one in flight.
+//   * KVA: the K and V columns go to the cache (KvAppend) instead of C.
+template <bool KVA>
 __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
                                                          const uint8_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ meta, int64_t N, int64_t K,
-                                                         Epilogue epi) {
+                                                         Epilogue epi, KvAppend kva) {
   constexpr int BMx = 256, BNx = 256, TM = 128, TN = 64, FM = 8, FN = 4, BKx = 32;
   constexpr int ROWB = BKx * 2;                   // 64 bytes per staged row
   constexpr int A_BYTES = BMx * ROWB;             // 16 KiB
@@ -873,12 +940,15 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
         for (int r = 0; r < 4; ++r) stg[(4 * (lane >> 4) + r) * SROW + j * 16 + (lane & 15)] = acc[i][j][r];
       __syncthreads();
       const int64_t m = m0 + wm * TM + i * 16 + rr;
-      if (m < M) {
+      const int64_t nw = n0 + wn * TN;  // this wave's 64 columns: one quantisation group of one head
+      if (KVA && nw >= kva.h && nw < N) {
+        if (m < M) kv_append_epilogue(epi, kva, stg + rr * SROW + cs, m, nw, cs);
+      } else if (m < M) {
         for (int c = 0; c < 16; c += 8) {
           const float4 lo = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c);
           const float4 hi = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c + 4);
           const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          epilogue_store8(epi, m, n0 + wn * TN + cs + c, v, N, vec);
+          epilogue_store8(epi, m, nw + cs + c, v, N, vec);
         }
       }
       __syncthreads();
@@ -1372,6 +1442,13 @@ fq_status run_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W
 
 using namespace fq;
 
+// Shapes the 256 x 256 kernel takes: packed weights, K a multiple of 128 and
+// enough tiles to fill the chip.
+static bool wide8_fits(int64_t M, int64_t N, int64_t K, const fq_weight* W) {
+  return M >= 1024 && N >= 1024 && K % 128 == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 128 &&
+         W->kind == FQ_WEIGHT_PACKED4;
+}
+
 // Test hook: FQ_GEMM_SMALL_TILES=1 in the environment routes every GEMM to the
 // 128x128 kernel (lets the tests compare the two large-M kernels).
 static const bool g_small_tiles_only = [] {
@@ -1421,10 +1498,10 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
     const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
-  } else if (M >= 1024 && N >= 1024 && K % 128 == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 128 &&
-             !g_small_tiles_only && W->kind == FQ_WEIGHT_PACKED4) {
+  } else if (wide8_fits(M, N, K, W) && !g_small_tiles_only) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-    gemm_wide8_kernel<<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi);
+    gemm_wide8_kernel<false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
+                                                         KvAppend{});
     r = launch_check("gemm_wide8_kernel");
   } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !g_small_tiles_only) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 128)));
@@ -1447,4 +1524,52 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     timing_end(tk, cls, 2.0 * M * N * K, bytes, st);
   }
   return r;
+}
+
+extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
+                                        const uint16_t* bias, float qscale, const fq_kv_layer* kv, int64_t b0,
+                                        int64_t B, int64_t T, int64_t pos, uint16_t* C, int64_t ldc, void* stream) {
+  clear_error();
+  FQ_CHECK_ARG(W != nullptr && kv != nullptr, "fq_qkv_gemm_append: NULL W or kv");
+  FQ_CHECK_ARG(kv_bits_valid(*kv), "fq_qkv_gemm_append: bits must be 4 or 16");
+  FQ_CHECK_ARG(kv->head_dim > 0 && kv->head_dim % 64 == 0 && kv->heads > 0,
+               "fq_qkv_gemm_append: head_dim must be a positive multiple of 64");
+  const int64_t h = (int64_t)kv->heads * kv->head_dim;
+  FQ_CHECK_ARG(W->n == 3 * h, "fq_qkv_gemm_append: W must have 3 * heads * head_dim rows");
+  FQ_CHECK_ARG(B >= 0 && T >= 0 && M == B * T, "fq_qkv_gemm_append: M must equal B * T");
+  FQ_CHECK_ARG(b0 >= 0 && pos >= 0 && b0 + B <= kv->batch && pos + T <= kv->capacity,
+               "fq_qkv_gemm_append: sequences or positions exceed the cache");
+  const uint32_t flags = (bias ? FQ_EPI_BIAS : 0u) | FQ_EPI_QSCALE;
+  const bool f16 = kv_is_f16(*kv);
+  const bool cache_ok = f16 ? (kv->k16 && kv->v16 && (uintptr_t)kv->k16 % 16 == 0 && (uintptr_t)kv->v16 % 16 == 0)
+                            : (kv->k_codes && kv->v_codes && kv->k_meta && kv->v_meta &&
+                               (uintptr_t)kv->k_codes % 8 == 0 && (uintptr_t)kv->v_codes % 8 == 0 &&
+                               (uintptr_t)kv->k_meta % 4 == 0 && (uintptr_t)kv->v_meta % 4 == 0);
+  const bool fused = M > 0 && wide8_fits(M, W->n, W->k, W) && !g_small_tiles_only && cache_ok &&
+                     (!bias || (uintptr_t)bias % 16 == 0) && kv->group == FQ_GROUP;
+  if (!fused) {
+    // unfused: the projection into C, then the append kernel reads K and V back
+    FQ_TRY(fq_dequant_gemm(A, M, lda, W, bias, nullptr, 0, flags, qscale, h, C, ldc, stream));
+    if (M == 0) return FQ_OK;
+    return fq_kv_append(kv, C + h, C + 2 * h, ldc, b0, B, T, pos, stream);
+  }
+  const int64_t N = W->n, K = W->k;
+  FQ_CHECK_ARG(K % 64 == 0 && lda >= K && lda % 8 == 0 && ldc >= N, "fq_qkv_gemm_append: bad K or strides");
+  FQ_CHECK_ARG(W->packed.group == FQ_GROUP && W->packed.rows == N && W->packed.cols == K && W->packed.codes &&
+                   W->packed.meta && (uintptr_t)W->packed.codes % 16 == 0 && (uintptr_t)W->packed.meta % 4 == 0,
+               "fq_qkv_gemm_append: bad packed weight");
+  FQ_CHECK_ARG(A && C && (uintptr_t)A % 16 == 0, "fq_qkv_gemm_append: NULL or misaligned A / C");
+  Epilogue epi{bias, nullptr, 0, flags, qscale, h, C, ldc};
+  KvAppend kva{kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->k16, kv->v16, h, kv->capacity, b0, pos,
+               (int)T, kv->heads, kv->head_dim, f16 ? 1 : 0};
+  hipStream_t st = as_stream(stream);
+  const int tk = timing_begin(st);
+  const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
+  gemm_wide8_kernel<true><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
+  FQ_TRY(launch_check("gemm_wide8_kernel"));
+  if (tk >= 0) {
+    const double bytes = 2.0 * M * K + 0.5625 * N * K + 2.0 * M * h + (f16 ? 2.0 : 0.5625) * 2.0 * M * h + 2.0 * N;
+    timing_end(tk, FQ_KC_GEMM_PREFILL, 2.0 * M * N * K, bytes, st);
+  }
+  return FQ_OK;
 }

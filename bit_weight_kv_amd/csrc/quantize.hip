@@ -13,6 +13,7 @@
 // fully coalesced; min/max are reduced across the 8 lanes with xor shuffles.
 // HBM traffic per element: 2 B read + 0.5 B codes + 1/16 B meta written.
 #include "common.h"
+#include "quant_group.h"
 
 namespace fq {
 namespace {
@@ -20,9 +21,7 @@ namespace {
 // Quantise this lane's 8 values of a 64-value group spread over lanes
 // sub = 0..7 of an aligned 8-lane segment.  Returns the lane's 8 codes as
 // nibbles (element 0 in bits 0..3) and the group's {min, scale} fp16 bits.
-// All arithmetic is IEEE fp32 with round-to-nearest-even; no contraction.
 __device__ inline uint32_t quant_group_lane(const uint4 raw, uint32_t& meta_bits) {
-#pragma clang fp contract(off)
   float v[8];
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -30,33 +29,9 @@ __device__ inline uint32_t quant_group_lane(const uint4 raw, uint32_t& meta_bits
     v[2 * j] = h2f((uint16_t)(w[j] & 0xFFFFu));
     v[2 * j + 1] = h2f((uint16_t)(w[j] >> 16));
   }
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) {
-    mn = fminf(mn, v[j]);
-    mx = fmaxf(mx, v[j]);
-  }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
-  if (mn == 0.0f) mn = 0.0f;  // canonical +0 minimum
-  float s32 = (mx - mn) / 15.0f;
-  if (s32 == 0.0f) s32 = 0.0f;  // canonical +0 scale
-  const half_t s16 = (half_t)s32;
-  const float s = (float)s16;
-  uint32_t packed = 0;
-  if (s != 0.0f) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float q = rintf((v[j] - mn) / s);
-      q = fminf(fmaxf(q, 0.0f), 15.0f);
-      packed |= (uint32_t)q << (4 * j);
-    }
-  }
-  meta_bits = (uint32_t)f2h(mn) | ((uint32_t)__builtin_bit_cast(uint16_t, s16) << 16);
-  return packed;
+  uint32_t packed[1];
+  quant_group<8, 8>(v, packed, meta_bits);
+  return packed[0];
 }
 
 __device__ inline uint4 load8(const uint16_t* p, bool aligned) {

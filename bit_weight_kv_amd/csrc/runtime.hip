@@ -188,8 +188,8 @@ fq_status layer_compute(fq_model* m, int l, const fq_kv_layer& kv, int64_t b0, i
   void* s = (void*)st;
   FQ_TRY(fq_layernorm(x, M, h, h, ln1g, ln1b, 1e-5f, m->h1, h, s));
   const float qscale = 1.0f / std::sqrt((float)m->d());
-  FQ_TRY(fq_dequant_gemm(m->h1, M, h, &wq, b_qkv, nullptr, 0, FQ_EPI_BIAS | FQ_EPI_QSCALE, qscale, h, m->qkv, 3 * h, s));
-  FQ_TRY(fq_kv_append(&kv, m->qkv + h, m->qkv + 2 * h, 3 * h, b0, B, T, pos, s));
+  // QKV projection; K/V go to the cache (quantised in the GEMM epilogue at prefill sizes)
+  FQ_TRY(fq_qkv_gemm_append(m->h1, M, h, &wq, b_qkv, qscale, &kv, b0, B, T, pos, m->qkv, 3 * h, s));
   if (T == 1)
     FQ_TRY(fq_decode_attention(m->qkv, 3 * h, &kv, b0, B, pos + 1, m->att, h, s));
   else

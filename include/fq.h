@@ -184,6 +184,23 @@ fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer*
 fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
                                int64_t T, int64_t pos, uint16_t* out, int64_t ldo, void* stream);
 
+/* QKV projection with the K/V append fused into its epilogue (FlexGen
+ * README, "Extreme Compression": the attention cache is stored in 4 bits; the
+ * fusion is this library's): the same results as
+ *   fq_dequant_gemm(A, M, lda, W, bias, NULL, 0, BIAS | QSCALE, qscale, h, C, ldc)
+ *   fq_kv_append(kv, C + h, C + 2h, ldc, b0, B, T, pos)
+ * bit for bit (q columns of C, cache codes and {min, scale} or fp16 entries).
+ *   W: [3h, K] rows q | k | v with h = kv->heads * kv->head_dim;  bias [3h] or NULL
+ *   A: device fp16 [M, K], M = B * T, row b*T + t = token t of sequence b0 + b
+ *   C: device fp16 [M, >= 3h] (ldc); columns [0, h) receive the scaled queries.
+ *      Columns [h, 3h) are written only where the fused form does not apply
+ *      (small M, fp16 weights, misaligned buffers); callers read only q.
+ * Errors: FQ_ERR_INVALID for M != B*T, W->n != 3h, ranges beyond the cache,
+ * and the argument errors of the two calls above. */
+fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const uint16_t* bias,
+                             float qscale, const fq_kv_layer* kv, int64_t b0, int64_t B, int64_t T, int64_t pos,
+                             uint16_t* C, int64_t ldc, void* stream);
+
 /* LayerNorm over rows: y = (x - mean) / sqrt(var + eps) * gamma + beta with
  * fp32 statistics (biased variance) and one rounding to fp16.
  *   x, y: device fp16 [M, h] with strides ldx, ldy;  gamma, beta: device fp16 [h]. */

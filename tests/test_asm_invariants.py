@@ -84,5 +84,5 @@ def test_inline_asm_mfma_kernels_keep_accumulators_in_place(gemm_asm):
         assert not bad, f"{name}: accumulator traffic between inline-asm MFMAs: {bad[:4]}"
         assert "scratch_" not in body, f"{name}: spills to scratch"
     # the 4-bit prefill kernel and every decode instantiation are covered
-    assert any("gemm_wide8_kernel" in n for n in checked), checked
+    assert sum("gemm_wide8_kernel" in n for n in checked) >= 2, checked  # plain and fused K/V append
     assert sum("gemm_decode_kernel" in n for n in checked) >= 4, checked
