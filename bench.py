@@ -43,6 +43,11 @@ CONFIGS = {
                                       desc="OPT-175B shape, batch 256: the 4-bit KV cache (184 GB) leaves HBM for 78 "
                                            "layers of 4-bit weights; the other 18 stream from pinned host memory in "
                                            "packed form (0.5625 byte per weight) every pass"),
+    "opt175b-4bit-b256-kvoffload": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=256,
+                                        prompt=512, gen=32, compress_weight=True, cache_resident_layers=84,
+                                        desc="OPT-175B shape, batch 256: all 4-bit weights in HBM; the 4-bit KV cache "
+                                             "of layers 84-95 (23 GB) in pinned host memory, its valid prefix staged "
+                                             "in and new positions written back every pass"),
     "opt175b-4bit-weights-f16-cache": dict(hidden=12288, heads=96, ffn=49152, layers=96, vocab=50272, batch=48,
                                            prompt=512, gen=32, compress_weight=True, compress_cache=False,
                                            desc="OPT-175B shape, weight-only compression: 4-bit g64 weights, fp16 KV "
@@ -380,7 +385,8 @@ def main():
     model = fq.Model(cfg["hidden"], cfg["heads"], cfg["ffn"], cfg["layers"], vocab=cfg["vocab"], max_pos=P + G + 2,
                      compress_weight=cfg["compress_weight"], resident_layers=cfg.get("resident_layers", -1),
                      host_layers=cfg.get("host_layers", 0), overlap=True, max_tokens=args.max_tokens,
-                     compress_cache=cfg.get("compress_cache", True))
+                     compress_cache=cfg.get("compress_cache", True),
+                     cache_resident_layers=cfg.get("cache_resident_layers", -1))
     model.init_random(args.seed)
     kv = fq.KVCache(model, B, P + G)
     last = [time.time()]
@@ -403,7 +409,7 @@ def main():
     t_start = time.perf_counter()
     for s in range(args.steps):
         out, st = fq.fq_generate(model, kv, ids, G)
-        stats.append((st.prefill_s, st.decode_s, st.h2d_bytes, st.h2d_s))
+        stats.append((st.prefill_s, st.decode_s, st.h2d_bytes, st.h2d_s, st.kv_h2d_bytes, st.kv_d2h_bytes))
         log(f"[bench] step {s}: {st.tokens_per_s:.2f} tok/s (prefill {st.prefill_s:.2f} s, decode {st.decode_s:.2f} s)")
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
@@ -422,7 +428,9 @@ def main():
         "phases": {"prefill_s": round(float(np.mean([s[0] for s in stats])), 3),
                    "decode_s": round(float(np.mean([s[1] for s in stats])), 3),
                    "h2d_GB": round(float(np.mean([s[2] for s in stats])) / 1e9, 2),
-                   "h2d_busy_s": round(float(np.mean([s[3] for s in stats])), 3)},
+                   "h2d_busy_s": round(float(np.mean([s[3] for s in stats])), 3),
+                   "kv_h2d_GB": round(float(np.mean([s[4] for s in stats])) / 1e9, 2),
+                   "kv_d2h_GB": round(float(np.mean([s[5] for s in stats])) / 1e9, 2)},
         "roofline": roof,
         "kernels": kernel_table(kstats, args.config),
     }

@@ -54,7 +54,7 @@ class fq_model_config(ctypes.Structure):
 
 class fq_policy(ctypes.Structure):
     _fields_ = [("compress_weight", c_i32), ("compress_cache", c_i32), ("resident_layers", c_i32),
-                ("host_layers", c_i32), ("overlap", c_i32), ("max_tokens", c_i64)]
+                ("host_layers", c_i32), ("overlap", c_i32), ("max_tokens", c_i64), ("cache_resident_layers", c_i32)]
 
 
 class fq_layer_weights(ctypes.Structure):
@@ -72,7 +72,7 @@ KERNEL_CLASSES = ("gemm_prefill", "gemm_decode", "lm_head", "decode_attention", 
 
 class fq_gen_stats(ctypes.Structure):
     _fields_ = [("prefill_s", c_f64), ("decode_s", c_f64), ("tokens_per_s", c_f64), ("h2d_bytes", c_f64),
-                ("h2d_s", c_f64)]
+                ("h2d_s", c_f64), ("kv_h2d_bytes", c_f64), ("kv_d2h_bytes", c_f64)]
 
 
 _P = ctypes.POINTER
@@ -244,10 +244,10 @@ class Model:
     """Owner of an fq_model handle (fq_model_create / fq_model_destroy)."""
 
     def __init__(self, hidden, heads, ffn, layers, vocab=0, max_pos=0, compress_weight=True, resident_layers=-1,
-                 host_layers=0, overlap=True, max_tokens=16384, compress_cache=True):
+                 host_layers=0, overlap=True, max_tokens=16384, compress_cache=True, cache_resident_layers=-1):
         self.cfg = fq_model_config(hidden, heads, ffn, layers, vocab, max_pos)
         self.pol = fq_policy(int(compress_weight), int(compress_cache), resident_layers, host_layers, int(overlap),
-                             max_tokens)
+                             max_tokens, cache_resident_layers)
         h = c_vp()
         _check(_lib.fq_model_create(ctypes.byref(self.cfg), ctypes.byref(self.pol), ctypes.byref(h)))
         self.handle = h

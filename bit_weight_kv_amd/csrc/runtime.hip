@@ -90,11 +90,23 @@ struct fq_model {
   bool streamed(int l) const { return layers[l].host_blob >= 0; }
 };
 
+// One buffer per layer, laid out [k codes | v codes | k meta | v meta] (4-bit)
+// or [k | v] (fp16), each tensor [batch, heads, capacity, per-position bytes].
 struct fq_kv {
   int layers = 0;
-  std::vector<fq_kv_layer> views;
+  std::vector<fq_kv_layer> views;  // device views; host views for offloaded layers
   std::vector<void*> allocs;
   int device = 0;
+  // offloaded layers (pinned host memory, staged through two device buffers)
+  std::vector<uint8_t*> host;  // per layer: host buffer or nullptr (resident)
+  uint8_t* stage[2] = {nullptr, nullptr};
+  fq_kv_layer stage_view[2] = {};
+  int staged[2] = {-1, -1};
+  size_t layer_bytes = 0;
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
+  double h2d_bytes = 0, d2h_bytes = 0;
+  bool offloaded(int l) const { return host[l] != nullptr; }
 };
 
 using namespace fq;
@@ -239,6 +251,64 @@ fq_status stream_collect(fq_model* m) {
   return FQ_OK;
 }
 
+// ---- cache offload ----------------------------------------------------------
+// Copy positions [p0, p1) of sequences [b0, b1) (every head, K and V, codes
+// and meta) between two buffers of one layer's cache layout: one strided copy
+// per tensor (rows = (sequence, head) pairs, pitch = capacity positions).
+// `dst` and `src` are views of the same shape and format.
+fq_status kv_copy_positions(const fq_kv_layer& dst, const fq_kv_layer& src, int64_t b0, int64_t b1, int64_t p0,
+                            int64_t p1, hipMemcpyKind kind, hipStream_t st, double* bytes) {
+  if (p1 <= p0 || b1 <= b0) return FQ_OK;
+  const int64_t H = dst.heads, cap = dst.capacity, d = dst.head_dim;
+  struct T {
+    const void* src;
+    void* dst;
+    size_t e;  // bytes per (sequence, head, position)
+  };
+  std::vector<T> ts;
+  if (kv_is_f16(dst)) {
+    ts = {{src.k16, dst.k16, (size_t)d * 2}, {src.v16, dst.v16, (size_t)d * 2}};
+  } else {
+    ts = {{src.k_codes, dst.k_codes, (size_t)d / 2}, {src.v_codes, dst.v_codes, (size_t)d / 2},
+          {src.k_meta, dst.k_meta, (size_t)(d / 64) * 4}, {src.v_meta, dst.v_meta, (size_t)(d / 64) * 4}};
+  }
+  for (const T& t : ts) {
+    const size_t pitch = (size_t)cap * t.e, off = (size_t)b0 * H * pitch + (size_t)p0 * t.e;
+    const size_t width = (size_t)(p1 - p0) * t.e, height = (size_t)(b1 - b0) * H;
+    FQ_HIP(hipMemcpy2DAsync((uint8_t*)t.dst + off, pitch, (const uint8_t*)t.src + off, pitch, width, height, kind,
+                            st));
+    *bytes += (double)width * height;
+  }
+  return FQ_OK;
+}
+
+// Stage offloaded layer l into slot l%2 on the cache copy stream: positions
+// [0, pos) of sequences [0, B) (the prefix the pass reads; the new positions
+// are written by the layer itself), after the slot's previous layer has been
+// written back (event consumed).
+fq_status kv_issue(fq_kv* kv, int l, int64_t B, int64_t pos) {
+  const int slot = l & 1;
+  if (kv->staged[slot] == l) return FQ_OK;
+  FQ_HIP(hipStreamWaitEvent(kv->copy_stream, kv->consumed[slot], 0));
+  FQ_TRY(kv_copy_positions(kv->stage_view[slot], kv->views[l], 0, B, 0, pos, hipMemcpyHostToDevice,
+                           kv->copy_stream, &kv->h2d_bytes));
+  FQ_HIP(hipEventRecord(kv->copied[slot], kv->copy_stream));
+  kv->staged[slot] = l;
+  return FQ_OK;
+}
+
+// After layer l computed on `st`: write positions [pos, pos+T) back to host
+// memory on the copy stream and release the slot.
+fq_status kv_writeback(fq_kv* kv, int l, int64_t B, int64_t T, int64_t pos, hipStream_t st) {
+  const int slot = l & 1;
+  FQ_HIP(hipEventRecord(kv->done[slot], st));
+  FQ_HIP(hipStreamWaitEvent(kv->copy_stream, kv->done[slot], 0));
+  FQ_TRY(kv_copy_positions(kv->views[l], kv->stage_view[slot], 0, B, pos, pos + T, hipMemcpyDeviceToHost,
+                           kv->copy_stream, &kv->d2h_bytes));
+  FQ_HIP(hipEventRecord(kv->consumed[slot], kv->copy_stream));
+  return FQ_OK;
+}
+
 // Run layers 0..L-1 over groups of at most cs sequences (layer-major, so a
 // streamed layer is copied once per pass and reused by every group).  x holds
 // B*T rows and is updated in place.
@@ -246,6 +316,7 @@ fq_status run_layers(fq_model* m, fq_kv* kv, int64_t B, int64_t T, int64_t pos, 
                      hipStream_t st) {
   const int L = m->cfg.layers;
   const int64_t h = m->h();
+  kv->staged[0] = kv->staged[1] = -1;  // staged caches are valid within one pass only
   for (int l = 0; l < L; ++l) {
     uint8_t* sp = nullptr;
     if (m->streamed(l)) {
@@ -254,14 +325,22 @@ fq_status run_layers(fq_model* m, fq_kv* kv, int64_t B, int64_t T, int64_t pos, 
       FQ_HIP(hipStreamWaitEvent(st, m->copied[slot], 0));
       sp = m->stage[slot];
     }
-    // prefetch layer l+1 into the other slot while layer l computes
+    const fq_kv_layer* view = &kv->views[l];
+    if (kv->offloaded(l)) {
+      FQ_TRY(kv_issue(kv, l, B, pos));
+      FQ_HIP(hipStreamWaitEvent(st, kv->copied[l & 1], 0));
+      view = &kv->stage_view[l & 1];
+    }
+    // prefetch layer l+1 (weights, cache) into the other slots while layer l computes
     if (m->pol.overlap && l + 1 < L && m->streamed(l + 1)) FQ_TRY(stream_issue(m, l + 1));
+    if (m->pol.overlap && l + 1 < L && kv->offloaded(l + 1)) FQ_TRY(kv_issue(kv, l + 1, B, pos));
     for (int64_t b0 = 0; b0 < B; b0 += cs) {
       const int64_t nb = std::min(cs, B - b0);
       uint16_t* xc = x + b0 * T * h;
-      FQ_TRY(layer_compute(m, l, kv->views[l], b0, nb, T, pos, xc, xc, sp, st));
+      FQ_TRY(layer_compute(m, l, *view, b0, nb, T, pos, xc, xc, sp, st));
     }
     if (m->streamed(l)) FQ_HIP(hipEventRecord(m->consumed[l & 1], st));
+    if (kv->offloaded(l)) FQ_TRY(kv_writeback(kv, l, B, T, pos, st));
   }
   return FQ_OK;
 }
@@ -544,10 +623,38 @@ extern "C" fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, in
   return FQ_OK;
 }
 
+namespace {
+// View of one layer's cache inside a buffer of the layout described at fq_kv.
+fq_kv_layer kv_view_at(uint8_t* base, bool f16, int64_t batch, int H, int64_t d, int64_t capacity) {
+  const size_t codes = (size_t)batch * H * capacity * d / 2;
+  const size_t meta = (size_t)batch * H * capacity * (d / 64) * 4;
+  const size_t elems = (size_t)batch * H * capacity * d;
+  fq_kv_layer v{};
+  if (f16) {
+    v.bits = 16;
+    v.k16 = reinterpret_cast<uint16_t*>(base);
+    v.v16 = reinterpret_cast<uint16_t*>(base) + elems;
+  } else {
+    v.bits = 4;
+    v.k_codes = base;
+    v.v_codes = base + codes;
+    v.k_meta = reinterpret_cast<uint16_t*>(base + 2 * codes);
+    v.v_meta = reinterpret_cast<uint16_t*>(base + 2 * codes + meta);
+  }
+  v.batch = batch;
+  v.heads = H;
+  v.head_dim = (int32_t)d;
+  v.capacity = capacity;
+  v.group = FQ_GROUP;
+  return v;
+}
+}  // namespace
+
 extern "C" fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capacity, fq_kv** out) {
   clear_error();
   FQ_CHECK_ARG(m && out, "fq_kv_create: NULL argument");
   FQ_CHECK_ARG(batch > 0 && capacity > 0, "fq_kv_create: bad size");
+  FQ_CHECK_ARG(m->pol.cache_resident_layers >= -1, "fq_kv_create: bad cache_resident_layers");
   *out = nullptr;
   fq_kv* kv = new (std::nothrow) fq_kv();
   if (!kv) return fail(FQ_ERR_OOM, "fq_kv_create: host allocation failed");
@@ -556,36 +663,47 @@ extern "C" fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capa
   const int H = m->cfg.heads;
   const int64_t d = m->d();
   const bool f16 = !m->pol.compress_cache;
-  const size_t codes = (size_t)batch * H * capacity * d / 2;
-  const size_t meta = (size_t)batch * H * capacity * (d / 64) * 4;
-  const size_t elems = (size_t)batch * H * capacity * d;  // fp16 cache: elements per tensor
-  for (int l = 0; l < kv->layers; ++l) {
+  const size_t elems = (size_t)batch * H * capacity * d;
+  kv->layer_bytes = f16 ? 2 * elems * 2 : 2 * (elems / 2 + elems / 64 * 4);
+  const int L = kv->layers;
+  const int resident = m->pol.cache_resident_layers < 0 ? L : std::min(L, m->pol.cache_resident_layers);
+  auto bail = [&](fq_status s, const char* msg) {
+    fq_kv_destroy(kv);
+    return fail(s, msg);
+  };
+  kv->host.assign(L, nullptr);
+  for (int l = 0; l < L; ++l) {
     uint8_t* base = nullptr;
-    hipError_t e = hipMalloc(&base, f16 ? 2 * elems * 2 : 2 * (codes + meta));
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      fq_kv_destroy(kv);
-      return fail(FQ_ERR_OOM, "fq_kv_create: device allocation failed");
-    }
-    kv->allocs.push_back(base);
-    fq_kv_layer v{};
-    if (f16) {
-      v.bits = 16;
-      v.k16 = reinterpret_cast<uint16_t*>(base);
-      v.v16 = reinterpret_cast<uint16_t*>(base) + elems;
+    if (l < resident) {
+      if (hipMalloc(&base, kv->layer_bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return bail(FQ_ERR_OOM, "fq_kv_create: device allocation failed");
+      }
+      kv->allocs.push_back(base);
     } else {
-      v.bits = 4;
-      v.k_codes = base;
-      v.v_codes = base + codes;
-      v.k_meta = reinterpret_cast<uint16_t*>(base + 2 * codes);
-      v.v_meta = reinterpret_cast<uint16_t*>(base + 2 * codes + meta);
+      if (hipHostMalloc((void**)&base, kv->layer_bytes, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        return bail(FQ_ERR_OOM, "fq_kv_create: pinned host allocation failed");
+      }
+      kv->host[l] = base;
     }
-    v.batch = batch;
-    v.heads = H;
-    v.head_dim = (int32_t)d;
-    v.capacity = capacity;
-    v.group = FQ_GROUP;
-    kv->views.push_back(v);
+    kv->views.push_back(kv_view_at(base, f16, batch, H, d, capacity));
+  }
+  if (resident < L) {
+    for (int k = 0; k < 2; ++k) {
+      if (hipMalloc(&kv->stage[k], kv->layer_bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        kv->stage[k] = nullptr;
+        return bail(FQ_ERR_OOM, "fq_kv_create: staging allocation failed");
+      }
+      kv->stage_view[k] = kv_view_at(kv->stage[k], f16, batch, H, d, capacity);
+      if (hipEventCreateWithFlags(&kv->copied[k], hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&kv->done[k], hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&kv->consumed[k], hipEventDisableTiming) != hipSuccess)
+        return bail(FQ_ERR_HIP, "fq_kv_create: event creation failed");
+    }
+    if (hipStreamCreateWithFlags(&kv->copy_stream, hipStreamNonBlocking) != hipSuccess)
+      return bail(FQ_ERR_HIP, "fq_kv_create: copy stream creation failed");
   }
   *out = kv;
   return FQ_OK;
@@ -595,6 +713,14 @@ extern "C" fq_status fq_kv_destroy(fq_kv* kv) {
   if (!kv) return FQ_OK;
   (void)hipDeviceSynchronize();
   for (void* p : kv->allocs) (void)hipFree(p);
+  for (uint8_t* p : kv->host)
+    if (p) (void)hipHostFree(p);
+  for (int k = 0; k < 2; ++k) {
+    if (kv->stage[k]) (void)hipFree(kv->stage[k]);
+    for (hipEvent_t e : {kv->copied[k], kv->done[k], kv->consumed[k]})
+      if (e) (void)hipEventDestroy(e);
+  }
+  if (kv->copy_stream) (void)hipStreamDestroy(kv->copy_stream);
   delete kv;
   return FQ_OK;
 }
@@ -620,14 +746,25 @@ extern "C" fq_status fq_layer_step(fq_model* m, int32_t layer, fq_kv* kv, int64_
   if (B == 0 || T == 0) return FQ_OK;
   FQ_CHECK_ARG(x && y && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0, "fq_layer_step: x/y NULL or misaligned");
   hipStream_t st = as_stream(stream);
+  uint8_t* sp = nullptr;
   if (m->streamed(layer)) {
     // synchronous staging of a host-resident layer into slot 0
     FQ_HIP(hipMemcpyAsync(m->stage[0], m->host_blobs[m->layers[layer].host_blob], m->blob_bytes(),
                           hipMemcpyHostToDevice, st));
     m->staged[0] = -1;
-    return layer_compute(m, layer, v, b0, B, T, pos, x, y, m->stage[0], st);
+    sp = m->stage[0];
   }
-  return layer_compute(m, layer, v, b0, B, T, pos, x, y, nullptr, st);
+  if (!kv->offloaded(layer)) return layer_compute(m, layer, v, b0, B, T, pos, x, y, sp, st);
+  // offloaded cache: stage the prefix of these sequences into slot 0, run the
+  // layer, write the new positions back, all on `stream`, then wait
+  FQ_HIP(hipStreamSynchronize(kv->copy_stream));
+  double bytes = 0;
+  FQ_TRY(kv_copy_positions(kv->stage_view[0], v, b0, b0 + B, 0, pos, hipMemcpyHostToDevice, st, &bytes));
+  kv->staged[0] = -1;
+  FQ_TRY(layer_compute(m, layer, kv->stage_view[0], b0, B, T, pos, x, y, sp, st));
+  FQ_TRY(kv_copy_positions(v, kv->stage_view[0], b0, b0 + B, pos, pos + T, hipMemcpyDeviceToHost, st, &bytes));
+  FQ_HIP(hipStreamSynchronize(st));
+  return FQ_OK;
 }
 
 namespace {
@@ -664,6 +801,7 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
   m->h2d_bytes = 0;
   m->h2d_s = 0;
   m->n_copies = 0;
+  kv->h2d_bytes = kv->d2h_bytes = 0;
 
   hipEvent_t ev[3];
   for (int i = 0; i < 3; ++i) FQ_HIP(hipEventCreate(&ev[i]));
@@ -719,6 +857,7 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
       progress(reported + 1, gen_len, progress_user);
     }
     FQ_HIP(hipEventSynchronize(ev[2]));
+    if (kv->copy_stream) FQ_HIP(hipStreamSynchronize(kv->copy_stream));  // last write-backs
     FQ_TRY(stream_collect(m));
     // d_out is [gen_len, B]; out_ids is [B, gen_len]
     std::vector<int32_t> tmp((size_t)gen_len * B);
@@ -734,6 +873,8 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
       stats->tokens_per_s = (double)B * gen_len / (stats->prefill_s + stats->decode_s);
       stats->h2d_bytes = m->h2d_bytes;
       stats->h2d_s = m->h2d_s;
+      stats->kv_h2d_bytes = kv->h2d_bytes;
+      stats->kv_d2h_bytes = kv->d2h_bytes;
     }
     return FQ_OK;
   };

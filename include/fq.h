@@ -231,6 +231,11 @@ typedef struct {
                               (l - resident_layers) % host_layers; 0 = one per layer */
   int32_t overlap;         /* 1: prefetch layer l+1 on a copy stream while layer l computes */
   int64_t max_tokens;      /* rows of the per-call activation workspace (0: default 16384) */
+  int32_t cache_resident_layers; /* KV cache placement (README, "Get Started": the --percent pair
+                              for the cache): layers 0..n-1 keep their cache in HBM, the rest in
+                              pinned host memory, staged through two device buffers per pass
+                              (the valid prefix copied in, the new positions copied back);
+                              -1 = all in HBM */
 } fq_policy;
 
 typedef struct fq_model fq_model;
@@ -279,7 +284,9 @@ fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, int32_t which
 
 /* KV cache for `batch` sequences of up to `capacity` positions, all layers:
  * 4-bit (0.5625 byte per cached element) when the policy compresses the
- * cache, else fp16 (2 bytes). */
+ * cache, else fp16 (2 bytes).  Layers at or beyond the policy's
+ * cache_resident_layers live in pinned host memory (fq_kv_layer_view then
+ * returns host pointers). */
 fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capacity, fq_kv** out);
 fq_status fq_kv_destroy(fq_kv* kv);
 fq_status fq_kv_layer_view(const fq_kv* kv, int32_t layer, fq_kv_layer* out);
@@ -302,7 +309,9 @@ typedef struct {
   double decode_s;       /* the remaining gen_len-1 steps */
   double tokens_per_s;   /* B * gen_len / (prefill_s + decode_s) */
   double h2d_bytes;      /* weight bytes streamed from host memory */
-  double h2d_s;          /* copy-stream busy time (sum of copy intervals) */
+  double h2d_s;          /* weight copy-stream busy time (sum of copy intervals) */
+  double kv_h2d_bytes;   /* cache bytes staged in from host memory (offloaded layers) */
+  double kv_d2h_bytes;   /* cache bytes written back to host memory */
 } fq_gen_stats;
 
 /* Greedy generation: embed the prompt, prefill every layer (prompt chunked

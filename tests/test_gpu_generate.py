@@ -74,6 +74,31 @@ def test_generate_compression_toggles_match_oracle(weight, cache):
     _compare(out, lg, ref, f"weight={weight} cache={cache}")
 
 
+@pytest.mark.parametrize("cache", [True, False])
+def test_offloaded_cache_equals_resident(cache):
+    """KV cache of layers beyond cache_resident_layers in pinned host memory
+    (staged prefix in, new positions back, per pass): identical tokens and
+    logits to the all-resident cache, with and without prefetch overlap and
+    together with streamed weights; the copied byte counts are the prefix and
+    new-position volumes."""
+    L, B, P, G = 4, 3, 12, 5
+    log(f"offloaded cache compress_cache={cache}")
+    ids, a_out, a_lg, _ = _gpu_generate(L, B, P, G, seed=5, compress_cache=cache)
+    runs = [_gpu_generate(L, B, P, G, seed=5, compress_cache=cache, cache_resident_layers=1),
+            _gpu_generate(L, B, P, G, seed=5, compress_cache=cache, cache_resident_layers=0, overlap=False),
+            _gpu_generate(L, B, P, G, seed=5, compress_cache=cache, cache_resident_layers=2, resident_layers=1)]
+    for _, out, lg, _ in runs:
+        assert np.array_equal(out, a_out) and np.array_equal(lg, a_lg)
+    d = H // NH
+    per_pos = B * NH * (2 * (d // 2 + d // 64 * 4) if cache else 2 * d * 2)  # one position, all sequences, K and V
+    h2d_pos = (G - 1) * P + (G - 2) * (G - 1) // 2                        # decode pass at pos stages [0, pos)
+    d2h_pos = P + G - 1                                                    # every position written back once
+    for (_, _, _, st), off in zip(runs, (L - 1, L, L - 2)):
+        assert st.kv_h2d_bytes == off * per_pos * h2d_pos and st.kv_d2h_bytes == off * per_pos * d2h_pos
+    mcfg = ModelConfig(LayerConfig(H, NH, F, compress_cache=cache), L, V, P + G + 2)
+    _compare(runs[0][1], runs[0][2], oracle.generate(ids, G, 5, mcfg), f"offloaded cache={cache}")
+
+
 def test_generate_deterministic_and_batch_independent():
     L, B, P, G = 2, 3, 12, 4
     ids, out1, lg1, _ = _gpu_generate(L, B, P, G, seed=1)

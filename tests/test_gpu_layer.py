@@ -94,7 +94,8 @@ def _copy_dev(dst, src, nbytes):
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
-    assert hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), ctypes.c_size_t(nbytes), 3) == 0
+    # hipMemcpyDefault: the source may be device memory or pinned host memory (offloaded cache)
+    assert hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), ctypes.c_size_t(nbytes), 4) == 0
 
 
 def _validate_f16_differences(gpu, ref16, ref64, what):
@@ -122,10 +123,11 @@ def _validate_f16_differences(gpu, ref16, ref64, what):
     return len(diff)
 
 
-def _layer_case(cfg, B, P, T, seed, bias_sigma, check_seqs=None, chunk=None, via_init=False):
+def _layer_case(cfg, B, P, T, seed, bias_sigma, check_seqs=None, chunk=None, via_init=False, cache_resident=-1):
     h = cfg.hidden
     model = fq.Model(h, cfg.heads, cfg.ffn, 1, max_tokens=max(B * P if chunk is None else chunk * P, B),
-                     compress_weight=cfg.compress_weight, compress_cache=cfg.compress_cache)
+                     compress_weight=cfg.compress_weight, compress_cache=cfg.compress_cache,
+                     cache_resident_layers=cache_resident)
     params = oracle.layer_params(seed, cfg, 0, bias_sigma)
     if via_init:
         model.init_random(seed, bias_sigma)
@@ -199,6 +201,15 @@ def test_layer_compression_toggles(weight, cache):
     log(f"layer tiny compress_weight={weight} compress_cache={cache}")
     cfg = LayerConfig(256, 4, 1024, compress_weight=weight, compress_cache=cache)
     _layer_case(cfg, B=8, P=64, T=4, seed=1, bias_sigma=0.02)
+
+
+@pytest.mark.parametrize("cache", [True, False])
+def test_layer_offloaded_cache(cache):
+    """The layer's cache in pinned host memory (staged per call), prefill in
+    chunks of 3 sequences then decode steps, 4-bit and fp16 cache."""
+    log(f"layer offloaded cache compress_cache={cache}")
+    cfg = LayerConfig(256, 4, 1024, compress_cache=cache)
+    _layer_case(cfg, B=8, P=64, T=4, seed=2, bias_sigma=0.02, chunk=3, cache_resident=0)
 
 
 def test_layer_weight_only_ragged_shapes():
