@@ -309,11 +309,13 @@ def kernel_only_decode_attention(fq, synth, torch, cfg, args):
 def kernel_only_gemm(fq, synth, torch, cfg, args, prefill):
     """The projection GEMMs of one layer, exactly as the prompt pass (prefill)
     or one decode step launches them: the batch's B*P prompt rows in chunks of
-    at most --max-tokens rows (or the B rows of a decode step), each chunk
-    through the QKV (bias, query scaling), out (bias, residual), FC1 (bias,
-    ReLU) and FC2 (bias, residual) products of that layer's packed weights.
-    Every layer of the workload repeats this launch list."""
-    h, F, B, P = cfg["hidden"], cfg["ffn"], cfg["batch"], cfg["prompt"]
+    whole sequences of at most --max-tokens rows (or the B rows of a decode
+    step), each chunk through the QKV (bias, query scaling, K/V appended to a
+    4-bit cache), out (bias, residual), FC1 (bias, ReLU) and FC2 (bias,
+    residual) products of that layer's packed weights.  Every layer of the
+    workload repeats this launch list."""
+    h, F, B, P, H = cfg["hidden"], cfg["ffn"], cfg["batch"], cfg["prompt"], cfg["heads"]
+    d = h // H
     model = fq.Model(h, cfg["heads"], F, 1, vocab=cfg["vocab"], max_pos=P + cfg["gen"] + 2,
                      compress_weight=True, max_tokens=args.max_tokens)
     model.init_random(args.seed)
@@ -321,7 +323,14 @@ def kernel_only_gemm(fq, synth, torch, cfg, args, prefill):
     W = {i: fq.fq_weight(fq.FQ_WEIGHT_PACKED4, model.packed_weight(0, i), None, n, k)
          for i, (n, k) in shapes.items()}
     total = B * P if prefill else B  # a decode step runs every sequence's one new row
-    rows = min(total, args.max_tokens)
+    T = P if prefill else 1
+    chunk = max(1, args.max_tokens // T) * T  # rows per launch: whole sequences
+    rows = min(total, chunk)
+    cap = P + cfg["gen"] - 1
+    cache = [torch.zeros((B, H, cap, d // 2), dtype=torch.uint8, device="cuda"),
+             torch.zeros((B, H, cap, d // 64, 2), dtype=torch.float16, device="cuda")]
+    cache += [torch.zeros_like(cache[0]), torch.zeros_like(cache[1])]
+    kv = fq.kv_layer_view(*cache)
     def act(cols, stream):
         t = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
         fq.fq_synth_normal_f16(t, args.seed, stream, 1.0)
@@ -332,10 +341,10 @@ def kernel_only_gemm(fq, synth, torch, cfg, args, prefill):
     bias = torch.zeros(max(3 * h, F), dtype=torch.float16, device="cuda")
     E = fq
     launches = []
-    for r0 in range(0, total, args.max_tokens):
-        M = min(args.max_tokens, total - r0)
-        fq.fq_dequant_gemm(h1[:M], W[0], qkv[:M], bias=bias, epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_QSCALE,
-                           qscale=(h // cfg["heads"]) ** -0.5, qscale_cols=h)
+    for r0 in range(0, total, chunk):
+        M = min(chunk, total - r0)
+        fq.fq_qkv_gemm_append(h1[:M], W[0], bias[:3 * h], d ** -0.5, kv, r0 // T, M // T, T, 0 if prefill else P,
+                              qkv[:M])
         fq.fq_dequant_gemm(att[:M], W[1], x1[:M], bias=bias, residual=x[:M],
                            epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_RESIDUAL)
         fq.fq_dequant_gemm(h1[:M], W[2], f[:M], bias=bias, epilogue=E.FQ_EPI_BIAS | E.FQ_EPI_RELU)

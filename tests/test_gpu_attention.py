@@ -130,3 +130,39 @@ def test_decode_full_size_sampled():
         ref = oracle.attention_decode(q[None, None], kh, vh)[0, 0]
         got = host(out[b, hh * d:(hh + 1) * d])
         assert_close(got, ref, rel=2e-3, abs_=4e-3, what=f"full-size b={b} h={hh}")
+
+
+def test_prefill_full_size_sampled():
+    """OPT-175B shape at prefill: 144 sequences x 96 heads x 128, a 512-token
+    prompt attended causally over its 4-bit cache in the launch the prompt pass
+    makes; sampled (b, h) pairs checked at every query position."""
+    B, H, d, T = 144, 96, 128, 512
+    h = H * d
+    log("prefill attention full-size")
+    kc = torch.empty((B, H, T, d // 2), dtype=torch.uint8, device="cuda:0")
+    km = torch.empty((B, H, T, d // 64, 2), dtype=torch.float16, device="cuda:0")
+    vc, vm = torch.empty_like(kc), torch.empty_like(km)
+    view = fq.kv_layer_view(kc, km, vc, vm)
+    chunk = 16
+    kbuf = torch.empty((chunk * T, h), dtype=torch.float16, device="cuda:0")
+    vbuf = torch.empty_like(kbuf)
+    for b0 in range(0, B, chunk):
+        fq.fq_synth_normal_f16(kbuf, 6, synth.STREAM["aux"] + 33, 1.0, first=b0 * T * h)
+        fq.fq_synth_normal_f16(vbuf, 6, synth.STREAM["aux"] + 34, 1.0, first=b0 * T * h)
+        fq.fq_kv_append(view, kbuf, vbuf, h, b0, chunk, T, 0)
+    del kbuf, vbuf
+    qd = torch.empty((B * T, h), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(qd, 6, synth.STREAM["aux"] + 35, 1.0 / d ** 0.5)
+    out = torch.empty((B * T, h), dtype=torch.float16, device="cuda:0")
+    fq.fq_prefill_attention(qd, view, 0, B, T, 0, out)
+    torch.cuda.synchronize()
+    for b, hh in ((0, 0), (77, 41), (143, 95)):
+        base = ((b * T + np.arange(T))[:, None] * h + hh * d + np.arange(d)[None]).astype(np.uint64).ravel()
+        k = synth.normal_f16(6, synth.STREAM["aux"] + 33, sigma=1.0, index=base).reshape(T, d)
+        v = synth.normal_f16(6, synth.STREAM["aux"] + 34, sigma=1.0, index=base).reshape(T, d)
+        q = synth.normal_f16(6, synth.STREAM["aux"] + 35, sigma=1.0 / d ** 0.5, index=base).reshape(T, d)
+        kh = oracle.dequant_f64(*oracle.quantize(k))[None, None]
+        vh = oracle.dequant_f64(*oracle.quantize(v))[None, None]
+        ref = oracle.attention_prefill_causal(q.astype(np.float64)[None, None], kh, vh)[0, 0]
+        got = host(out[b * T:(b + 1) * T, hh * d:(hh + 1) * d])
+        assert_close(got, ref, rel=2e-3, abs_=4e-3, what=f"prefill full-size b={b} h={hh}")

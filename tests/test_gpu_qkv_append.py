@@ -92,3 +92,45 @@ def test_fused_append_argument_errors():
                           torch.zeros((2 * h, h // 64, 2), dtype=torch.float16, device="cuda:0"), 2 * h, h)
     with pytest.raises(fq.FqError):   # W is not [3h, K]
         fq.fq_qkv_gemm_append(a, W2, None, 1.0, view, 0, 2, 2, 0, c)
+
+
+def test_fused_append_full_size():
+    """OPT-175B QKV projection in the prompt pass's launch configuration: a
+    16384-row chunk (32 sequences x 512 tokens, sequences 32..63 of a 64-sequence
+    cache), h = 12288, weights generated and quantised on the GPU.  The fused
+    form equals the two-call form on every q value and cache byte; sampled
+    groups match the oracle's quantisation of the projection's fp16 K/V."""
+    from synth.gen import layer_stream
+    H, d, B, T, b0 = 96, 128, 32, 512, 32
+    h = H * d
+    M, N, K = B * T, 3 * h, h
+    log("qkv append full-size")
+    w = torch.empty((N, K), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(w, 0, layer_stream(0, "w_qkv"), 0.02)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda:0")
+    meta = torch.empty((N, K // 64, 2), dtype=torch.float16, device="cuda:0")
+    fq.fq_quantize(w, codes, meta)
+    del w
+    W = fq.weight_packed(codes, meta, N, K)
+    a = torch.empty((M, K), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(a, 0, synth.STREAM["hidden"], 1.0)
+    bias = torch.empty((N,), dtype=torch.float16, device="cuda:0")
+    fq.fq_synth_normal_f16(bias, 0, layer_stream(0, "b_qkv"), 0.02)
+    view1, keep1 = _cache("q4", 64, H, T, d)
+    c1 = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(a, W, c1, bias=bias, epilogue=fq.FQ_EPI_BIAS | fq.FQ_EPI_QSCALE, qscale=d ** -0.5,
+                       qscale_cols=h)
+    fq.fq_kv_append(view1, c1[:, h:], c1[:, 2 * h:], N, b0, B, T, 0)
+    view2, keep2 = _cache("q4", 64, H, T, d)
+    c2 = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fq.fq_qkv_gemm_append(a, W, bias, d ** -0.5, view2, b0, B, T, 0, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1[:, :h], c2[:, :h]), "q columns differ"
+    for t1, t2 in zip(keep1, keep2):
+        assert torch.equal(t1, t2), "cache contents differ"
+    kc, km = keep2[0], keep2[1]
+    for b, t, hh in ((0, 0, 0), (17, 300, 50), (31, 511, 95)):
+        x = host(c1[b * T + t, h + hh * d:h + (hh + 1) * d]).reshape(1, d)
+        rc, rm = oracle.quantize(x)
+        assert np.array_equal(host(kc[b0 + b, hh, t]), rc[0])
+        assert np.array_equal(bits16(host(km[b0 + b, hh, t])), bits16(rm[0]))
