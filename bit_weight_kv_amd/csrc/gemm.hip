@@ -1350,7 +1350,8 @@ fq_status run_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
 // blocks x (K steps per block + ring fill), plus the fp32 partial traffic
 // (written and read back by the reduction) priced at 4 TB/s.
 int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB) {
-  const double step_us = std::max(0.15, 0.06 * MB);
+  // measured: one K step of a block takes ~1.3 us at 9 row groups
+  const double step_us = std::max(0.15, 0.145 * MB);
   int best = 1;
   double best_t = 1e30;
   for (int s = 1; s <= std::min(16, std::max(1, KT / 4)); ++s) {
