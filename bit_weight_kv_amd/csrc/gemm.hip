@@ -617,14 +617,16 @@ __device__ inline void mfma16x16x32_acc_ordered(float4_t& acc, const half8_t& a,
 // (1024 + c), exact fp16 subtract of 1024, one packed fp16 FMA c*s + min with
 // {min, scale} taken from the halves of `ms`.  Its outputs are consumed by
 // later MFMAs only, never inside this block.
-__device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
-                                     const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
-                                     uint32_t w, uint32_t ms, half8_t& out) {
+// General form: MFMA k computes c_k += a_k * b_k.
+__device__ inline void mfma4_rebuild_ab(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a0,
+                                        const half8_t& a1, const half8_t& a2, const half8_t& a3, const half8_t& b0,
+                                        const half8_t& b1, const half8_t& b2, const half8_t& b3, uint32_t w,
+                                        uint32_t ms, half8_t& out) {
   // separate volatile statements keep their order; one accumulator per MFMA
   // statement keeps every accumulator in place (a statement binding several
   // makes the register allocator copy them around)
   uint32_t o0, o1, o2, o3, lo, hi;
-  mfma16x16x32_acc_ordered(c0, a, b0);
+  mfma16x16x32_acc_ordered(c0, a0, b0);
   asm volatile(
       "v_and_b32 %0, 0x0f0f0f0f, %4\n\t"
       "v_lshrrev_b32 %1, 4, %4\n\t"
@@ -633,7 +635,7 @@ __device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, f
       "v_perm_b32 %3, %1, %0, %6"
       : "=&v"(lo), "=&v"(hi), "=&v"(o0), "=&v"(o1)
       : "v"(w), "s"(0x0C040C00u), "s"(0x0C050C01u));
-  mfma16x16x32_acc_ordered(c1, a, b1);
+  mfma16x16x32_acc_ordered(c1, a1, b1);
   asm volatile(
       "v_perm_b32 %0, %5, %4, %6\n\t"
       "v_perm_b32 %1, %5, %4, %7\n\t"
@@ -642,7 +644,7 @@ __device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, f
       "v_or_b32 %0, 0x64006400, %0"
       : "=&v"(o2), "=&v"(o3), "+v"(o0), "+v"(o1)
       : "v"(lo), "v"(hi), "s"(0x0C060C02u), "s"(0x0C070C03u));
-  mfma16x16x32_acc_ordered(c2, a, b2);
+  mfma16x16x32_acc_ordered(c2, a2, b2);
   asm volatile(
       "v_or_b32 %3, 0x64006400, %3\n\t"
       "v_pk_add_f16 %0, %0, %4\n\t"
@@ -651,7 +653,7 @@ __device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, f
       "v_pk_add_f16 %3, %3, %4"
       : "+v"(o0), "+v"(o1), "+v"(o2), "+v"(o3)
       : "s"(0xE400E400u));
-  mfma16x16x32_acc_ordered(c3, a, b3);
+  mfma16x16x32_acc_ordered(c3, a3, b3);
   asm volatile(
       "v_pk_fma_f16 %0, %0, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
       "v_pk_fma_f16 %1, %1, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
@@ -660,6 +662,12 @@ __device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, f
       : "+v"(o0), "+v"(o1), "+v"(o2), "+v"(o3)
       : "v"(ms));
   out = __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
+}
+
+__device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
+                                     const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
+                                     uint32_t w, uint32_t ms, half8_t& out) {
+  mfma4_rebuild_ab(c0, c1, c2, c3, a, a, a, a, b0, b1, b2, b3, w, ms, out);
 }
 
 // One row's 16 accumulators of a K or V group (columns nw + cs .. nw + cs + 15
@@ -1280,6 +1288,158 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __rest
   }
 }
 
+// ---- 4-bit decode GEMM, two waves per SIMD ----------------------------------
+// The same block tile and copy ring as gemm_decode_kernel (256 weight rows x
+// every row of A, K step 64), with 8 waves of 32 weight rows each: two waves
+// share a SIMD, so one wave's LDS and barrier waits overlap the other's
+// MFMAs.  Per K step a wave runs 2 slices x MB row blocks x 2 MFMAs and
+// rebuilds 4 operand words for the next step (its 2 rows x 2 slices), each
+// carried by the 4 MFMAs of a pair of row blocks.
+template <int MB>
+__global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ meta, int64_t N, int64_t K,
+                                                           int k_tiles_per_split, Epilogue epi,
+                                                           float* __restrict__ partial) {
+  constexpr int ROWS = MB * 16, ROWS_PAD = (ROWS + 63) / 64 * 64;
+  constexpr int A_INSTR = ROWS_PAD / 64;  // A copies per wave per step (8 rows of 128 B each)
+  constexpr int PER = A_INSTR + 2;        // + one codes copy + one {min, scale} copy
+  constexpr int A_BYTES = ROWS_PAD * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
+  constexpr int S = 4;
+  static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
+  static_assert(MB >= 4, "two pairs of row blocks per slice carry the reconstructions");
+  static_assert((S - 3) * PER <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t n_blk = (int64_t)blockIdx.x * 256;
+  const int64_t m_base = (int64_t)blockIdx.z * ROWS;
+  const int KT = (int)(K / BK);
+  const int kt0 = blockIdx.y * k_tiles_per_split;
+  const int kt1 = min(KT, kt0 + k_tiles_per_split);
+
+  // A copies: instruction q = wave + 8t fills rows 8q..8q+7 (lane -> row
+  // 8q + lane / 8, slot lane % 8 holding chunk slot ^ (row % 8)); rows past M
+  // are clamped (read, never stored)
+  const uint16_t* a_src[A_INSTR];
+#pragma unroll
+  for (int t = 0; t < A_INSTR; ++t) {
+    const int r = 8 * (wave + 8 * t) + (lane >> 3);
+    a_src[t] = A + min(m_base + r, M - 1) * lda + ((lane & 7) ^ (r & 7)) * 8;
+  }
+  const uint8_t* c_src = codes + min(n_blk + wave * 32 + (lane >> 1), N - 1) * (K / 2) + (lane & 1) * 16;
+  const uint16_t* m_src = meta + min(n_blk + wave * 32 + (lane & 31), N - 1) * (K / 64) * 2;
+  auto issue = [&](int kt, int slot) {
+    const uint32_t st = lds_base + slot * STAGE;
+#pragma unroll
+    for (int t = 0; t < A_INSTR; ++t) dma_lds16(a_src[t] + (int64_t)kt * BK, st + (wave + 8 * t) * 1024);
+    dma_lds16(c_src + (int64_t)kt * 32, st + A_BYTES + wave * 32 * 32);
+    if (lane < 32) dma_lds4(m_src + (int64_t)kt * 2, st + A_BYTES + C_BYTES + wave * 128);
+  };
+  // this lane's weight rows: wave * 32 + 16 j + l16
+  uint2 cw[2];
+  uint32_t cm[2];
+  auto read_codes = [&](int slot) {
+    const uint8_t* st = lds + slot * STAGE + A_BYTES;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = wave * 32 + j * 16 + l16;
+      cw[j] = *reinterpret_cast<const uint2*>(st + row * 32 + g4 * 8);
+      cm[j] = *reinterpret_cast<const uint32_t*>(st + C_BYTES + row * 4);
+    }
+  };
+  auto rebuild = [&](int j, int w, half8_t (&b)[2][2]) {
+    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
+    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
+    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+    uint32_t o[4];
+    dequant8(w ? cw[j].y : cw[j].x, mn2, s2, o);
+    b[w][j] = __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+
+  float4_t acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  if (kt0 < kt1) {
+    for (int t = 0; t < S - 1 && kt0 + t < kt1; ++t) issue(kt0 + t, t);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    half8_t bA[2][2], bB[2][2];
+    read_codes(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) rebuild(j, w, bA);
+    // One K step: MFMAs on `bcur`, step kt+1's operand rebuilt into `bnxt`
+    // by the row-block pairs (0, 1) and (2, 3) of each slice (slice ks
+    // rebuilds word ks of rows 0 and 1).
+    auto step = [&](int kt, half8_t (&bcur)[2][2], half8_t (&bnxt)[2][2]) {
+      const int it = kt - kt0, slot = it % S;
+      if (kt > kt0) {
+        // steps kt and kt+1 complete in every wave; step kt-1's slot free
+        if (kt + S - 2 < kt1)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
+      if (kt + 1 < kt1) read_codes((it + 1) % S);
+      const uint8_t* As_ = lds + slot * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        half8_t af[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = i * 16 + l16, ch = 2 * g4 + ks;
+          af[i] = *reinterpret_cast<const half8_t*>(As_ + r * 128 + ((ch ^ (r & 7)) * 16));
+          __builtin_amdgcn_sched_barrier(0);  // issue in use order
+        }
+        // (past the last step the rebuilds fill an unused buffer: a runtime
+        // condition here would split the MFMA chain)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          mfma4_rebuild_ab(acc[2 * p][0], acc[2 * p][1], acc[2 * p + 1][0], acc[2 * p + 1][1], af[2 * p], af[2 * p],
+                           af[2 * p + 1], af[2 * p + 1], bcur[ks][0], bcur[ks][1], bcur[ks][0], bcur[ks][1],
+                           ks ? cw[p].y : cw[p].x, cm[p], bnxt[ks][p]);
+#pragma unroll
+        for (int i = 4; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) mfma16x16x32_acc_ordered(acc[i][j], af[i], bcur[ks][j]);
+      }
+    };
+    // pairs of steps: every split has an even number of steps (the host
+    // guarantees it), so the MFMA chain is one piece of code
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      step(kt, bA, bB);
+      step(kt + 1, bB, bA);
+    }
+    // the last MFMAs' results are read by VALU instructions below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  }
+
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n_blk + wave * 32 + j * 16 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m_base + i * 16 + 4 * g4 + r;
+        if (m < M && n < N) {
+          if (partial)
+            partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
+          else
+            epilogue_store(epi, m, n, acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
                                                             int64_t N, Epilogue epi) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1367,6 +1527,12 @@ int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB) {
   return best;
 }
 
+// Test/benchmark hook: FQ_DECODE_WAVES=4 selects the 4-wave decode kernel.
+static bool decode_four_waves() {
+  const char* e = getenv("FQ_DECODE_WAVES");
+  return e && e[0] == '4';
+}
+
 template <int MB>
 fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
                      hipStream_t st) {
@@ -1380,9 +1546,15 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
   float* partial = nullptr;
   if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
   const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)splits, (unsigned)zb);
-  gemm_decode_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps, epi,
-                                                     partial);
-  FQ_TRY(launch_check("gemm_decode_kernel"));
+  if (decode_four_waves()) {
+    gemm_decode_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps, epi,
+                                                       partial);
+    FQ_TRY(launch_check("gemm_decode_kernel"));
+  } else {
+    gemm_decode8_kernel<MB><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps,
+                                                        epi, partial);
+    FQ_TRY(launch_check("gemm_decode8_kernel"));
+  }
   if (splits > 1) {
     splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
     FQ_TRY(launch_check("splitk_reduce_kernel"));

@@ -63,6 +63,17 @@ def test_gemm_packed_shapes(M, N, K):
     _tol_check(got, ref, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("M", [64, 100, 144, 256])
+def test_gemm_decode_kernels(M, waves, monkeypatch):
+    """The two 4-bit decode kernels (4 waves x 64 weight rows, 8 waves x 32;
+    the library reads FQ_DECODE_WAVES at each call) over ragged N, split K."""
+    if waves == "4":
+        monkeypatch.setenv("FQ_DECODE_WAVES", "4")
+    got, ref = _run(M, 1000, 2048, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, seed=M)
+    _tol_check(got, ref, f"decode kernel waves={waves} M={M}")
+
+
 @pytest.mark.parametrize("flags,qcols", [
     (fq.FQ_EPI_BIAS | fq.FQ_EPI_QSCALE, 96),
     (fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU, 0),
