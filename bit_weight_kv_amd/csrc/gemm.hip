@@ -127,16 +127,18 @@ __device__ inline void epilogue_store8(const Epilogue& e, int64_t m, int64_t n, 
 }
 
 // 8 codes (one 32-bit word, element 2k in the low nibble of byte k) -> 8 fp16
-// values fp16(mn + c*s) in natural order, as 4 packed pairs.
+// values fp16(mn + c*s) in natural order, as 4 packed pairs.  Pair j comes
+// from byte j alone: the byte duplicated into halves 0 and 1 (a byte
+// permute), then one AND-OR keeps the low nibble under exponent 0x64 (1024 + c,
+// ulp 1) and the high nibble, still at bits 4..7, under exponent 0x54
+// (64 + c: at that exponent bit 4 is worth 1); an exact fp16 subtract of
+// {1024, 64} leaves the two codes, and one packed fp16 FMA rounds c*s + mn once.
 __device__ inline void dequant8(uint32_t w, half2_t mn2, half2_t s2, uint32_t out[4]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: c0 c2 c4 c6
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: c1 c3 c5 c7
-  const half2_t bias = {(half_t)-1024.0f, (half_t)-1024.0f};
+  const half2_t bias = {(half_t)-1024.0f, (half_t)-64.0f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    // bytes [lo.b_j, 0, hi.b_j, 0] then exponent 0x64: halves (1024 + c_2j, 1024 + c_2j+1)
-    const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + j) << 16 | (uint32_t)j;
-    const uint32_t p = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    const uint32_t sel = 0x0C000C00u | (uint32_t)j << 16 | (uint32_t)j;  // bytes {b_j, 0, b_j, 0}
+    const uint32_t p = (__builtin_amdgcn_perm(w, w, sel) & 0x00F0000Fu) | 0x54006400u;
     const half2_t c = __builtin_bit_cast(half2_t, p) + bias;  // exact: small integers
     out[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
   }
@@ -612,11 +614,11 @@ __device__ inline void mfma16x16x32_acc_ordered(float4_t& acc, const half8_t& a,
 // interleaved between them: a wave's VALU work overlaps its own MFMAs only
 // when the two are interleaved finely (measured: 8 MFMAs + 16 independent
 // VALU ops cost 162 cycles interleaved, 213 back to back, 147 for the MFMAs
-// alone).  The VALU part is dequant8 instruction for instruction: nibbles to
-// bytes (and, shift, and), byte permutes into {c, 0x00} pairs, exponent OR
-// (1024 + c), exact fp16 subtract of 1024, one packed fp16 FMA c*s + min with
-// {min, scale} taken from the halves of `ms`.  Its outputs are consumed by
-// later MFMAs only, never inside this block.
+// alone).  The VALU part is dequant8 instruction for instruction: per pair a
+// byte permute and an AND-OR with the two exponents, the exact fp16 subtract
+// of {1024, 64}, one packed fp16 FMA c*s + min with {min, scale} taken from
+// the halves of `ms` -- 16 instructions per 8 weights.  Its outputs are
+// consumed by later MFMAs only, never inside this block.
 // General form: MFMA k computes c_k += a_k * b_k.
 __device__ inline void mfma4_rebuild_ab(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a0,
                                         const half8_t& a1, const half8_t& a2, const half8_t& a3, const half8_t& b0,
@@ -625,34 +627,32 @@ __device__ inline void mfma4_rebuild_ab(float4_t& c0, float4_t& c1, float4_t& c2
   // separate volatile statements keep their order; one accumulator per MFMA
   // statement keeps every accumulator in place (a statement binding several
   // makes the register allocator copy them around)
-  uint32_t o0, o1, o2, o3, lo, hi;
+  uint32_t o0, o1, o2, o3;
+  const uint32_t keep = 0x00F0000Fu;  // VGPR operand: one scalar operand per VOP3 instruction
   mfma16x16x32_acc_ordered(c0, a0, b0);
   asm volatile(
-      "v_and_b32 %0, 0x0f0f0f0f, %4\n\t"
-      "v_lshrrev_b32 %1, 4, %4\n\t"
-      "v_and_b32 %1, 0x0f0f0f0f, %1\n\t"
-      "v_perm_b32 %2, %1, %0, %5\n\t"
-      "v_perm_b32 %3, %1, %0, %6"
-      : "=&v"(lo), "=&v"(hi), "=&v"(o0), "=&v"(o1)
-      : "v"(w), "s"(0x0C040C00u), "s"(0x0C050C01u));
+      "v_perm_b32 %0, %2, %2, %4\n\t"
+      "v_perm_b32 %1, %2, %2, %5\n\t"
+      "v_and_or_b32 %0, %0, %3, %6\n\t"
+      "v_and_or_b32 %1, %1, %3, %6"
+      : "=&v"(o0), "=&v"(o1)
+      : "v"(w), "v"(keep), "s"(0x0C000C00u), "s"(0x0C010C01u), "s"(0x54006400u));
   mfma16x16x32_acc_ordered(c1, a1, b1);
   asm volatile(
-      "v_perm_b32 %0, %5, %4, %6\n\t"
-      "v_perm_b32 %1, %5, %4, %7\n\t"
-      "v_or_b32 %2, 0x64006400, %2\n\t"
-      "v_or_b32 %3, 0x64006400, %3\n\t"
-      "v_or_b32 %0, 0x64006400, %0"
-      : "=&v"(o2), "=&v"(o3), "+v"(o0), "+v"(o1)
-      : "v"(lo), "v"(hi), "s"(0x0C060C02u), "s"(0x0C070C03u));
+      "v_perm_b32 %0, %2, %2, %4\n\t"
+      "v_perm_b32 %1, %2, %2, %5\n\t"
+      "v_and_or_b32 %0, %0, %3, %6\n\t"
+      "v_and_or_b32 %1, %1, %3, %6"
+      : "=&v"(o2), "=&v"(o3)
+      : "v"(w), "v"(keep), "s"(0x0C020C02u), "s"(0x0C030C03u), "s"(0x54006400u));
   mfma16x16x32_acc_ordered(c2, a2, b2);
   asm volatile(
-      "v_or_b32 %3, 0x64006400, %3\n\t"
       "v_pk_add_f16 %0, %0, %4\n\t"
       "v_pk_add_f16 %1, %1, %4\n\t"
       "v_pk_add_f16 %2, %2, %4\n\t"
       "v_pk_add_f16 %3, %3, %4"
       : "+v"(o0), "+v"(o1), "+v"(o2), "+v"(o3)
-      : "s"(0xE400E400u));
+      : "s"(0xD400E400u));
   mfma16x16x32_acc_ordered(c3, a3, b3);
   asm volatile(
       "v_pk_fma_f16 %0, %0, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
