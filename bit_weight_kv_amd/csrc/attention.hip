@@ -15,8 +15,10 @@
 //   2. softmax with block max / sum reductions (exp2 of log2(e)-scaled scores);
 //   3. values: 16 lanes cover one position's codes (4 bytes = 8 channels per
 //      lane), 16 positions are in flight per block; each lane accumulates
-//      sum_j (p_j s_jg) c_ji and sum_j p_j min_jg, then the 16 partial sums
-//      are reduced through LDS.
+//      sum_j (p_j s_jg) c_ji -- two positions at a time, as fp32 dot products
+//      of exact fp16 code pairs with the fp16 pair {p_1 s_1, p_2 s_2} -- and
+//      sum_j p_j min_jg in fp32, then the 16 partial sums are reduced through
+//      LDS.
 //
 // The fp16 cache (cache compression off, weights possibly still compressed)
 // goes through the same kernels instantiated with F16 = true: keys and values
@@ -50,16 +52,29 @@ __device__ inline float block_sum256(float v, float* red) {
 }
 
 // Codes of 8 consecutive channels (one word) as exact fp16 integers, 4 pairs
-// in natural channel order.
+// in natural channel order: byte j duplicated into both halves, the low nibble
+// kept under exponent 0x64 (1024 + c) and the high nibble, at bits 4..7, under
+// exponent 0x54 (64 + c), then an exact subtract of {1024, 64}.
 __device__ inline void codes8_f16(uint32_t w, half2_t out[4]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const half2_t bias = {(half_t)-1024.0f, (half_t)-1024.0f};
+  const half2_t bias = {(half_t)-1024.0f, (half_t)-64.0f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + j) << 16 | (uint32_t)j;
-    const uint32_t p = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    const uint32_t sel = 0x0C000C00u | (uint32_t)j << 16 | (uint32_t)j;
+    const uint32_t p = (__builtin_amdgcn_perm(w, w, sel) & 0x00F0000Fu) | 0x54006400u;
     out[j] = __builtin_bit_cast(half2_t, p) + bias;
+  }
+}
+
+// Channel k of two positions as an exact fp16 pair {c1_k, c2_k}, for the 8
+// channels of code words w1 and w2 (even channels: low nibbles under
+// exponent 0x64; odd: high nibbles under 0x54).
+__device__ inline void codes8_pairs(uint32_t w1, uint32_t w2, half2_t out[8]) {
+  const half2_t lo_bias = {(half_t)-1024.0f, (half_t)-1024.0f}, hi_bias = {(half_t)-64.0f, (half_t)-64.0f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t t = __builtin_amdgcn_perm(w2, w1, 0x0C000C00u | (uint32_t)(4 + q) << 16 | (uint32_t)q);
+    out[2 * q] = __builtin_bit_cast(half2_t, (t & 0x000F000Fu) | 0x64006400u) + lo_bias;
+    out[2 * q + 1] = __builtin_bit_cast(half2_t, (t & 0x00F000F0u) | 0x54005400u) + hi_bias;
   }
 }
 
@@ -201,14 +216,22 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   const int g = wl / 8;  // group of this lane's 8 channels
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float bsum = 0.f;
-  for (int j = slot; j < len; j += SLOTS) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[wl];
-    const uint32_t mb = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + g];
-    const float pj = p[j];
-    const float a = pj * h2f((uint16_t)(mb >> 16));
-    bsum += pj * h2f((uint16_t)(mb & 0xFFFF));
+  // two positions per iteration: sum_j (p_j s_j) c_jk as fp32 dot products of
+  // the fp16 pairs {c_1k, c_2k} and {p_1 s_1, p_2 s_2}
+  for (int j = slot; j < len; j += 2 * SLOTS) {
+    const int j2 = j + SLOTS;
+    const bool two = j2 < len;
+    const uint32_t w1 = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[wl];
+    const uint32_t mb1 = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + g];
+    const uint32_t w2 = two ? reinterpret_cast<const uint32_t*>(vc + (row0 + j2) * (D / 2))[wl] : 0u;
+    const uint32_t mb2 = two ? reinterpret_cast<const uint32_t*>(vm)[(row0 + j2) * G + g] : 0u;
+    const float p1 = p[j], p2 = two ? p[j2] : 0.f;
+    bsum += p1 * h2f((uint16_t)(mb1 & 0xFFFF)) + p2 * h2f((uint16_t)(mb2 & 0xFFFF));
+    const half2_t a2 = {(half_t)(p1 * h2f((uint16_t)(mb1 >> 16))), (half_t)(p2 * h2f((uint16_t)(mb2 >> 16)))};
+    half2_t c[8];
+    codes8_pairs(w1, w2, c);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += a * (float)((w >> (4 * k)) & 0xF);
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_fdot2(c[k], a2, acc[k], false);
   }
   float* part = smem + ((len + 3) & ~3);
 #pragma unroll
