@@ -93,16 +93,21 @@ def measured_traffic(kernel):
     since the counters were taken."""
     import hashlib
     import re
-    summary = {"gemm_prefill": ("profiles/gemm_prefill_opt175b_4bit_b144.md", "bit_weight_kv_amd/csrc/gemm.hip"),
-               "gemm_decode": ("profiles/gemm_decode_opt175b_4bit_b144.md", "bit_weight_kv_amd/csrc/gemm.hip"),
+    csrc = "bit_weight_kv_amd/csrc/"
+    gemm_src = [csrc + "gemm.hip", csrc + "quant_group.h", csrc + "common.h"]
+    summary = {"gemm_prefill": ("profiles/gemm_prefill_opt175b_4bit_b144.md", gemm_src),
+               "gemm_decode": ("profiles/gemm_decode_opt175b_4bit_b144.md", gemm_src),
                "decode_attention": ("profiles/decode_attention_opt175b_4bit_b144.md",
-                                    "bit_weight_kv_amd/csrc/attention.hip")}
+                                    [csrc + "attention.hip", csrc + "common.h"])}
     if kernel not in summary:
         return None
-    md, src = (os.path.join(ROOT, f) for f in summary[kernel])
+    md, srcs = summary[kernel]
     try:
-        text = open(md).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        text = open(os.path.join(ROOT, md)).read()
+        h = hashlib.sha256()
+        for f in srcs:  # the sources the kernel is built from, in this order
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        digest = h.hexdigest()
     except OSError:
         return None
     t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
