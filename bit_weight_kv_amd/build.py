@@ -23,6 +23,14 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-source additions.  attention.hip: MFMA results in ordinary VGPRs -- the
+# causal prefill kernel rescales and reads its accumulators with vector
+# instructions every key chunk, and with the default accumulator registers
+# every chunk moved them there and back (and the extra registers cost the
+# second wave per SIMD).  gemm.hip keeps its inline-asm MFMAs on the
+# accumulator registers.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
@@ -40,7 +48,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [hipcc()] + [f for f in FLAGS if f != "-shared"] + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc()] + [f for f in FLAGS if f != "-shared"] + SOURCE_FLAGS.get(src, []) + inc +
+               ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
