@@ -523,39 +523,53 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       }
     }
     // ---- online softmax per query (lane l16 of each query block) ----
+    // The exponent base m of a query moves only when its running maximum
+    // exceeds m by more than 8 (log2 units): p = 2^(s - m) <= 256 stays well
+    // inside fp16, the result is unchanged mathematically (the sum l uses the
+    // same base), and the rescale of O is skipped in most chunks (a
+    // wave-uniform branch).  Chunks wholly below the wave's first query and
+    // inside the keys need no mask.
+    const bool unmasked = k0 + KC - 1 <= pos + t0 && k0 + KC <= nkeys;
     half8_t pf[2][2];  // [query block][32-wide key slice], B operand of O^T
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int64_t qpos = pos + t0 + qb * 16 + l16;
+      const int qpos = (int)(pos + t0) + qb * 16 + l16;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t kpos = k0 + kb * 16 + 4 * g4 + r;
-          const float v = (kpos <= qpos && kpos < nkeys) ? sacc[kb][qb][r] * kL2e : -INFINITY;
+          float v = sacc[kb][qb][r] * kL2e;
+          if (!unmasked) {
+            const int kpos = (int)k0 + kb * 16 + 4 * g4 + r;
+            v = (kpos <= qpos && kpos < (int)nkeys) ? v : -INFINITY;
+          }
           sacc[kb][qb][r] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[qb], mx);
-      const float alpha = mnew == -INFINITY ? 1.f : exp2f(mrun[qb] - mnew);
+      if (__any(mx > mrun[qb] + 8.f)) {
+        const float mnew = mx > mrun[qb] + 8.f ? mx : mrun[qb];
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun[qb] - mnew);
+        lrun[qb] *= alpha;
+        mrun[qb] = mnew;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) oacc[i][qb] *= alpha;
+      }
+      const float mb = mrun[qb] == -INFINITY ? 0.f : mrun[qb];  // a row with no key yet: every p is 0
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = mnew == -INFINITY ? 0.f : exp2f(sacc[kb][qb][r] - mnew);
+          const float e = __builtin_amdgcn_exp2f(sacc[kb][qb][r] - mb);
           sacc[kb][qb][r] = e;
           sum += e;
         }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
-      lrun[qb] = lrun[qb] * alpha + sum;
-      mrun[qb] = mnew;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i) oacc[i][qb] *= alpha;
+      lrun[qb] += sum;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
