@@ -1565,9 +1565,10 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
 fq_status dispatch_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
                           hipStream_t st) {
   const int64_t mb = ceil_div(M, 16);
-  // the streaming decode kernel for 4-bit weights from 49 rows up (at least
-  // 8 MFMA groups per K step to carry the reconstructions) and even K steps
-  if (W->kind == FQ_WEIGHT_PACKED4 && (W->k / BK) % 2 == 0 && mb >= 4) {
+  // the streaming decode kernel for 4-bit weights and even K steps; below 49
+  // rows it runs with 4 row blocks (the rows past M are clamped reads, never
+  // stored): the weight stream, not the MFMAs, sets its time there
+  if (W->kind == FQ_WEIGHT_PACKED4 && (W->k / BK) % 2 == 0) {
     if (mb <= 4) return run_decode<4>(A, M, lda, W, epi, st);
     if (mb <= 6) return run_decode<6>(A, M, lda, W, epi, st);
     if (mb <= 8) return run_decode<8>(A, M, lda, W, epi, st);
