@@ -1623,12 +1623,12 @@ static bool wide8_fits(int64_t M, int64_t N, int64_t K, const fq_weight* W) {
          W->kind == FQ_WEIGHT_PACKED4;
 }
 
-// Test hook: FQ_GEMM_SMALL_TILES=1 in the environment routes every GEMM to the
-// 128x128 kernel (lets the tests compare the two large-M kernels).
-static const bool g_small_tiles_only = [] {
+// Test hook: FQ_GEMM_SMALL_TILES=1 in the environment at the time of the call
+// routes every GEMM to the 128x128 kernel (lets the tests compare the kernels).
+static bool small_tiles_only() {
   const char* e = getenv("FQ_GEMM_SMALL_TILES");
   return e && e[0] == '1';
-}();
+}
 
 
 extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
@@ -1660,9 +1660,10 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
   hipStream_t st = as_stream(stream);
   // Tile choice: enough tiles to fill 256 CUs, split-K when the grid is small.
   const int KT = (int)(K / 64);
+  const bool small_tiles = small_tiles_only();
   const int tk = timing_begin(st);
   fq_status r;
-  if (M <= 256 && !g_small_tiles_only) {
+  if (M <= 256 && !small_tiles) {
     r = dispatch_skinny(A, M, lda, W, epi, st);
   } else if (M <= 32) {
     const int64_t tiles = ceil_div(N, 64);
@@ -1672,12 +1673,12 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
     const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
-  } else if (wide8_fits(M, N, K, W) && !g_small_tiles_only) {
+  } else if (wide8_fits(M, N, K, W) && !small_tiles) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
     gemm_wide8_kernel<false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
                                                          KvAppend{});
     r = launch_check("gemm_wide8_kernel");
-  } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !g_small_tiles_only) {
+  } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !small_tiles) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 128)));
     if (W->kind == FQ_WEIGHT_PACKED4)
       gemm_big_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, nullptr, N, K, epi);
@@ -1719,7 +1720,7 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
                             : (kv->k_codes && kv->v_codes && kv->k_meta && kv->v_meta &&
                                (uintptr_t)kv->k_codes % 8 == 0 && (uintptr_t)kv->v_codes % 8 == 0 &&
                                (uintptr_t)kv->k_meta % 4 == 0 && (uintptr_t)kv->v_meta % 4 == 0);
-  const bool fused = M > 0 && wide8_fits(M, W->n, W->k, W) && !g_small_tiles_only && cache_ok &&
+  const bool fused = M > 0 && wide8_fits(M, W->n, W->k, W) && !small_tiles_only() && cache_ok &&
                      (!bias || (uintptr_t)bias % 16 == 0) && kv->group == FQ_GROUP;
   if (!fused) {
     // unfused: the projection into C, then the append kernel reads K and V back

@@ -148,6 +148,19 @@ def test_gemm_packed_256x128_kernel():
     _tol_check(got, ref, "packed 256x128")
 
 
+@pytest.mark.parametrize("packed", [True, False])
+def test_gemm_small_tile_kernel_against_large_tiles(packed, monkeypatch):
+    """The 128x128 kernel (forced by FQ_GEMM_SMALL_TILES, read at each call)
+    against the oracle on a shape the large-tile kernels take (256x256 for
+    packed weights, 256x128 for fp16), ragged in M."""
+    M, N, K = 4100, 4096, 1024
+    got_large, ref = _run(M, N, K, fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU, packed=packed, seed=11)
+    _tol_check(got_large, ref, f"large tiles packed={packed}")
+    monkeypatch.setenv("FQ_GEMM_SMALL_TILES", "1")
+    got_small, ref2 = _run(M, N, K, fq.FQ_EPI_BIAS | fq.FQ_EPI_RELU, packed=packed, seed=11)
+    _tol_check(got_small, ref2, f"128x128 tiles packed={packed}")
+
+
 def test_gemm_empty_m_is_noop():
     W = fq.weight_f16(torch.zeros((64, 64), dtype=torch.float16, device="cuda:0"))
     out = torch.full((1, 64), 7.0, dtype=torch.float16, device="cuda:0")
