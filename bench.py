@@ -364,7 +364,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the batch dimension would shard over "
-              f"GPUs with no exchange, which this build does not launch.", file=sys.stderr)
+              f"GPUs with no exchange, which this program does not launch.", file=sys.stderr)
         sys.exit(2)
     cfg = CONFIGS[args.config]
     if args.cpu_baseline_only:

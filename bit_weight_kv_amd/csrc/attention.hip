@@ -1,5 +1,5 @@
-// Attention over the KV cache: the decode kernel (K3, one new query
-// per sequence) and the causal prefill kernel (K5, T new queries).
+// Attention over the KV cache: the decode kernel (one new query
+// per sequence) and the causal prefill kernel (T new queries).
 //
 // Cache format (FlexGen README, "Extreme Compression": the attention cache is
 // stored in 4 bits): per sequence b, head h and position j, head_dim/2 bytes

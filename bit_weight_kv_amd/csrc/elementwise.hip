@@ -1,5 +1,5 @@
-// Small kernels around the projections: LayerNorm (K4), token + position
-// embedding and greedy argmax (K6), the seeded input generator, and the
+// Small kernels around the projections: LayerNorm, token + position
+// embedding and greedy argmax, the seeded input generator, and the
 // library's error state.
 #include <cmath>
 #include <cstdio>

@@ -1,4 +1,4 @@
-// Dequant-fused projection GEMM (K2) and its fp16-weight variant (K2f):
+// Dequant-fused projection GEMM and its fp16-weight variant:
 //   C[M, N] = epilogue(A[M, K] * W^T),  A fp16 row-major, W [N, K].
 //
 // The compressed weight is the 4-bit group format (groups of 64 along K, fp16

@@ -1,4 +1,4 @@
-// Group-wise 4-bit min/max quantisation (K1): weights at load time and the
+// Group-wise 4-bit min/max quantisation: weights at load time and the
 // K/V of new tokens on append; plus the debug reconstruction.
 //
 // Method: FlexGen README (giters.com mirror), key features, "Extreme

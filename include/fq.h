@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
   FQ_OK = 0,
   FQ_ERR_INVALID = -1,     /* bad argument or shape */
-  FQ_ERR_UNSUPPORTED = -2, /* valid request outside what this build implements */
+  FQ_ERR_UNSUPPORTED = -2, /* valid request outside what this library implements */
   FQ_ERR_OOM = -3,         /* device or pinned-host allocation failed */
   FQ_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } fq_status;
