@@ -97,6 +97,12 @@ def test_offloaded_cache_equals_resident(cache):
         assert st.kv_h2d_bytes == off * per_pos * h2d_pos and st.kv_d2h_bytes == off * per_pos * d2h_pos
     mcfg = ModelConfig(LayerConfig(H, NH, F, compress_cache=cache), L, V, P + G + 2)
     _compare(runs[0][1], runs[0][2], oracle.generate(ids, G, 5, mcfg), f"offloaded cache={cache}")
+    # prefill in chunks of 2 sequences (max_tokens = 2 prompts): one staging and
+    # one write-back per layer serve every chunk
+    _, r_out, r_lg, _ = _gpu_generate(L, B, P, G, seed=5, compress_cache=cache, max_tokens=2 * P)
+    _, o_out, o_lg, _ = _gpu_generate(L, B, P, G, seed=5, compress_cache=cache, max_tokens=2 * P,
+                                      cache_resident_layers=1)
+    assert np.array_equal(o_out, r_out) and np.array_equal(o_lg, r_lg)
 
 
 def test_generate_deterministic_and_batch_independent():

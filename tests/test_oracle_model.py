@@ -3,7 +3,8 @@
 quantisation group never spans two tokens), a zero-weight layer that reduces
 to its residual path in closed form, the fp16-cache variant against torch's
 causal attention, the 4-bit and fp16 caches agreeing where quantisation is
-lossless, and greedy-generation consistency."""
+lossless, closed forms of the embedding offsets and the LM head's
+orientation, and greedy-generation consistency."""
 import numpy as np
 
 import synth
@@ -117,6 +118,34 @@ def test_cache_toggle_agrees_on_grid_exact_keys_and_values():
             assert np.array_equal(c["v"][:, :, :6].reshape(2, 4, 6, 64)[0, 1, 3], p["b_qkv"][512 + 64:512 + 128])
     assert np.array_equal(outs[0]["y"].view(np.uint16), outs[1]["y"].view(np.uint16))
     assert np.array_equal(outs[0]["o"].view(np.uint16), outs[1]["o"].view(np.uint16))
+
+
+def test_embed_closed_form_offsets():
+    """Token row plus the position row at p + 2 (the OPT position offset), for
+    positions pos0..pos0+T-1: integer-valued tables make every sum exact."""
+    V, P, h = 10, 12, 64
+    emb = (np.arange(V)[:, None] * np.ones((1, h))).astype(np.float16)        # E[i] = i
+    pos = (16.0 * np.arange(P)[:, None] * np.ones((1, h))).astype(np.float16)  # Pos[j] = 16 j
+    ids = np.array([[3, 7, 0], [9, 1, 4]])
+    x = embed(ids, emb, pos, 4)
+    want = ids[..., None] + 16.0 * (np.arange(4, 7) + 2)[None, :, None]
+    assert np.array_equal(x.astype(np.float64), np.broadcast_to(want, (2, 3, h)))
+
+
+def test_lm_head_closed_form_orientation():
+    """A row of alternating +-1 has mean 0 and variance 1, so the final
+    LayerNorm (gamma 1, beta 0) gives +-1/sqrt(1 + 1e-5), which rounds to +-1 in
+    fp16; with unit-vector embedding rows the logits are those entries, and
+    rows of zeros give 0 -- the product is LN(x) E^T, not its transpose."""
+    h, V = 64, 80
+    x = np.where(np.arange(h) % 2 == 0, 1.0, -1.0).astype(np.float16)[None]
+    emb = np.zeros((V, h), np.float16)
+    emb[np.arange(h), np.arange(h)] = 1.0
+    emb[h + 3, 5] = 2.0
+    lg = lm_head_logits(x, np.ones(h, np.float16), np.zeros(h, np.float16), emb)
+    want = np.concatenate([x[0].astype(np.float64), np.zeros(V - h)])
+    want[h + 3] = 2.0 * x[0, 5]
+    assert lg.shape == (1, V) and np.array_equal(lg[0], want)
 
 
 def test_argmax_ties_lowest_index():
