@@ -134,3 +134,34 @@ def test_fused_append_full_size():
         rc, rm = oracle.quantize(x)
         assert np.array_equal(host(kc[b0 + b, hh, t]), rc[0])
         assert np.array_equal(bits16(host(km[b0 + b, hh, t])), bits16(rm[0]))
+
+
+def test_fused_append_empty_and_head_dim_64_fused_path():
+    """M = 0 (no sequences or no tokens) is a no-op that leaves the cache and C
+    untouched; head_dim 64 through the fused kernel (4 heads share a 256-wide
+    tile) equals the two-call form."""
+    H, d = 16, 64
+    h = H * d
+    view, keep = _cache("q4", 2, H, 8, d)
+    W = fq.weight_packed(torch.zeros((3 * h, h // 2), dtype=torch.uint8, device="cuda:0"),
+                         torch.zeros((3 * h, h // 64, 2), dtype=torch.float16, device="cuda:0"), 3 * h, h)
+    a = torch.zeros((0, h), dtype=torch.float16, device="cuda:0")
+    c = torch.full((1, 3 * h), 5.0, dtype=torch.float16, device="cuda:0")
+    fq.fq_qkv_gemm_append(a, W, None, 1.0, view, 0, 0, 4, 0, c)   # B = 0
+    fq.fq_qkv_gemm_append(a, W, None, 1.0, view, 0, 2, 0, 0, c)   # T = 0
+    torch.cuda.synchronize()
+    assert (c == 5.0).all() and not any(t.any() for t in keep)
+    test_fused_append_equals_two_calls(16, 64, 2, 2048, 4, 1, "q4")
+
+
+def test_decode_attention_length_limit_and_empty_batch():
+    """Lengths beyond the score buffer are refused on the host; B = 0 is a no-op."""
+    H, d = 2, 64
+    view, keep = _cache("q4", 1, H, 30001, d)
+    q = torch.zeros((1, H * d), dtype=torch.float16, device="cuda:0")
+    out = torch.full((1, H * d), 3.0, dtype=torch.float16, device="cuda:0")
+    with pytest.raises(fq.FqError):
+        fq.fq_decode_attention(q, view, 0, 1, 30001, out)
+    fq.fq_decode_attention(q, view, 0, 0, 5, out)
+    torch.cuda.synchronize()
+    assert (out == 3.0).all()
