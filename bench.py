@@ -178,11 +178,11 @@ def cpu_baseline(cfg, seed):
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        cores = min(16, os.cpu_count() or 1)
     h, H, F = cfg["hidden"], cfg["heads"], cfg["ffn"]
     lcfg = oracle.LayerConfig(h, H, F, compress_weight=cfg["compress_weight"],
                               compress_cache=cfg.get("compress_cache", True))
-    workers = os.cpu_count() or 1
+    workers = min(16, os.cpu_count() or 1)  # the host share of one GPU
     t0 = time.time()
 
     def gen(name, shape, sigma):
