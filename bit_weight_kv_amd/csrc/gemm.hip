@@ -24,6 +24,7 @@
 // passes through the epilogue; used when the M x N grid cannot fill 256 CUs.
 #include <cstdlib>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "quant_group.h"
@@ -964,6 +965,266 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
   }
 }
 
+// ---- large-M kernel, one wave per SIMD, weight operand rebuilt in registers --
+// 256 x 256 block tile, 4 waves in 2 x 2, each 128 x 128 (8 x 8 MFMA 16x16x32
+// tiles, 256 fp32 accumulators pinned to AGPRs), K step 64 (two MFMA k
+// slices, one quantisation group) per barrier.
+//   * A: four LDS stages of 256 rows x 128 bytes (chunk c of row r at slot
+//     c ^ (r & 7)); step kt+3's copies are issued during step kt.
+//   * codes: three slots of 256 rows x 32 code bytes + 256 {min, scale}
+//     pairs; step kt+3's copies are issued during step kt.
+//   * the weight operand never passes through LDS as fp16: each wave rebuilds
+//     its own (128 weight rows x the next step's 64 k, 16 code words per
+//     lane) in registers between its MFMAs.
+//   * one barrier per step; the wait before it leaves this step's copies in
+//     flight, so the next step's A stage is complete one step early and its
+//     first fragment is read before the barrier.
+// Per K step a wave reads 16 A fragments and 24 code words from LDS: a
+// quarter of the fragment traffic per flop of the 8-wave kernel, whose waves
+// also read the fp16 B tile.
+//
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): an
+// unrolled loop whatever the optimiser decides (an array indexed by the loop
+// variable stays in registers).
+template <typename F, int... Is>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <bool KVA>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int64_t lda, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ meta, int64_t N, int64_t K, Epilogue epi, KvAppend kva) {
+  constexpr int BMx = 256, BNx = 256, TM = 128, TN = 128, FM = 8, FN = 8, BKx = 64;
+  constexpr int ROWB = BKx * 2;                                   // 128 bytes per staged A row
+  constexpr int A_BYTES = BMx * ROWB;                             // 32 KiB
+  constexpr int C_CODES = BNx * 32, C_BYTES = C_CODES + BNx * 4;  // 9 KiB per code slot
+  constexpr int SC = 3;
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[A_BYTES], a_lds1[A_BYTES], a_lds2[A_BYTES],
+      a_lds3[A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t c_lds[SC * C_BYTES];
+  auto a_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? a_lds0 : S == 1 ? a_lds1 : S == 2 ? a_lds2 : a_lds3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int fr = lane & 15, fk = lane >> 4;
+
+  // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 4 M
+  // tiles x 8 N tiles
+  const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
+  const int64_t nblk = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  int64_t lid = bid;
+  {
+    const int64_t per_xcd = nblk / 8;
+    if (bid < per_xcd * 8) lid = (bid % 8) * per_xcd + bid / 8;
+  }
+  constexpr int GM = 4;
+  const int64_t group = lid / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t gsize = min((int64_t)GM, tiles_m - first_m);
+  const int64_t in_group = lid - group * GM * tiles_n;
+  const int64_t m0 = (first_m + in_group % gsize) * BMx, n0 = (in_group / gsize) * BNx;
+  const int KT = (int)(K / BKx);  // a multiple of 4
+
+  // A copies: instruction q (0..31) fills rows 8q..8q+7 (lane -> row
+  // 8q + lane / 8, slot lane & 7 holding chunk slot ^ (row & 7)); wave w
+  // issues q = w + 4t
+  const uint16_t* a_src[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int r = 8 * (wave + 4 * t) + (lane >> 3);
+    a_src[t] = A + min(m0 + r, M - 1) * lda + ((lane & 7) ^ (r & 7)) * 8;
+  }
+  auto issue_a = [&](auto s, int kt) {
+    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dma_lds16(a_src[t] + (int64_t)kt * BKx, dst + (wave + 4 * t) * 1024);
+  };
+  // codes: instruction p (0..7) fills rows 32p..32p+31 (lane -> row
+  // 32p + lane / 2, 16 bytes each); wave w issues p = w and w + 4.  Meta:
+  // wave w copies rows 64w..64w+63, 4 bytes per lane.
+  const uint8_t* c_src[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    c_src[t] = codes + min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) * (K / 2) + (lane & 1) * 16;
+  const uint16_t* m_src = meta + min(n0 + 64 * wave + lane, N - 1) * (K / 64) * 2;
+  const uint32_t c_base = (uint32_t)(uintptr_t)c_lds;
+  auto issue_codes = [&](int kt) {
+    const uint32_t dst = c_base + (kt % SC) * C_BYTES;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dma_lds16(c_src[t] + (int64_t)kt * 32, dst + 32 * (wave + 4 * t) * 32);
+    dma_lds4(m_src + (int64_t)kt * 2, dst + C_CODES + 64 * wave * 4);
+  };
+  // this lane's weight operand: column block j = weight row wn * TN + 16 j + fr,
+  // slice ks = k chunk 4 ks + fk of the step (one code word), {min, scale} per row
+  uint32_t cw[2][FN], cm[FN];
+  auto read_codes = [&](int kt) {
+    const uint8_t* slot = c_lds + (kt % SC) * C_BYTES;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * TN + j * 16 + fr;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) cw[ks][j] = *reinterpret_cast<const uint32_t*>(slot + row * 32 + (4 * ks + fk) * 4);
+      cm[j] = *reinterpret_cast<const uint32_t*>(slot + C_CODES + row * 4);
+    }
+  };
+  auto rebuild = [&](int ks, int j) {
+    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
+    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
+    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+    uint32_t o[4];
+    dequant8(cw[ks][j], mn2, s2, o);
+    return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+  auto a_frag = [&](const uint8_t* As_, int ks, int i) {
+    const int r = wm * TM + i * 16 + fr;
+    return *reinterpret_cast<const half8_t*>(As_ + r * ROWB + (((4 * ks + fk) ^ (r & 7)) * 16));
+  };
+
+  float4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  // prologue: codes and A of steps 0..2; operand of step 0 rebuilt
+  issue_codes(0);
+  issue_codes(1);
+  issue_codes(2);
+  issue_a(I0{}, 0);
+  issue_a(I1{}, 1);
+  issue_a(I2{}, 2);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  half8_t bA[2][FN], bB[2][FN];
+  read_codes(0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bA[ks][j] = rebuild(ks, j);
+  half8_t af = a_frag(a_lds0, 0, 0);
+
+  // step kt: A stage kt % 4 (S), operand in bA for even kt (P = 0), else bB;
+  // af holds this step's first A fragment.  Issues step kt+3's A and codes,
+  // one copy per row block;
+  // rebuilds step kt+1's operand into the other register set: rebuild r
+  // (slice r / 8, column block r % 8) rides on the MFMAs of row block
+  // slot r + 2 (slot = 8 ks + i), the last four two to a slot, so the code
+  // words read at the start of the step have 32 MFMAs to arrive.  The last
+  // row block reads the next step's first fragment (its stage is complete).
+  // The conditions are run-time branches around the copies and waits only.
+  // (each of the four calls is its own instantiation: a step body inlined
+  // twice keeps the accumulators out of registers)
+  auto step = [&](auto s, int kt) {
+    constexpr int S = decltype(s)::value;
+    constexpr int P = S & 1;
+    using S3 = std::integral_constant<int, (S + 3) % 4>;
+    using S1 = std::integral_constant<int, (S + 1) % 4>;
+    half8_t(&bcur)[2][FN] = P == 0 ? bA : bB;
+    half8_t(&bnxt)[2][FN] = P == 0 ? bB : bA;
+    const uint8_t* As_ = a_st(s);
+    read_codes(kt + 1);  // stale but harmless past the last step
+    const bool more = kt + 3 < KT;
+    static_for<2 * FM>([&](auto sc) {
+      constexpr int SL = decltype(sc)::value;
+      constexpr int ks = SL / FM, i = SL % FM;
+      // one of this step's 11 copies per row block, between the MFMAs
+      if constexpr (SL < 8) {
+        if (more) dma_lds16(a_src[SL] + (int64_t)(kt + 3) * BKx, (uint32_t)(uintptr_t)a_st(S3{}) + (wave + 4 * SL) * 1024);
+      } else if constexpr (SL < 10) {
+        if (more) dma_lds16(c_src[SL - 8] + (int64_t)(kt + 3) * 32, c_base + ((kt + 3) % SC) * C_BYTES + 32 * (wave + 4 * (SL - 8)) * 32);
+      } else if constexpr (SL == 10) {
+        if (more) dma_lds4(m_src + (int64_t)(kt + 3) * 2, c_base + ((kt + 3) % SC) * C_BYTES + C_CODES + 64 * wave * 4);
+      }
+      const half8_t an = SL + 1 < 2 * FM ? a_frag(As_, (SL + 1) / FM, (SL + 1) % FM) : a_frag(a_st(S1{}), 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SL < 2) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
+      } else if constexpr (SL < 14) {
+        constexpr int r = SL - 2;
+        half8_t nb;
+        mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
+                         bcur[ks][2], bcur[ks][3], cw[r / FN][r % FN], cm[r % FN], nb);
+        bnxt[r / FN][r % FN] = nb;
+#pragma unroll
+        for (int j = 4; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
+      } else {
+        constexpr int r0 = 12 + 2 * (SL - 14), r1 = r0 + 1;
+        half8_t nb0, nb1;
+        mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
+                         bcur[ks][2], bcur[ks][3], cw[r0 / FN][r0 % FN], cm[r0 % FN], nb0);
+        mfma4_rebuild_ab(acc[i][4], acc[i][5], acc[i][6], acc[i][7], af, af, af, af, bcur[ks][4], bcur[ks][5],
+                         bcur[ks][6], bcur[ks][7], cw[r1 / FN][r1 % FN], cm[r1 % FN], nb1);
+        bnxt[r0 / FN][r0 % FN] = nb0;
+        bnxt[r1 / FN][r1 % FN] = nb1;
+      }
+      af = an;
+    });
+    if (more)
+      asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the same LDS wait where the compiler sees it (already satisfied): it
+    // then knows the prefetched fragment has arrived and adds no wait before
+    // the next step's first MFMAs, which would also cover the code reads
+    // issued after the barrier
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+  };
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    step(I2{}, kt + 2);
+    step(I3{}, kt + 3);
+  }
+  // the last MFMAs' results are read by VALU instructions below: wait out
+  // the MFMA write -> VALU read latency the compiler cannot see
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  // epilogue staged through LDS, 16 rows x 128 columns per wave at a time
+  // (row stride 132 floats), waves 0-1 in A stage 0, waves 2-3 in stage 1
+  {
+    constexpr int SROW = 132;
+    float* stg = reinterpret_cast<float*>((wave >> 1) == 0 ? a_lds0 : a_lds1) + (wave & 1) * 16 * SROW;
+    const bool vec = epilogue_vec_ok(epi);
+    const int rr = lane >> 2, cs = (lane & 3) * 16;
+    static_for<FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(4 * (lane >> 4) + r) * SROW + j * 16 + (lane & 15)] = acc[i][j][r];
+      __syncthreads();
+      const int64_t m = m0 + wm * TM + i * 16 + rr;
+      for (int p = 0; p < 2; ++p) {
+        const int64_t nw = n0 + wn * TN + p * 64;  // one quantisation group of one head
+        if (KVA && nw >= kva.h && nw < N) {
+          if (m < M) kv_append_epilogue(epi, kva, stg + rr * SROW + p * 64 + cs, m, nw, cs);
+        } else if (m < M) {
+          for (int c = 0; c < 16; c += 8) {
+            const float4 lo = *reinterpret_cast<const float4*>(stg + rr * SROW + p * 64 + cs + c);
+            const float4 hi = *reinterpret_cast<const float4*>(stg + rr * SROW + p * 64 + cs + c + 4);
+            const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            epilogue_store8(epi, m, nw + cs + c, v, N, vec);
+          }
+        }
+      }
+      __syncthreads();
+    });
+  }
+}
+
 // ---- small-M ("decode") kernel ------------------------------------------------
 // For M <= 256 (one decode step of the whole batch) a block owns every row of
 // C and 256 weight rows; each of its 4 waves owns 64 weight rows and all
@@ -1616,9 +1877,9 @@ fq_status run_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W
 
 using namespace fq;
 
-// Shapes the 256 x 256 kernel takes: packed weights, K a multiple of 128 and
+// Shapes the 256 x 256 kernels take: packed weights, K a multiple of 128 and
 // enough tiles to fill the chip.
-static bool wide8_fits(int64_t M, int64_t N, int64_t K, const fq_weight* W) {
+static bool tile256_fits(int64_t M, int64_t N, int64_t K, const fq_weight* W) {
   return M >= 1024 && N >= 1024 && K % 128 == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 128 &&
          W->kind == FQ_WEIGHT_PACKED4;
 }
@@ -1628,6 +1889,16 @@ static bool wide8_fits(int64_t M, int64_t N, int64_t K, const fq_weight* W) {
 static bool small_tiles_only() {
   const char* e = getenv("FQ_GEMM_SMALL_TILES");
   return e && e[0] == '1';
+}
+
+// Among shapes the 256 x 256 tiles take: the one-wave-per-SIMD kernel where
+// its K loop applies (K a multiple of 256), else the 8-wave kernel.  Test
+// hook: FQ_GEMM_W4=0 in the environment at the time of the call selects the
+// 8-wave kernel for every K (the two accumulate in the same order, so their
+// outputs are identical).
+static bool use_w4(int64_t K) {
+  const char* e = getenv("FQ_GEMM_W4");
+  return K % 256 == 0 && !(e && e[0] == '0');
 }
 
 
@@ -1673,11 +1944,17 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
     const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
-  } else if (wide8_fits(M, N, K, W) && !small_tiles) {
+  } else if (tile256_fits(M, N, K, W) && !small_tiles) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-    gemm_wide8_kernel<false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
-                                                         KvAppend{});
-    r = launch_check("gemm_wide8_kernel");
+    if (use_w4(K)) {
+      gemm_w4_kernel<false><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
+                                                        KvAppend{});
+      r = launch_check("gemm_w4_kernel");
+    } else {
+      gemm_wide8_kernel<false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
+                                                           KvAppend{});
+      r = launch_check("gemm_wide8_kernel");
+    }
   } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !small_tiles) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 128)));
     if (W->kind == FQ_WEIGHT_PACKED4)
@@ -1720,7 +1997,7 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
                             : (kv->k_codes && kv->v_codes && kv->k_meta && kv->v_meta &&
                                (uintptr_t)kv->k_codes % 8 == 0 && (uintptr_t)kv->v_codes % 8 == 0 &&
                                (uintptr_t)kv->k_meta % 4 == 0 && (uintptr_t)kv->v_meta % 4 == 0);
-  const bool fused = M > 0 && wide8_fits(M, W->n, W->k, W) && !small_tiles_only() && cache_ok &&
+  const bool fused = M > 0 && tile256_fits(M, W->n, W->k, W) && !small_tiles_only() && cache_ok &&
                      (!bias || (uintptr_t)bias % 16 == 0) && kv->group == FQ_GROUP;
   if (!fused) {
     // unfused: the projection into C, then the append kernel reads K and V back
@@ -1740,8 +2017,13 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
   const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-  gemm_wide8_kernel<true><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
-  FQ_TRY(launch_check("gemm_wide8_kernel"));
+  if (use_w4(K)) {
+    gemm_w4_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
+    FQ_TRY(launch_check("gemm_w4_kernel"));
+  } else {
+    gemm_wide8_kernel<true><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
+    FQ_TRY(launch_check("gemm_wide8_kernel"));
+  }
   if (tk >= 0) {
     const double bytes = 2.0 * M * K + 0.5625 * N * K + 2.0 * M * h + (f16 ? 2.0 : 0.5625) * 2.0 * M * h + 2.0 * N;
     timing_end(tk, FQ_KC_GEMM_PREFILL, 2.0 * M * N * K, bytes, st);

@@ -141,6 +141,29 @@ def test_gemm_large_tile_vector_epilogue():
     _tol_check(got, ref, "vector epilogue qscale f32")
 
 
+@pytest.mark.parametrize("M,N,K,flags,f32", [
+    (2100, 3900, 512, "bias|residual|relu", False),
+    (2049, 4104, 256, "bias|qscale", True),
+    (4096, 8192, 1024, "bias", False),
+])
+def test_gemm_256_kernels_identical(M, N, K, flags, f32, monkeypatch):
+    """The two 256 x 256 kernels (one wave per SIMD with the weight operand
+    rebuilt in registers, and the 8-wave one staging it in LDS; FQ_GEMM_W4=0
+    selects the latter) add the same products in the same order: outputs equal
+    bit for bit, ragged in M and N, every epilogue, fp16 and fp32 output; and
+    both within the oracle bound."""
+    fl = 0
+    for f in flags.split("|"):
+        fl |= {"bias": fq.FQ_EPI_BIAS, "residual": fq.FQ_EPI_RESIDUAL, "relu": fq.FQ_EPI_RELU,
+               "qscale": fq.FQ_EPI_QSCALE}[f]
+    log(f"gemm 256 kernels M={M} N={N} K={K} {flags} f32={f32}")
+    got_w4, ref = _run(M, N, K, fl, seed=13, qcols=1000, f32out=f32)
+    monkeypatch.setenv("FQ_GEMM_W4", "0")
+    got_w8, _ = _run(M, N, K, fl, seed=13, qcols=1000, f32out=f32)
+    assert np.array_equal(got_w4.view(np.uint32 if f32 else np.uint16), got_w8.view(np.uint32 if f32 else np.uint16))
+    _tol_check(got_w4, ref, "256x256 kernels")
+
+
 def test_gemm_packed_256x128_kernel():
     """4-bit weights with K not a multiple of 128 take the 256 x 128 kernel."""
     log("gemm packed 256x128 K=192")

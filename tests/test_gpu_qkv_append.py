@@ -25,7 +25,7 @@ def _cache(fmt, batch, H, cap, d):
     return fq.kv_layer_view_f16(*t), t
 
 
-# (H, d, B, T, pos, b0, fmt): the first three take the fused 256 x 256 kernel
+# (H, d, B, T, pos, b0, fmt): the first three take a fused 256 x 256 kernel
 # (ragged M = 2100 in the second), the last one the two-call fallback (small M).
 CASES = [(8, 128, 4, 1024, 0, 0, "q4"), (12, 128, 3, 700, 5, 1, "q4"), (16, 64, 4, 1024, 3, 0, "f16"),
          (4, 64, 2, 5, 2, 1, "q4")]
@@ -33,6 +33,17 @@ CASES = [(8, 128, 4, 1024, 0, 0, "q4"), (12, 128, 3, 700, 5, 1, "q4"), (16, 64, 
 
 @pytest.mark.parametrize("H,d,B,T,pos,b0,fmt", CASES)
 def test_fused_append_equals_two_calls(H, d, B, T, pos, b0, fmt):
+    _fused_vs_two_calls(H, d, B, T, pos, b0, fmt)
+
+
+@pytest.mark.parametrize("H,d,B,T,pos,b0,fmt", CASES[:3])
+def test_fused_append_equals_two_calls_8wave_kernel(H, d, B, T, pos, b0, fmt, monkeypatch):
+    """The same through the 8-wave 256 x 256 kernel (FQ_GEMM_W4=0)."""
+    monkeypatch.setenv("FQ_GEMM_W4", "0")
+    _fused_vs_two_calls(H, d, B, T, pos, b0, fmt)
+
+
+def _fused_vs_two_calls(H, d, B, T, pos, b0, fmt):
     h = H * d
     M, K, N = B * T, h, 3 * h
     log(f"qkv append H={H} d={d} B={B} T={T} pos={pos} b0={b0} {fmt} (M={M})")
@@ -151,7 +162,7 @@ def test_fused_append_empty_and_head_dim_64_fused_path():
     fq.fq_qkv_gemm_append(a, W, None, 1.0, view, 0, 2, 0, 0, c)   # T = 0
     torch.cuda.synchronize()
     assert (c == 5.0).all() and not any(t.any() for t in keep)
-    test_fused_append_equals_two_calls(16, 64, 2, 2048, 4, 1, "q4")
+    _fused_vs_two_calls(16, 64, 2, 2048, 4, 1, "q4")
 
 
 def test_decode_attention_length_limit_and_empty_batch():
