@@ -966,22 +966,26 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
 }
 
 // ---- large-M kernel, one wave per SIMD, weight operand rebuilt in registers --
-// 256 x 256 block tile, 4 waves in 2 x 2, each 128 x 128 (8 x 8 MFMA 16x16x32
-// tiles, 256 fp32 accumulators pinned to AGPRs), K step 64 (two MFMA k
-// slices, one quantisation group) per barrier.
+// 256 x 256 block tile, 4 waves side by side in N, each 256 x 64 (16 x 4 MFMA
+// 16x16x32 tiles, 256 fp32 accumulators pinned to AGPRs), K step 64 (two
+// MFMA k slices, one quantisation group) per barrier.
 //   * A: four LDS stages of 256 rows x 128 bytes (chunk c of row r at slot
-//     c ^ (r & 7)); step kt+3's copies are issued during step kt.
+//     c ^ (r & 7)); step kt+3's copies are issued during step kt, one copy
+//     instruction per row block of MFMAs.
 //   * codes: three slots of 256 rows x 32 code bytes + 256 {min, scale}
 //     pairs; step kt+3's copies are issued during step kt.
 //   * the weight operand never passes through LDS as fp16: each wave rebuilds
-//     its own (128 weight rows x the next step's 64 k, 16 code words per
-//     lane) in registers between its MFMAs.
+//     its own 64 weight rows x the next step's 64 k (8 code words per lane)
+//     in registers, one rebuild carried by every 16 MFMAs; no two waves
+//     rebuild the same weights.
+//   * each wave reads every A fragment of the stage (32 per step), three
+//     ahead of its MFMAs.
 //   * one barrier per step; the wait before it leaves this step's copies in
 //     flight, so the next step's A stage is complete one step early and its
-//     first fragment is read before the barrier.
-// Per K step a wave reads 16 A fragments and 24 code words from LDS: a
-// quarter of the fragment traffic per flop of the 8-wave kernel, whose waves
-// also read the fp16 B tile.
+//     first fragments are read before the barrier.
+// Against the 8-wave kernel: the same order of additions (identical
+// outputs), no fp16 B tile in LDS, and half the reconstruction work per
+// flop of a 2 x 2 arrangement of the same waves.
 //
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): an
 // unrolled loop whatever the optimiser decides (an array indexed by the loop
@@ -999,7 +1003,7 @@ template <bool KVA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t lda, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ meta, int64_t N, int64_t K, Epilogue epi, KvAppend kva) {
-  constexpr int BMx = 256, BNx = 256, TM = 128, TN = 128, FM = 8, FN = 8, BKx = 64;
+  constexpr int BMx = 256, BNx = 256, TN = 64, FM = 16, FN = 4, BKx = 64;
   constexpr int ROWB = BKx * 2;                                   // 128 bytes per staged A row
   constexpr int A_BYTES = BMx * ROWB;                             // 32 KiB
   constexpr int C_CODES = BNx * 32, C_BYTES = C_CODES + BNx * 4;  // 9 KiB per code slot
@@ -1017,7 +1021,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wn = wave;
   const int fr = lane & 15, fk = lane >> 4;
 
   // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 4 M
@@ -1067,7 +1071,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int t = 0; t < 2; ++t) dma_lds16(c_src[t] + (int64_t)kt * 32, dst + 32 * (wave + 4 * t) * 32);
     dma_lds4(m_src + (int64_t)kt * 2, dst + C_CODES + 64 * wave * 4);
   };
-  // this lane's weight operand: column block j = weight row wn * TN + 16 j + fr,
+  // this lane's weight operand: column block j = weight row 64 wn + 16 j + fr,
   // slice ks = k chunk 4 ks + fk of the step (one code word), {min, scale} per row
   uint32_t cw[2][FN], cm[FN];
   auto read_codes = [&](int kt) {
@@ -1089,7 +1093,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
   };
   auto a_frag = [&](const uint8_t* As_, int ks, int i) {
-    const int r = wm * TM + i * 16 + fr;
+    const int r = i * 16 + fr;
     return *reinterpret_cast<const half8_t*>(As_ + r * ROWB + (((4 * ks + fk) ^ (r & 7)) * 16));
   };
 
@@ -1113,19 +1117,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int j = 0; j < FN; ++j) bA[ks][j] = rebuild(ks, j);
-  half8_t af = a_frag(a_lds0, 0, 0);
+  // A fragments three slots ahead (slot = 16 ks + i) in a ring of 4: the
+  // ring's size divides the 32 slots of a step, so slot s of every step
+  // uses entry s % 4
+  half8_t fa[4];
+  fa[0] = a_frag(a_lds0, 0, 0);
+  fa[1] = a_frag(a_lds0, 0, 1);
+  fa[2] = a_frag(a_lds0, 0, 2);
 
-  // step kt: A stage kt % 4 (S), operand in bA for even kt (P = 0), else bB;
-  // af holds this step's first A fragment.  Issues step kt+3's A and codes,
-  // one copy per row block;
-  // rebuilds step kt+1's operand into the other register set: rebuild r
-  // (slice r / 8, column block r % 8) rides on the MFMAs of row block
-  // slot r + 2 (slot = 8 ks + i), the last four two to a slot, so the code
-  // words read at the start of the step have 32 MFMAs to arrive.  The last
-  // row block reads the next step's first fragment (its stage is complete).
-  // The conditions are run-time branches around the copies and waits only.
-  // (each of the four calls is its own instantiation: a step body inlined
-  // twice keeps the accumulators out of registers)
+  // step kt: A stage kt % 4 (S), operand in bA for even kt (P = 0), else bB.
+  // Reads step kt+1's code words (their copies completed at the last
+  // barrier), issues step kt+3's copies over the first 11 row-block slots
+  // (slot = 16 ks + i), and rebuilds step kt+1's operand into the other
+  // register set: rebuild r (slice r / 4, column block r % 4) rides on the 4
+  // MFMAs of slot 4 + 3 r, so the code words have 4 slots to arrive.  The
+  // last three slots read the next step's first three fragments (that stage
+  // is complete).  The conditions are run-time branches around the copies
+  // and waits only.  (each of the four calls is its own instantiation: a
+  // step body inlined twice keeps the accumulators out of registers)
   auto step = [&](auto s, int kt) {
     constexpr int S = decltype(s)::value;
     constexpr int P = S & 1;
@@ -1139,7 +1148,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_for<2 * FM>([&](auto sc) {
       constexpr int SL = decltype(sc)::value;
       constexpr int ks = SL / FM, i = SL % FM;
-      // one of this step's 11 copies per row block, between the MFMAs
       if constexpr (SL < 8) {
         if (more) dma_lds16(a_src[SL] + (int64_t)(kt + 3) * BKx, (uint32_t)(uintptr_t)a_st(S3{}) + (wave + 4 * SL) * 1024);
       } else if constexpr (SL < 10) {
@@ -1147,39 +1155,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       } else if constexpr (SL == 10) {
         if (more) dma_lds4(m_src + (int64_t)(kt + 3) * 2, c_base + ((kt + 3) % SC) * C_BYTES + C_CODES + 64 * wave * 4);
       }
-      const half8_t an = SL + 1 < 2 * FM ? a_frag(As_, (SL + 1) / FM, (SL + 1) % FM) : a_frag(a_st(S1{}), 0, 0);
+      constexpr int NX = SL + 3;
+      fa[NX % 4] = NX < 2 * FM ? a_frag(As_, NX / FM, NX % FM) : a_frag(a_st(S1{}), 0, NX - 2 * FM);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SL < 2) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
-      } else if constexpr (SL < 14) {
-        constexpr int r = SL - 2;
+      const half8_t& af = fa[SL % 4];
+      if constexpr (SL >= 4 && (SL - 4) % 3 == 0 && (SL - 4) / 3 < 2 * FN) {
+        constexpr int r = (SL - 4) / 3;
         half8_t nb;
         mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
                          bcur[ks][2], bcur[ks][3], cw[r / FN][r % FN], cm[r % FN], nb);
         bnxt[r / FN][r % FN] = nb;
-#pragma unroll
-        for (int j = 4; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
       } else {
-        constexpr int r0 = 12 + 2 * (SL - 14), r1 = r0 + 1;
-        half8_t nb0, nb1;
-        mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
-                         bcur[ks][2], bcur[ks][3], cw[r0 / FN][r0 % FN], cm[r0 % FN], nb0);
-        mfma4_rebuild_ab(acc[i][4], acc[i][5], acc[i][6], acc[i][7], af, af, af, af, bcur[ks][4], bcur[ks][5],
-                         bcur[ks][6], bcur[ks][7], cw[r1 / FN][r1 % FN], cm[r1 % FN], nb1);
-        bnxt[r0 / FN][r0 % FN] = nb0;
-        bnxt[r1 / FN][r1 % FN] = nb1;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
       }
-      af = an;
     });
     if (more)
       asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // the same LDS wait where the compiler sees it (already satisfied): it
-    // then knows the prefetched fragment has arrived and adds no wait before
-    // the next step's first MFMAs, which would also cover the code reads
-    // issued after the barrier
+    // then knows the prefetched fragments have arrived and adds no wait
+    // before the next step's first MFMAs, which would also cover the code
+    // reads issued after the barrier
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
   };
   for (int kt = 0; kt < KT; kt += 4) {
@@ -1192,11 +1190,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // the MFMA write -> VALU read latency the compiler cannot see
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  // epilogue staged through LDS, 16 rows x 128 columns per wave at a time
-  // (row stride 132 floats), waves 0-1 in A stage 0, waves 2-3 in stage 1
+  // epilogue staged through LDS, 16 rows x 64 columns per wave at a time
+  // (row stride 68 floats), wave w in half (w & 1) of A stage w / 2
   {
-    constexpr int SROW = 132;
-    float* stg = reinterpret_cast<float*>((wave >> 1) == 0 ? a_lds0 : a_lds1) + (wave & 1) * 16 * SROW;
+    constexpr int SROW = 68;
+    float* stg = reinterpret_cast<float*>(((wave >> 1) == 0 ? a_lds0 : a_lds1) + (wave & 1) * 8192);
     const bool vec = epilogue_vec_ok(epi);
     const int rr = lane >> 2, cs = (lane & 3) * 16;
     static_for<FM>([&](auto ic) {
@@ -1206,18 +1204,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int r = 0; r < 4; ++r) stg[(4 * (lane >> 4) + r) * SROW + j * 16 + (lane & 15)] = acc[i][j][r];
       __syncthreads();
-      const int64_t m = m0 + wm * TM + i * 16 + rr;
-      for (int p = 0; p < 2; ++p) {
-        const int64_t nw = n0 + wn * TN + p * 64;  // one quantisation group of one head
-        if (KVA && nw >= kva.h && nw < N) {
-          if (m < M) kv_append_epilogue(epi, kva, stg + rr * SROW + p * 64 + cs, m, nw, cs);
-        } else if (m < M) {
-          for (int c = 0; c < 16; c += 8) {
-            const float4 lo = *reinterpret_cast<const float4*>(stg + rr * SROW + p * 64 + cs + c);
-            const float4 hi = *reinterpret_cast<const float4*>(stg + rr * SROW + p * 64 + cs + c + 4);
-            const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            epilogue_store8(epi, m, nw + cs + c, v, N, vec);
-          }
+      const int64_t m = m0 + i * 16 + rr;
+      const int64_t nw = n0 + wn * TN;  // this wave's 64 columns: one quantisation group of one head
+      if (KVA && nw >= kva.h && nw < N) {
+        if (m < M) kv_append_epilogue(epi, kva, stg + rr * SROW + cs, m, nw, cs);
+      } else if (m < M) {
+        for (int c = 0; c < 16; c += 8) {
+          const float4 lo = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c);
+          const float4 hi = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c + 4);
+          const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          epilogue_store8(epi, m, nw + cs + c, v, N, vec);
         }
       }
       __syncthreads();
