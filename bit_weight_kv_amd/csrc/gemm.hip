@@ -597,6 +597,17 @@ __device__ inline void dma_lds4(const void* g, uint32_t lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
+// The same copies addressed as a wave-uniform 64-bit base (SGPRs) plus a
+// 32-bit per-lane byte offset: half the per-lane address bytes, and a base
+// that advances with scalar adds only.
+__device__ inline void dma_lds16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ inline void dma_lds4_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
 // acc += a * b (16x16x32 fp16 MFMA) with the accumulator pinned to AGPRs.
 // Through the builtin, a wave holding 256 accumulators gets part of them
 // assigned to VGPRs and copied around every MFMA.  Consumers of acc after the
@@ -1042,34 +1053,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t m0 = (first_m + in_group % gsize) * BMx, n0 = (in_group / gsize) * BNx;
   const int KT = (int)(K / BKx);  // a multiple of 4
 
-  // A copies: instruction q (0..31) fills rows 8q..8q+7 (lane -> row
-  // 8q + lane / 8, slot lane & 7 holding chunk slot ^ (row & 7)); wave w
-  // issues q = w + 4t
-  const uint16_t* a_src[8];
+  // Copies, as a wave-uniform base (the block's first row and the step) plus
+  // a fixed 32-bit byte offset per lane.  The wave index is read into a
+  // scalar register once, so every LDS destination is scalar too.
+  //   A: instruction q (0..31) fills rows 8q..8q+7 (lane -> row 8q + lane / 8,
+  //   slot lane & 7 holding chunk slot ^ (row & 7)); wave w issues q = w + 4t.
+  //   codes: instruction p (0..7) fills rows 32p..32p+31 (lane -> row
+  //   32p + lane / 2, 16 bytes each); wave w issues p = w and w + 4.
+  //   meta: wave w copies rows 64w..64w+63, 4 bytes per lane.
+  // Rows beyond M or N are clamped to the last one: read, never stored.
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+  const uint8_t* c_blk = codes + n0 * (K / 2);
+  const uint8_t* m_blk = reinterpret_cast<const uint8_t*>(meta + n0 * (K / 64) * 2);
+  uint32_t a_off[8], c_off[2];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int r = 8 * (wave + 4 * t) + (lane >> 3);
-    a_src[t] = A + min(m0 + r, M - 1) * lda + ((lane & 7) ^ (r & 7)) * 8;
+    a_off[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * lda * 2 + ((lane & 7) ^ (r & 7)) * 16);
   }
-  auto issue_a = [&](auto s, int kt) {
-    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) dma_lds16(a_src[t] + (int64_t)kt * BKx, dst + (wave + 4 * t) * 1024);
-  };
-  // codes: instruction p (0..7) fills rows 32p..32p+31 (lane -> row
-  // 32p + lane / 2, 16 bytes each); wave w issues p = w and w + 4.  Meta:
-  // wave w copies rows 64w..64w+63, 4 bytes per lane.
-  const uint8_t* c_src[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    c_src[t] = codes + min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) * (K / 2) + (lane & 1) * 16;
-  const uint16_t* m_src = meta + min(n0 + 64 * wave + lane, N - 1) * (K / 64) * 2;
+    c_off[t] = (uint32_t)((min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) - n0) * (K / 2) + (lane & 1) * 16);
+  const uint32_t m_off = (uint32_t)((min(n0 + 64 * wave + lane, N - 1) - n0) * (K / 64) * 4);
   const uint32_t c_base = (uint32_t)(uintptr_t)c_lds;
+  auto issue_a = [&](auto s, int kt) {
+    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + swave * 1024;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, dst + t * 4096);
+  };
   auto issue_codes = [&](int kt) {
     const uint32_t dst = c_base + (kt % SC) * C_BYTES;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) dma_lds16(c_src[t] + (int64_t)kt * 32, dst + 32 * (wave + 4 * t) * 32);
-    dma_lds4(m_src + (int64_t)kt * 2, dst + C_CODES + 64 * wave * 4);
+    for (int t = 0; t < 2; ++t) dma_lds16_s(c_off[t], c_blk + (int64_t)kt * 32, dst + (swave + 4 * t) * 1024);
+    dma_lds4_s(m_off, m_blk + (int64_t)kt * 4, dst + C_CODES + swave * 256);
   };
   // this lane's weight operand: column block j = weight row 64 wn + 16 j + fr,
   // slice ks = k chunk 4 ks + fk of the step (one code word), {min, scale} per row
@@ -1128,13 +1145,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // step kt: A stage kt % 4 (S), operand in bA for even kt (P = 0), else bB.
   // Reads step kt+1's code words (their copies completed at the last
   // barrier), issues step kt+3's copies over the first 11 row-block slots
-  // (slot = 16 ks + i), and rebuilds step kt+1's operand into the other
-  // register set: rebuild r (slice r / 4, column block r % 4) rides on the 4
-  // MFMAs of slot 4 + 3 r, so the code words have 4 slots to arrive.  The
-  // last three slots read the next step's first three fragments (that stage
-  // is complete).  The conditions are run-time branches around the copies
-  // and waits only.  (each of the four calls is its own instantiation: a
-  // step body inlined twice keeps the accumulators out of registers)
+  // (slot = 16 ks + i; 11 per wave, so the wait before the barrier leaves
+  // exactly this step's copies in flight), and rebuilds step kt+1's operand
+  // into the other register set: rebuild r (slice r / 4, column block r % 4)
+  // rides on the 4 MFMAs of slot 4 + 3 r, so the code words have 4 slots to
+  // arrive.  The last three slots read the next step's first three
+  // fragments (that stage is complete).  (each of the four calls is its own
+  // instantiation: a step body inlined twice keeps the accumulators out of
+  // registers)
   auto step = [&](auto s, int kt) {
     constexpr int S = decltype(s)::value;
     constexpr int P = S & 1;
@@ -1144,16 +1162,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     half8_t(&bnxt)[2][FN] = P == 0 ? bB : bA;
     const uint8_t* As_ = a_st(s);
     read_codes(kt + 1);  // stale but harmless past the last step
-    const bool more = kt + 3 < KT;
+    // step kt+3's copies, clamped to the last step: past it they rewrite an
+    // A stage and a code slot that no later step reads (each was last read
+    // the step before), so the MFMA chain carries no branches
+    const int kc = min(kt + 3, KT - 1);
+    const uint8_t* a_step = a_blk + (int64_t)kc * 128;
+    const uint8_t* c_step = c_blk + (int64_t)kc * 32;
+    const uint8_t* m_step = m_blk + (int64_t)kc * 4;
+    const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
+    const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
     static_for<2 * FM>([&](auto sc) {
       constexpr int SL = decltype(sc)::value;
       constexpr int ks = SL / FM, i = SL % FM;
       if constexpr (SL < 8) {
-        if (more) dma_lds16(a_src[SL] + (int64_t)(kt + 3) * BKx, (uint32_t)(uintptr_t)a_st(S3{}) + (wave + 4 * SL) * 1024);
+        dma_lds16_s(a_off[SL], a_step, a_dst + SL * 4096);
       } else if constexpr (SL < 10) {
-        if (more) dma_lds16(c_src[SL - 8] + (int64_t)(kt + 3) * 32, c_base + ((kt + 3) % SC) * C_BYTES + 32 * (wave + 4 * (SL - 8)) * 32);
+        dma_lds16_s(c_off[SL - 8], c_step, c_dst + (swave + 4 * (SL - 8)) * 1024);
       } else if constexpr (SL == 10) {
-        if (more) dma_lds4(m_src + (int64_t)(kt + 3) * 2, c_base + ((kt + 3) % SC) * C_BYTES + C_CODES + 64 * wave * 4);
+        dma_lds4_s(m_off, m_step, c_dst + C_CODES + swave * 256);
       }
       constexpr int NX = SL + 3;
       fa[NX % 4] = NX < 2 * FM ? a_frag(As_, NX / FM, NX % FM) : a_frag(a_st(S1{}), 0, NX - 2 * FM);
@@ -1170,10 +1196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
       }
     });
-    if (more)
-      asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // the same LDS wait where the compiler sees it (already satisfied): it
     // then knows the prefetched fragments have arrived and adds no wait
     // before the next step's first MFMAs, which would also cover the code
@@ -1186,6 +1209,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     step(I2{}, kt + 2);
     step(I3{}, kt + 3);
   }
+  // the last steps' copies land in stages the epilogue reuses
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   // the last MFMAs' results are read by VALU instructions below: wait out
   // the MFMA write -> VALU read latency the compiler cannot see
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1888,13 +1913,15 @@ static bool small_tiles_only() {
 }
 
 // Among shapes the 256 x 256 tiles take: the one-wave-per-SIMD kernel where
-// its K loop applies (K a multiple of 256), else the 8-wave kernel.  Test
-// hook: FQ_GEMM_W4=0 in the environment at the time of the call selects the
-// 8-wave kernel for every K (the two accumulate in the same order, so their
-// outputs are identical).
-static bool use_w4(int64_t K) {
+// its K loop applies (K a multiple of 256) and its 32-bit per-lane copy
+// offsets cannot overflow (up to 255 rows of lda or K / 2 bytes past the
+// block's first row), else the 8-wave kernel.  Test hook: FQ_GEMM_W4=0 in
+// the environment at the time of the call selects the 8-wave kernel for
+// every shape (the two accumulate in the same order, so their outputs are
+// identical).
+static bool use_w4(int64_t K, int64_t lda) {
   const char* e = getenv("FQ_GEMM_W4");
-  return K % 256 == 0 && !(e && e[0] == '0');
+  return K % 256 == 0 && lda <= (int64_t{1} << 22) && K <= (int64_t{1} << 24) && !(e && e[0] == '0');
 }
 
 
@@ -1942,7 +1969,7 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
   } else if (tile256_fits(M, N, K, W) && !small_tiles) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-    if (use_w4(K)) {
+    if (use_w4(K, lda)) {
       gemm_w4_kernel<false><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
                                                         KvAppend{});
       r = launch_check("gemm_w4_kernel");
@@ -2013,7 +2040,7 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
   const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-  if (use_w4(K)) {
+  if (use_w4(K, lda)) {
     gemm_w4_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
     FQ_TRY(launch_check("gemm_w4_kernel"));
   } else {
