@@ -1604,21 +1604,28 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
 
   // A copies: instruction q = wave + 8t fills rows 8q..8q+7 (lane -> row
   // 8q + lane / 8, slot lane % 8 holding chunk slot ^ (row % 8)); rows past M
-  // are clamped (read, never stored)
-  const uint16_t* a_src[A_INSTR];
+  // are clamped (read, never stored).  Every copy is addressed as a
+  // wave-uniform base (the block's first row or weight row, plus the step)
+  // and a fixed 32-bit byte offset per lane (the host keeps lda small
+  // enough); the wave index sits in a scalar register.
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(A + m_base * lda);
+  const uint8_t* c_blk = codes + n_blk * (K / 2);
+  const uint8_t* m_blk = reinterpret_cast<const uint8_t*>(meta + n_blk * (K / 64) * 2);
+  uint32_t a_off[A_INSTR];
 #pragma unroll
   for (int t = 0; t < A_INSTR; ++t) {
     const int r = 8 * (wave + 8 * t) + (lane >> 3);
-    a_src[t] = A + min(m_base + r, M - 1) * lda + ((lane & 7) ^ (r & 7)) * 8;
+    a_off[t] = (uint32_t)((min(m_base + r, M - 1) - m_base) * lda * 2 + ((lane & 7) ^ (r & 7)) * 16);
   }
-  const uint8_t* c_src = codes + min(n_blk + wave * 32 + (lane >> 1), N - 1) * (K / 2) + (lane & 1) * 16;
-  const uint16_t* m_src = meta + min(n_blk + wave * 32 + (lane & 31), N - 1) * (K / 64) * 2;
+  const uint32_t c_off = (uint32_t)((min(n_blk + wave * 32 + (lane >> 1), N - 1) - n_blk) * (K / 2) + (lane & 1) * 16);
+  const uint32_t m_off = (uint32_t)((min(n_blk + wave * 32 + (lane & 31), N - 1) - n_blk) * (K / 64) * 4);
   auto issue = [&](int kt, int slot) {
     const uint32_t st = lds_base + slot * STAGE;
 #pragma unroll
-    for (int t = 0; t < A_INSTR; ++t) dma_lds16(a_src[t] + (int64_t)kt * BK, st + (wave + 8 * t) * 1024);
-    dma_lds16(c_src + (int64_t)kt * 32, st + A_BYTES + wave * 32 * 32);
-    if (lane < 32) dma_lds4(m_src + (int64_t)kt * 2, st + A_BYTES + C_BYTES + wave * 128);
+    for (int t = 0; t < A_INSTR; ++t) dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, st + (swave + 8 * t) * 1024);
+    dma_lds16_s(c_off, c_blk + (int64_t)kt * 32, st + A_BYTES + swave * 32 * 32);
+    if (lane < 32) dma_lds4_s(m_off, m_blk + (int64_t)kt * 4, st + A_BYTES + C_BYTES + swave * 128);
   };
   // this lane's weight rows: wave * 32 + 16 j + l16
   uint2 cw[2];
@@ -1847,10 +1854,11 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
 fq_status dispatch_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
                           hipStream_t st) {
   const int64_t mb = ceil_div(M, 16);
-  // the streaming decode kernel for 4-bit weights and even K steps; below 49
-  // rows it runs with 4 row blocks (the rows past M are clamped reads, never
+  // the streaming decode kernel for 4-bit weights and even K steps (and lda
+  // and K small enough for its 32-bit per-lane copy offsets); below 49 rows
+  // it runs with 4 row blocks (the rows past M are clamped reads, never
   // stored): the weight stream, not the MFMAs, sets its time there
-  if (W->kind == FQ_WEIGHT_PACKED4 && (W->k / BK) % 2 == 0) {
+  if (W->kind == FQ_WEIGHT_PACKED4 && (W->k / BK) % 2 == 0 && lda <= (int64_t{1} << 22) && W->k <= (int64_t{1} << 24)) {
     if (mb <= 4) return run_decode<4>(A, M, lda, W, epi, st);
     if (mb <= 6) return run_decode<6>(A, M, lda, W, epi, st);
     if (mb <= 8) return run_decode<8>(A, M, lda, W, epi, st);
