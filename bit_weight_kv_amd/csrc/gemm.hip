@@ -626,11 +626,14 @@ __device__ inline void mfma16x16x32_acc_ordered(float4_t& acc, const half8_t& a,
 // interleaved between them: a wave's VALU work overlaps its own MFMAs only
 // when the two are interleaved finely (measured: 8 MFMAs + 16 independent
 // VALU ops cost 162 cycles interleaved, 213 back to back, 147 for the MFMAs
-// alone).  The VALU part is dequant8 instruction for instruction: per pair a
-// byte permute and an AND-OR with the two exponents, the exact fp16 subtract
-// of {1024, 64}, one packed fp16 FMA c*s + min with {min, scale} taken from
-// the halves of `ms` -- 16 instructions per 8 weights.  Its outputs are
-// consumed by later MFMAs only, never inside this block.
+// alone).  13 instructions per 8 weights: the even elements' nibbles masked
+// into a byte word and the odd elements' shifted into another; two byte
+// permutes pair them as elements {0,1,2,3} and {4,5,6,7}; the scaled fp8
+// conversion turns each byte into an exact fp16 integer (as an OCP e4m3 value
+// a byte c < 16 is c * 2^-9, so the scale 2^9 gives c); one packed fp16 FMA
+// per pair rounds c*s + min once, with {min, scale} taken from the halves of
+// `ms` -- the same values as dequant8.  Its outputs are consumed by later
+// MFMAs only, never inside this block.
 // General form: MFMA k computes c_k += a_k * b_k.
 __device__ inline void mfma4_rebuild_ab(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a0,
                                         const half8_t& a1, const half8_t& a2, const half8_t& a3, const half8_t& b0,
@@ -639,32 +642,28 @@ __device__ inline void mfma4_rebuild_ab(float4_t& c0, float4_t& c1, float4_t& c2
   // separate volatile statements keep their order; one accumulator per MFMA
   // statement keeps every accumulator in place (a statement binding several
   // makes the register allocator copy them around)
-  uint32_t o0, o1, o2, o3;
-  const uint32_t keep = 0x00F0000Fu;  // VGPR operand: one scalar operand per VOP3 instruction
+  uint32_t t, u, p0, p1, o0, o1, o2, o3;
   mfma16x16x32_acc_ordered(c0, a0, b0);
   asm volatile(
-      "v_perm_b32 %0, %2, %2, %4\n\t"
-      "v_perm_b32 %1, %2, %2, %5\n\t"
-      "v_and_or_b32 %0, %0, %3, %6\n\t"
-      "v_and_or_b32 %1, %1, %3, %6"
-      : "=&v"(o0), "=&v"(o1)
-      : "v"(w), "v"(keep), "s"(0x0C000C00u), "s"(0x0C010C01u), "s"(0x54006400u));
+      "v_and_b32 %0, %3, %2\n\t"      // t: bytes {e0, e2, e4, e6}
+      "v_lshrrev_b32 %1, 4, %2\n\t"
+      "v_and_b32 %1, %3, %1"            // u: bytes {e1, e3, e5, e7}
+      : "=&v"(t), "=&v"(u)
+      : "v"(w), "s"(0x0F0F0F0Fu));
   mfma16x16x32_acc_ordered(c1, a1, b1);
   asm volatile(
-      "v_perm_b32 %0, %2, %2, %4\n\t"
-      "v_perm_b32 %1, %2, %2, %5\n\t"
-      "v_and_or_b32 %0, %0, %3, %6\n\t"
-      "v_and_or_b32 %1, %1, %3, %6"
-      : "=&v"(o2), "=&v"(o3)
-      : "v"(w), "v"(keep), "s"(0x0C020C02u), "s"(0x0C030C03u), "s"(0x54006400u));
+      "v_perm_b32 %0, %3, %4, %5\n\t"  // bytes {e0, e1, e2, e3}
+      "v_perm_b32 %1, %3, %4, %6\n\t"  // bytes {e4, e5, e6, e7}
+      "v_cvt_scalef32_pk_f16_fp8 %2, %0, %7"
+      : "=&v"(p0), "=&v"(p1), "=&v"(o0)
+      : "v"(u), "v"(t), "s"(0x05010400u), "s"(0x07030602u), "s"(0x44000000u));  // 512.0f
   mfma16x16x32_acc_ordered(c2, a2, b2);
   asm volatile(
-      "v_pk_add_f16 %0, %0, %4\n\t"
-      "v_pk_add_f16 %1, %1, %4\n\t"
-      "v_pk_add_f16 %2, %2, %4\n\t"
-      "v_pk_add_f16 %3, %3, %4"
-      : "+v"(o0), "+v"(o1), "+v"(o2), "+v"(o3)
-      : "s"(0xD400E400u));
+      "v_cvt_scalef32_pk_f16_fp8 %0, %3, %5 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %1, %4, %5\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %2, %4, %5 op_sel:[1,0,0]"
+      : "=&v"(o1), "=&v"(o2), "=&v"(o3)
+      : "v"(p0), "v"(p1), "s"(0x44000000u));
   mfma16x16x32_acc_ordered(c3, a3, b3);
   asm volatile(
       "v_pk_fma_f16 %0, %0, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
