@@ -1016,11 +1016,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int BMx = 256, BNx = 256, TN = 64, FM = 16, FN = 4, BKx = 64;
   constexpr int ROWB = BKx * 2;                                   // 128 bytes per staged A row
   constexpr int A_BYTES = BMx * ROWB;                             // 32 KiB
-  constexpr int C_CODES = BNx * 32, C_BYTES = C_CODES + BNx * 4;  // 9 KiB per code slot
+  constexpr int C_BYTES = BNx * 32;  // 8 KiB per code slot
+  constexpr int M_BYTES = BNx * 16;  // {min, scale} of 4 steps per weight row: 4 KiB per buffer
   constexpr int SC = 3;
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[A_BYTES], a_lds1[A_BYTES], a_lds2[A_BYTES],
       a_lds3[A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t c_lds[SC * C_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t m_lds[2 * M_BYTES];
   auto a_st = [&](auto s) -> uint8_t* {
     constexpr int S = decltype(s)::value;
     return S == 0 ? a_lds0 : S == 1 ? a_lds1 : S == 2 ? a_lds2 : a_lds3;
@@ -1075,6 +1077,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int t = 0; t < 2; ++t)
     c_off[t] = (uint32_t)((min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) - n0) * (K / 2) + (lane & 1) * 16);
   const uint32_t m_off = (uint32_t)((min(n0 + 64 * wave + lane, N - 1) - n0) * (K / 64) * 4);
+  const uint32_t m_base = (uint32_t)(uintptr_t)m_lds;
   const uint32_t c_base = (uint32_t)(uintptr_t)c_lds;
   auto issue_a = [&](auto s, int kt) {
     const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + swave * 1024;
@@ -1085,19 +1088,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t dst = c_base + (kt % SC) * C_BYTES;
 #pragma unroll
     for (int t = 0; t < 2; ++t) dma_lds16_s(c_off[t], c_blk + (int64_t)kt * 32, dst + (swave + 4 * t) * 1024);
-    dma_lds4_s(m_off, m_blk + (int64_t)kt * 4, dst + C_CODES + swave * 256);
+  };
+  // {min, scale} of steps 4g..4g+3 (16 bytes per weight row) into buffer g % 2
+  auto issue_meta = [&](int g, int buf) {
+    dma_lds16_s(m_off, m_blk + (int64_t)g * 16, m_base + buf * M_BYTES + swave * 1024);
   };
   // this lane's weight operand: column block j = weight row 64 wn + 16 j + fr,
   // slice ks = k chunk 4 ks + fk of the step (one code word), {min, scale} per row
   uint32_t cw[2][FN], cm[FN];
   auto read_codes = [&](int kt) {
     const uint8_t* slot = c_lds + (kt % SC) * C_BYTES;
+    const uint8_t* mrow = m_lds + ((kt >> 2) & 1) * M_BYTES + (kt & 3) * 4;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = wn * TN + j * 16 + fr;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) cw[ks][j] = *reinterpret_cast<const uint32_t*>(slot + row * 32 + (4 * ks + fk) * 4);
-      cm[j] = *reinterpret_cast<const uint32_t*>(slot + C_CODES + row * 4);
+      cm[j] = *reinterpret_cast<const uint32_t*>(mrow + row * 16);
     }
   };
   auto rebuild = [&](int ks, int j) {
@@ -1123,6 +1130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   issue_codes(0);
   issue_codes(1);
   issue_codes(2);
+  issue_meta(0, 0);
   issue_a(I0{}, 0);
   issue_a(I1{}, 1);
   issue_a(I2{}, 2);
@@ -1167,7 +1175,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int kc = min(kt + 3, KT - 1);
     const uint8_t* a_step = a_blk + (int64_t)kc * 128;
     const uint8_t* c_step = c_blk + (int64_t)kc * 32;
-    const uint8_t* m_step = m_blk + (int64_t)kc * 4;
+    // (steps with kt % 4 == 0 also copy the {min, scale} of steps kt+4..kt+7)
+    const int gm = min((kt >> 2) + 1, (KT >> 2) - 1);
     const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
     const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
     static_for<2 * FM>([&](auto sc) {
@@ -1177,8 +1186,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dma_lds16_s(a_off[SL], a_step, a_dst + SL * 4096);
       } else if constexpr (SL < 10) {
         dma_lds16_s(c_off[SL - 8], c_step, c_dst + (swave + 4 * (SL - 8)) * 1024);
-      } else if constexpr (SL == 10) {
-        dma_lds4_s(m_off, m_step, c_dst + C_CODES + swave * 256);
+      } else if constexpr (SL == 10 && S == 0) {
+        issue_meta(gm, ((kt >> 2) + 1) & 1);
       }
       constexpr int NX = SL + 3;
       fa[NX % 4] = NX < 2 * FM ? a_frag(As_, NX / FM, NX % FM) : a_frag(a_st(S1{}), 0, NX - 2 * FM);
@@ -1195,7 +1204,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
       }
     });
-    asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (S == 0)
+      asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // the same LDS wait where the compiler sees it (already satisfied): it
     // then knows the prefetched fragments have arrived and adds no wait
     // before the next step's first MFMAs, which would also cover the code
@@ -1920,15 +1932,17 @@ static bool small_tiles_only() {
 }
 
 // Among shapes the 256 x 256 tiles take: the one-wave-per-SIMD kernel where
-// its K loop applies (K a multiple of 256) and its 32-bit per-lane copy
-// offsets cannot overflow (up to 255 rows of lda or K / 2 bytes past the
-// block's first row), else the 8-wave kernel.  Test hook: FQ_GEMM_W4=0 in
-// the environment at the time of the call selects the 8-wave kernel for
-// every shape (the two accumulate in the same order, so their outputs are
+// its K loop applies (K a multiple of 256), its 32-bit per-lane copy offsets
+// cannot overflow (up to 255 rows of lda or K / 2 bytes past the block's
+// first row) and the {min, scale} array is 16-byte aligned (copied 16 bytes
+// per row), else the 8-wave kernel.  Test hook: FQ_GEMM_W4=0 in the
+// environment at the time of the call selects the 8-wave kernel for every
+// shape (the two accumulate in the same order, so their outputs are
 // identical).
-static bool use_w4(int64_t K, int64_t lda) {
+static bool use_w4(int64_t K, int64_t lda, const fq_weight* W) {
   const char* e = getenv("FQ_GEMM_W4");
-  return K % 256 == 0 && lda <= (int64_t{1} << 22) && K <= (int64_t{1} << 24) && !(e && e[0] == '0');
+  return K % 256 == 0 && lda <= (int64_t{1} << 22) && K <= (int64_t{1} << 24) &&
+         (uintptr_t)W->packed.meta % 16 == 0 && !(e && e[0] == '0');
 }
 
 
@@ -1976,7 +1990,7 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
   } else if (tile256_fits(M, N, K, W) && !small_tiles) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-    if (use_w4(K, lda)) {
+    if (use_w4(K, lda, W)) {
       gemm_w4_kernel<false><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
                                                         KvAppend{});
       r = launch_check("gemm_w4_kernel");
@@ -2047,7 +2061,7 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(st);
   const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-  if (use_w4(K, lda)) {
+  if (use_w4(K, lda, W)) {
     gemm_w4_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
     FQ_TRY(launch_check("gemm_w4_kernel"));
   } else {
