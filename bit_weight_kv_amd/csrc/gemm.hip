@@ -1594,10 +1594,12 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ meta, int64_t N, int64_t K,
                                                            int k_tiles_per_split, Epilogue epi,
                                                            float* __restrict__ partial) {
-  constexpr int ROWS = MB * 16, ROWS_PAD = (ROWS + 63) / 64 * 64;
-  constexpr int A_INSTR = ROWS_PAD / 64;  // A copies per wave per step (8 rows of 128 B each)
-  constexpr int PER = A_INSTR + 2;        // + one codes copy + one {min, scale} copy
-  constexpr int A_BYTES = ROWS_PAD * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
+  constexpr int ROWS = MB * 16;
+  constexpr int NQ = ROWS / 8;                  // A copies per step (8 rows of 128 B each)
+  constexpr int A_INSTR = (NQ + 7) / 8;         // per wave: waves below NQ % 8 (all when 0) issue A_INSTR,
+  constexpr int EXTRA = NQ % 8 ? NQ % 8 : 8;    // the others one fewer
+  constexpr int PER = A_INSTR + 2, PER_LO = PER - (EXTRA < 8 ? 1 : 0);  // + one codes + one {min, scale} copy
+  constexpr int A_BYTES = ROWS * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
   constexpr int S = 4;
   static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
   static_assert(MB >= 4, "two pairs of row blocks per slice carry the reconstructions");
@@ -1613,9 +1615,9 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
   const int kt0 = blockIdx.y * k_tiles_per_split;
   const int kt1 = min(KT, kt0 + k_tiles_per_split);
 
-  // A copies: instruction q = wave + 8t fills rows 8q..8q+7 (lane -> row
-  // 8q + lane / 8, slot lane % 8 holding chunk slot ^ (row % 8)); rows past M
-  // are clamped (read, never stored).  Every copy is addressed as a
+  // A copies: instruction q = wave + 8t (q < NQ) fills rows 8q..8q+7 (lane ->
+  // row 8q + lane / 8, slot lane % 8 holding chunk slot ^ (row % 8)); rows
+  // past M are clamped (read, never stored).  Every copy is addressed as a
   // wave-uniform base (the block's first row or weight row, plus the step)
   // and a fixed 32-bit byte offset per lane (the host keeps lda small
   // enough); the wave index sits in a scalar register.
@@ -1634,7 +1636,9 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
   auto issue = [&](int kt, int slot) {
     const uint32_t st = lds_base + slot * STAGE;
 #pragma unroll
-    for (int t = 0; t < A_INSTR; ++t) dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, st + (swave + 8 * t) * 1024);
+    for (int t = 0; t < A_INSTR; ++t)
+      if (t + 1 < A_INSTR || swave < EXTRA)
+        dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, st + (swave + 8 * t) * 1024);
     dma_lds16_s(c_off, c_blk + (int64_t)kt * 32, st + A_BYTES + swave * 32 * 32);
     if (lane < 32) dma_lds4_s(m_off, m_blk + (int64_t)kt * 4, st + A_BYTES + C_BYTES + swave * 128);
   };
@@ -1681,9 +1685,12 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
       const int it = kt - kt0, slot = it % S;
       if (kt > kt0) {
         // steps kt and kt+1 complete in every wave; step kt-1's slot free
-        if (kt + S - 2 < kt1)
-          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER) : "memory");
-        else
+        if (kt + S - 2 < kt1) {
+          if (swave < EXTRA)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER_LO) : "memory");
+        } else
           asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       }
       if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);

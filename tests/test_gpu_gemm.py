@@ -224,3 +224,35 @@ def test_gemm_full_size_sampled(M, which):
     ref = oracle.gemm(arows, oracle.dequant_f16(*oracle.quantize(wrows)))
     got = host(out[torch.as_tensor(rows, device="cuda:0")][:, torch.as_tensor(cols, device="cuda:0")])
     _tol_check(got, ref, f"{which} M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,w4", [(2100, 3900, 512, "1"), (2100, 3900, 512, "0"), (144, 1024, 512, "1")])
+def test_gemm_strided_operands(M, N, K, w4, monkeypatch):
+    """A, C and the residual with row strides beyond their widths (A padded by
+    64 columns, C and the residual by 8): the one-wave-per-SIMD 256 x 256
+    kernel, the 8-wave one (FQ_GEMM_W4=0) and the decode kernel (M = 144)
+    give exactly the contiguous call's output, untouched padding, and stay
+    within the oracle bound."""
+    monkeypatch.setenv("FQ_GEMM_W4", w4)
+    log(f"gemm strided M={M} N={N} K={K} w4={w4}")
+    a = synth.normal_f16(21, synth.STREAM["aux"] + 1, (M, K), 1.0)
+    w = synth.normal_f16(21, synth.STREAM["aux"] + 2, (N, K), 0.02)
+    b = synth.normal_f16(21, synth.STREAM["aux"] + 3, (N,), 0.1)
+    r = synth.normal_f16(21, synth.STREAM["aux"] + 4, (M, N), 1.0)
+    c, m = oracle.quantize(w)
+    W = fq.weight_packed(dev(c), dev(m), N, K)
+    flags = fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL
+    ad, bd, rd = dev(a), dev(b), dev(r)
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(ad, W, out, bias=bd, residual=rd, epilogue=flags)
+    a_pad = torch.zeros((M, K + 64), dtype=torch.float16, device="cuda:0")
+    a_pad[:, :K] = ad
+    r_pad = torch.zeros((M, N + 8), dtype=torch.float16, device="cuda:0")
+    r_pad[:, :N] = rd
+    c_pad = torch.full((M, N + 8), 3.0, dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(a_pad[:, :K], W, c_pad[:, :N], bias=bd, residual=r_pad[:, :N], epilogue=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(out, c_pad[:, :N]), "strided operands change the result"
+    assert (c_pad[:, N:] == 3.0).all(), "padding columns of C written"
+    ref = oracle.gemm(a, oracle.dequant_f16(c, m), b) + r.astype(np.float64)
+    _tol_check(host(out), ref, "strided")
