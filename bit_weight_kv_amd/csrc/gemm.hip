@@ -1588,7 +1588,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __rest
 // MFMAs.  Per K step a wave runs 2 slices x MB row blocks x 2 MFMAs and
 // rebuilds 4 operand words for the next step (its 2 rows x 2 slices), each
 // carried by the 4 MFMAs of a pair of row blocks.
-template <int MB>
+//
+// META4: {min, scale} copied 4 steps at a time (16 bytes per weight row, a
+// 2-buffer ring beside the stages) when every split starts on a multiple of 4
+// steps, instead of 4 bytes per row each step.
+template <int MB, bool META4>
 __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
                                                            const uint8_t* __restrict__ codes,
                                                            const uint16_t* __restrict__ meta, int64_t N, int64_t K,
@@ -1598,14 +1602,18 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
   constexpr int NQ = ROWS / 8;                  // A copies per step (8 rows of 128 B each)
   constexpr int A_INSTR = (NQ + 7) / 8;         // per wave: waves below NQ % 8 (all when 0) issue A_INSTR,
   constexpr int EXTRA = NQ % 8 ? NQ % 8 : 8;    // the others one fewer
-  constexpr int PER = A_INSTR + 2, PER_LO = PER - (EXTRA < 8 ? 1 : 0);  // + one codes + one {min, scale} copy
-  constexpr int A_BYTES = ROWS * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
+  // copies per wave per step: A, one of codes, one of {min, scale} (META4:
+  // one every fourth step, counted separately)
+  constexpr int PER = A_INSTR + (META4 ? 1 : 2), PER_LO = PER - (EXTRA < 8 ? 1 : 0);
+  constexpr int A_BYTES = ROWS * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + (META4 ? 0 : 256 * 4);
+  constexpr int M_BYTES = 256 * 16;
   constexpr int S = 4;
   static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
   static_assert(MB >= 4, "two pairs of row blocks per slice carry the reconstructions");
-  static_assert((S - 3) * PER <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
+  static_assert((S - 3) * PER + 1 <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE + (META4 ? 2 * M_BYTES : 0)];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  uint8_t* const mring = lds + S * STAGE;  // META4: group g's {min, scale} in buffer g % 2, 16 bytes per row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -1640,18 +1648,27 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
       if (t + 1 < A_INSTR || swave < EXTRA)
         dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, st + (swave + 8 * t) * 1024);
     dma_lds16_s(c_off, c_blk + (int64_t)kt * 32, st + A_BYTES + swave * 32 * 32);
-    if (lane < 32) dma_lds4_s(m_off, m_blk + (int64_t)kt * 4, st + A_BYTES + C_BYTES + swave * 128);
+    if constexpr (META4) {
+      if ((kt & 3) == 0 && lane < 32)
+        dma_lds16_s(m_off, m_blk + (int64_t)(kt >> 2) * 16,
+                    (uint32_t)(uintptr_t)mring + ((kt >> 2) & 1) * M_BYTES + swave * 512);
+    } else {
+      if (lane < 32) dma_lds4_s(m_off, m_blk + (int64_t)kt * 4, st + A_BYTES + C_BYTES + swave * 128);
+    }
   };
   // this lane's weight rows: wave * 32 + 16 j + l16
   uint2 cw[2];
   uint32_t cm[2];
-  auto read_codes = [&](int slot) {
+  auto read_codes = [&](int slot, int kt) {
     const uint8_t* st = lds + slot * STAGE + A_BYTES;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = wave * 32 + j * 16 + l16;
       cw[j] = *reinterpret_cast<const uint2*>(st + row * 32 + g4 * 8);
-      cm[j] = *reinterpret_cast<const uint32_t*>(st + C_BYTES + row * 4);
+      if constexpr (META4)
+        cm[j] = *reinterpret_cast<const uint32_t*>(mring + ((kt >> 2) & 1) * M_BYTES + row * 16 + (kt & 3) * 4);
+      else
+        cm[j] = *reinterpret_cast<const uint32_t*>(st + C_BYTES + row * 4);
     }
   };
   auto rebuild = [&](int j, int w, half8_t (&b)[2][2]) {
@@ -1673,28 +1690,34 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
     for (int t = 0; t < S - 1 && kt0 + t < kt1; ++t) issue(kt0 + t, t);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     half8_t bA[2][2], bB[2][2];
-    read_codes(0);
+    read_codes(0, kt0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int w = 0; w < 2; ++w) rebuild(j, w, bA);
     // One K step: MFMAs on `bcur`, step kt+1's operand rebuilt into `bnxt`
     // by the row-block pairs (0, 1) and (2, 3) of each slice (slice ks
-    // rebuilds word ks of rows 0 and 1).
-    auto step = [&](int kt, half8_t (&bcur)[2][2], half8_t (&bnxt)[2][2]) {
+    // rebuilds word ks of rows 0 and 1).  PH = kt % 4 (META4) or kt % 2.
+    // (each call is its own instantiation: a step body inlined twice keeps
+    // the accumulators out of registers)
+    auto step = [&](auto ph, int kt, half8_t (&bcur)[2][2], half8_t (&bnxt)[2][2]) {
+      constexpr int PH = decltype(ph)::value;
+      // copies in flight after the wait: those of step kt+2, which carry the
+      // {min, scale} of its group when META4 and kt+2 is a multiple of 4
+      constexpr int MX = (META4 && PH == 2) ? 1 : 0;
       const int it = kt - kt0, slot = it % S;
       if (kt > kt0) {
         // steps kt and kt+1 complete in every wave; step kt-1's slot free
         if (kt + S - 2 < kt1) {
           if (swave < EXTRA)
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER + MX) : "memory");
           else
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER_LO) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER_LO + MX) : "memory");
         } else
           asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       }
       if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
-      if (kt + 1 < kt1) read_codes((it + 1) % S);
+      if (kt + 1 < kt1) read_codes((it + 1) % S, kt + 1);
       const uint8_t* As_ = lds + slot * STAGE;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -1718,11 +1741,25 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
           for (int j = 0; j < 2; ++j) mfma16x16x32_acc_ordered(acc[i][j], af[i], bcur[ks][j]);
       }
     };
-    // pairs of steps: every split has an even number of steps (the host
-    // guarantees it), so the MFMA chain is one piece of code
-    for (int kt = kt0; kt < kt1; kt += 2) {
-      step(kt, bA, bB);
-      step(kt + 1, bB, bA);
+    // groups of steps: every split has a multiple of 4 steps (META4) or an
+    // even number (the host guarantees it), so the MFMA chain is one piece
+    // of code
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    if constexpr (META4) {
+      for (int kt = kt0; kt < kt1; kt += 4) {
+        step(I0{}, kt, bA, bB);
+        step(I1{}, kt + 1, bB, bA);
+        step(I2{}, kt + 2, bA, bB);
+        step(I3{}, kt + 3, bB, bA);
+      }
+    } else {
+      for (int kt = kt0; kt < kt1; kt += 2) {
+        step(I0{}, kt, bA, bB);
+        step(I1{}, kt + 1, bB, bA);
+      }
     }
     // the last MFMAs' results are read by VALU instructions below
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1847,8 +1884,11 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
   const int KT = (int)(W->k / BK);
   const int64_t zb = ceil_div(M, 16 * MB);
   int splits = decode_splits(ceil_div(N, 256) * zb, KT, M, N, MB);
-  // the kernel runs K steps in pairs: even steps per split (KT is even here)
-  const int kps = ((KT + splits - 1) / splits + 1) & ~1;
+  // the kernel runs K steps in groups: a multiple of 4 per split when the
+  // {min, scale} go 4 steps at a time (K a multiple of 256 and that array
+  // 16-byte aligned), else an even number (KT is even here)
+  const bool meta4 = KT % 4 == 0 && (uintptr_t)W->packed.meta % 16 == 0;
+  const int kps = meta4 ? ((KT + splits - 1) / splits + 3) & ~3 : ((KT + splits - 1) / splits + 1) & ~1;
   splits = (KT + kps - 1) / kps;
   float* partial = nullptr;
   if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
@@ -1858,8 +1898,12 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
                                                        partial);
     FQ_TRY(launch_check("gemm_decode_kernel"));
   } else {
-    gemm_decode8_kernel<MB><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps,
-                                                        epi, partial);
+    if (meta4)
+      gemm_decode8_kernel<MB, true><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,
+                                                                kps, epi, partial);
+    else
+      gemm_decode8_kernel<MB, false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,
+                                                                 kps, epi, partial);
     FQ_TRY(launch_check("gemm_decode8_kernel"));
   }
   if (splits > 1) {

@@ -65,13 +65,41 @@ def test_gemm_packed_shapes(M, N, K):
 
 @pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("M", [64, 100, 144, 256])
-def test_gemm_decode_kernels(M, waves, monkeypatch):
+@pytest.mark.parametrize("K", [2048, 384])
+def test_gemm_decode_kernels(M, waves, K, monkeypatch):
     """The two 4-bit decode kernels (4 waves x 64 weight rows, 8 waves x 32;
-    the library reads FQ_DECODE_WAVES at each call) over ragged N, split K."""
+    the library reads FQ_DECODE_WAVES at each call) over ragged N, split K;
+    K = 384 (6 steps) takes the 8-wave kernel's per-step {min, scale} copies,
+    K = 2048 the 4-step ones."""
     if waves == "4":
         monkeypatch.setenv("FQ_DECODE_WAVES", "4")
-    got, ref = _run(M, 1000, 2048, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, seed=M)
-    _tol_check(got, ref, f"decode kernel waves={waves} M={M}")
+    got, ref = _run(M, 1000, K, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, seed=M)
+    _tol_check(got, ref, f"decode kernel waves={waves} M={M} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(144, 1000, 2048), (2100, 3900, 512)])
+def test_gemm_meta_alignment_fallback(M, N, K):
+    """A {min, scale} array that is 4- but not 16-byte aligned takes the kernels
+    that copy it 4 bytes per row (the decode kernel's per-step copies, the
+    8-wave 256 x 256 kernel): the same output as the aligned array, bit for
+    bit (both paths add the same products in the same order)."""
+    log(f"gemm meta alignment M={M} N={N} K={K}")
+    a = synth.normal_f16(23, synth.STREAM["aux"] + 1, (M, K), 1.0)
+    w = synth.normal_f16(23, synth.STREAM["aux"] + 2, (N, K), 0.02)
+    c, m = oracle.quantize(w)
+    cd, md = dev(c), dev(m)
+    ad = dev(a)
+    out1 = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(ad, fq.weight_packed(cd, md, N, K), out1)
+    flat = torch.zeros(md.numel() + 2, dtype=torch.float16, device="cuda:0")
+    flat[2:] = md.reshape(-1)
+    m_off = flat[2:].view(md.shape)  # 4 bytes past a 256-byte-aligned allocation
+    assert m_off.data_ptr() % 16 == 4
+    out2 = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    fq.fq_dequant_gemm(ad, fq.weight_packed(cd, m_off, N, K), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    _tol_check(host(out1), oracle.gemm(a, oracle.dequant_f16(c, m)), "meta alignment")
 
 
 @pytest.mark.parametrize("flags,qcols", [
