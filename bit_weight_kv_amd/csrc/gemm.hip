@@ -675,6 +675,59 @@ __device__ inline void mfma4_rebuild_ab(float4_t& c0, float4_t& c1, float4_t& c2
   out = __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
 }
 
+// The same reconstruction spread over two groups of four MFMAs (at most 7
+// VALU instructions beside each group): with one wave per SIMD the wave
+// issues everything itself, and 13 instructions around 4 MFMAs crowd their
+// issue slots.  The first half leaves the two paired byte words and the
+// first converted pair in p0, p1, o0; the second half finishes into `out`.
+__device__ inline void mfma4_rebuild_h1(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
+                                        const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
+                                        uint32_t w, uint32_t& p0, uint32_t& p1, uint32_t& o0) {
+  uint32_t t, u;
+  mfma16x16x32_acc_ordered(c0, a, b0);
+  asm volatile(
+      "v_and_b32 %0, %3, %2\n\t"
+      "v_lshrrev_b32 %1, 4, %2"
+      : "=&v"(t), "=&v"(u)
+      : "v"(w), "s"(0x0F0F0F0Fu));
+  mfma16x16x32_acc_ordered(c1, a, b1);
+  asm volatile("v_and_b32 %0, %1, %0" : "+v"(u) : "s"(0x0F0F0F0Fu));
+  mfma16x16x32_acc_ordered(c2, a, b2);
+  asm volatile(
+      "v_perm_b32 %0, %2, %3, %4\n\t"
+      "v_perm_b32 %1, %2, %3, %5"
+      : "=&v"(p0), "=&v"(p1)
+      : "v"(u), "v"(t), "s"(0x05010400u), "s"(0x07030602u));
+  mfma16x16x32_acc_ordered(c3, a, b3);
+  asm volatile("v_cvt_scalef32_pk_f16_fp8 %0, %1, %2" : "=&v"(o0) : "v"(p0), "s"(0x44000000u));
+}
+__device__ inline void mfma4_rebuild_h2(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
+                                        const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
+                                        uint32_t p0, uint32_t p1, uint32_t o0, uint32_t ms, half8_t& out) {
+  uint32_t o1, o2, o3;
+  mfma16x16x32_acc_ordered(c0, a, b0);
+  asm volatile(
+      "v_cvt_scalef32_pk_f16_fp8 %0, %2, %4 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_f16_fp8 %1, %3, %4"
+      : "=&v"(o1), "=&v"(o2)
+      : "v"(p0), "v"(p1), "s"(0x44000000u));
+  mfma16x16x32_acc_ordered(c1, a, b1);
+  asm volatile(
+      "v_cvt_scalef32_pk_f16_fp8 %0, %2, %3 op_sel:[1,0,0]\n\t"
+      "v_pk_fma_f16 %1, %1, %4, %4 op_sel:[0,1,0] op_sel_hi:[1,1,0]"
+      : "=&v"(o3), "+v"(o0)
+      : "v"(p1), "s"(0x44000000u), "v"(ms));
+  mfma16x16x32_acc_ordered(c2, a, b2);
+  asm volatile(
+      "v_pk_fma_f16 %0, %0, %2, %2 op_sel:[0,1,0] op_sel_hi:[1,1,0]\n\t"
+      "v_pk_fma_f16 %1, %1, %2, %2 op_sel:[0,1,0] op_sel_hi:[1,1,0]"
+      : "+v"(o1), "+v"(o2)
+      : "v"(ms));
+  mfma16x16x32_acc_ordered(c3, a, b3);
+  asm volatile("v_pk_fma_f16 %0, %0, %1, %1 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "+v"(o3) : "v"(ms));
+  out = __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
+}
+
 __device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
                                      const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
                                      uint32_t w, uint32_t ms, half8_t& out) {
@@ -1155,8 +1208,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // (slot = 16 ks + i; 11 per wave, so the wait before the barrier leaves
   // exactly this step's copies in flight), and rebuilds step kt+1's operand
   // into the other register set: rebuild r (slice r / 4, column block r % 4)
-  // rides on the 4 MFMAs of slot 4 + 3 r, so the code words have 4 slots to
-  // arrive.  The last three slots read the next step's first three
+  // rides on the MFMAs of slots 4 + 3 r and 5 + 3 r (two halves), so the
+  // code words have 4 slots to arrive.  The last three slots read the next step's first three
   // fragments (that stage is complete).  (each of the four calls is its own
   // instantiation: a step body inlined twice keeps the accumulators out of
   // registers)
@@ -1179,6 +1232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int gm = min((kt >> 2) + 1, (KT >> 2) - 1);
     const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
     const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
+    uint32_t sp0 = 0, sp1 = 0, so0 = 0;  // a reconstruction's values between its two slots
     static_for<2 * FM>([&](auto sc) {
       constexpr int SL = decltype(sc)::value;
       constexpr int ks = SL / FM, i = SL % FM;
@@ -1195,9 +1249,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const half8_t& af = fa[SL % 4];
       if constexpr (SL >= 4 && (SL - 4) % 3 == 0 && (SL - 4) / 3 < 2 * FN) {
         constexpr int r = (SL - 4) / 3;
+        mfma4_rebuild_h1(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, bcur[ks][0], bcur[ks][1], bcur[ks][2],
+                         bcur[ks][3], cw[r / FN][r % FN], sp0, sp1, so0);
+      } else if constexpr (SL >= 5 && (SL - 5) % 3 == 0 && (SL - 5) / 3 < 2 * FN) {
+        constexpr int r = (SL - 5) / 3;
         half8_t nb;
-        mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
-                         bcur[ks][2], bcur[ks][3], cw[r / FN][r % FN], cm[r % FN], nb);
+        mfma4_rebuild_h2(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, bcur[ks][0], bcur[ks][1], bcur[ks][2],
+                         bcur[ks][3], sp0, sp1, so0, cm[r % FN], nb);
         bnxt[r / FN][r % FN] = nb;
       } else {
 #pragma unroll
