@@ -425,14 +425,44 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   constexpr float kL2e = 1.4426950408889634f;
 
+  // 4-bit cache: the raw codes and {min, scale} of the next chunk are loaded
+  // into registers before the current chunk's products, so their latency
+  // hides behind them; they are converted and stored at the next chunk's
+  // start.  K: thread -> (position tid / 2, half tid % 2: D/16 code words and
+  // one {min, scale}); V: thread -> (8 positions of storage chunk pc, channel
+  // word dc: one code word and one {min, scale} per position).
+  uint32_t rk[D / 16], rkm = 0, rv[8], rvm[8];
+  auto load_raw = [&](int64_t k0) {
+    if constexpr (!F16) {
+      if (tid < 128) {
+        const int key = tid >> 1, hf = tid & 1;
+        const int64_t j = min(k0 + key, nkeys - 1);
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(kc + (row0 + j) * (D / 2));
+#pragma unroll
+        for (int w = 0; w < D / 16; ++w) rk[w] = cw[hf * (D / 16) + w];
+        rkm = reinterpret_cast<const uint32_t*>(km)[(row0 + j) * G + hf * (D / 16) * 8 / 64];
+      } else {
+        const int u = tid - 128, pc = u & 7, dc = u >> 3;
+        if (dc < D / 8) {
+          const int sl = pc >> 2, qq = pc & 3;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
+            const int64_t j = min(k0 + key, nkeys - 1);
+            rv[jj] = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[dc];
+            rvm[jj] = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + dc / 8];
+          }
+        }
+      }
+    }
+  };
+  load_raw(0);
   for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
     __syncthreads();
     // ---- reconstruct K (threads 0..127) and V (threads 128..255) ----
     if (tid < 128) {
       const int key = tid >> 1, hf = tid & 1;  // 2 threads per position, D/2 channels each
       const int64_t j = min(k0 + key, nkeys - 1);
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(kc + (row0 + j) * (D / 2));
-      const uint32_t* mw = reinterpret_cast<const uint32_t*>(km) + (row0 + j) * G;
 #pragma unroll
       for (int w = 0; w < D / 16; ++w) {  // 8-channel words of this half
         const int word = hf * (D / 16) + w;
@@ -442,11 +472,11 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
           const uint4 r4 = *reinterpret_cast<const uint4*>(k16 + (row0 + j) * D + d0);
           o[0] = r4.x, o[1] = r4.y, o[2] = r4.z, o[3] = r4.w;
         } else {
-          const uint32_t mb = mw[d0 / 64];
+          const uint32_t mb = rkm;  // one group per half (D/2 = 64 channels at d = 128, 32 at d = 64)
           const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
           const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
           const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-          const uint32_t code = cw[word];
+          const uint32_t code = rk[w];
           const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
@@ -468,14 +498,14 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
         uint32_t vals[8][4];                  // [position][channel pair]
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
-          const int64_t j = min(k0 + key, nkeys - 1);
           if constexpr (F16) {
+            const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
+            const int64_t j = min(k0 + key, nkeys - 1);
             const uint4 r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + j) * D + dc * 8);
             vals[jj][0] = r4.x, vals[jj][1] = r4.y, vals[jj][2] = r4.z, vals[jj][3] = r4.w;
           } else {
-            const uint32_t code = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[dc];
-            const uint32_t mb = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + dc / 8];
+            const uint32_t code = rv[jj];
+            const uint32_t mb = rvm[jj];
             const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
             const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
             const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
@@ -504,6 +534,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       }
     }
     __syncthreads();
+    if (k0 + KC < nkeys) load_raw(k0 + KC);
     // skip chunks entirely after this wave's last query (causal)
     if (k0 > pos + t0 + 31) continue;
     // ---- S^T = K^ Q^T : 4 key blocks x 2 query blocks ----
