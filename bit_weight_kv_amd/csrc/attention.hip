@@ -174,20 +174,18 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
     qsum[g] = s;
   }
 
-  // ---- scores ----
+  // ---- scores: two positions per thread and iteration, both positions'
+  // codes requested before either is used (the second clamped to a valid
+  // row and discarded when past the end) ----
   float lmax = -INFINITY;
-  for (int j = tid; j < len; j += 256) {
-    const uint4* crow = reinterpret_cast<const uint4*>(kc + (row0 + j) * (D / 2));
-    const uint32_t* mrow = reinterpret_cast<const uint32_t*>(km) + (row0 + j) * G;
+  auto score = [&](const uint4 (&c)[2 * G], const uint32_t (&mb)[G]) {
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint32_t mb = mrow[g];
       float dc = 0.f;
 #pragma unroll
       for (int v4 = 0; v4 < 2; ++v4) {
-        const uint4 c = crow[g * 2 + v4];
-        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+        const uint32_t w[4] = {c[g * 2 + v4].x, c[g * 2 + v4].y, c[g * 2 + v4].z, c[g * 2 + v4].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           half2_t cc[4];
@@ -197,12 +195,47 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
           for (int u = 0; u < 4; ++u) dc = __builtin_amdgcn_fdot2(cc[u], qv[base + u], dc, false);
         }
       }
-      s += h2f((uint16_t)(mb >> 16)) * dc + h2f((uint16_t)(mb & 0xFFFF)) * qsum[g];
+      s += h2f((uint16_t)(mb[g] >> 16)) * dc + h2f((uint16_t)(mb[g] & 0xFFFF)) * qsum[g];
     }
-    s *= kLog2e;
-    p[j] = s;
-    lmax = fmaxf(lmax, s);
+    return s * kLog2e;
+  };
+  for (int j = tid; j < len; j += 512) {
+    const int jb = min(j + 256, len - 1);
+    const uint4* crow1 = reinterpret_cast<const uint4*>(kc + (row0 + j) * (D / 2));
+    const uint4* crow2 = reinterpret_cast<const uint4*>(kc + (row0 + jb) * (D / 2));
+    uint4 c1[2 * G], c2[2 * G];
+    uint32_t m1[G], m2[G];
+#pragma unroll
+    for (int i = 0; i < 2 * G; ++i) c1[i] = crow1[i];
+#pragma unroll
+    for (int i = 0; i < 2 * G; ++i) c2[i] = crow2[i];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m1[g] = reinterpret_cast<const uint32_t*>(km)[(row0 + j) * G + g];
+      m2[g] = reinterpret_cast<const uint32_t*>(km)[(row0 + jb) * G + g];
+    }
+    const float s1 = score(c1, m1);
+    p[j] = s1;
+    lmax = fmaxf(lmax, s1);
+    if (j + 256 < len) {
+      const float s2 = score(c2, m2);
+      p[j + 256] = s2;
+      lmax = fmaxf(lmax, s2);
+    }
   }
+  // the value pass's first code words are requested before the softmax
+  // reductions (they do not depend on the probabilities), and each
+  // iteration below requests the next one's before its own arithmetic
+  const int g = wl / 8;  // group of this lane's 8 channels
+  uint32_t nw1 = 0, nm1 = 0, nw2 = 0, nm2 = 0;
+  auto load_v = [&](int j) {
+    const int j1 = min(j, len - 1), j2 = min(j + SLOTS, len - 1);  // clamped rows: read, never used
+    nw1 = reinterpret_cast<const uint32_t*>(vc + (row0 + j1) * (D / 2))[wl];
+    nm1 = reinterpret_cast<const uint32_t*>(vm)[(row0 + j1) * G + g];
+    nw2 = reinterpret_cast<const uint32_t*>(vc + (row0 + j2) * (D / 2))[wl];
+    nm2 = reinterpret_cast<const uint32_t*>(vm)[(row0 + j2) * G + g];
+  };
+  load_v(slot);
   const float mx = block_max256(lmax, red);
   float lsum = 0.f;
   for (int j = tid; j < len; j += 256) {
@@ -213,7 +246,6 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   const float inv = 1.0f / block_sum256(lsum, red);  // also orders the p[] writes before the reads below
 
   // ---- values ----
-  const int g = wl / 8;  // group of this lane's 8 channels
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float bsum = 0.f;
   // two positions per iteration: sum_j (p_j s_j) c_jk as fp32 dot products of
@@ -221,10 +253,8 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   for (int j = slot; j < len; j += 2 * SLOTS) {
     const int j2 = j + SLOTS;
     const bool two = j2 < len;
-    const uint32_t w1 = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[wl];
-    const uint32_t mb1 = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + g];
-    const uint32_t w2 = two ? reinterpret_cast<const uint32_t*>(vc + (row0 + j2) * (D / 2))[wl] : 0u;
-    const uint32_t mb2 = two ? reinterpret_cast<const uint32_t*>(vm)[(row0 + j2) * G + g] : 0u;
+    const uint32_t w1 = nw1, mb1 = nm1, w2 = two ? nw2 : 0u, mb2 = two ? nm2 : 0u;
+    if (j + 2 * SLOTS < len) load_v(j + 2 * SLOTS);
     const float p1 = p[j], p2 = two ? p[j2] : 0.f;
     bsum += p1 * h2f((uint16_t)(mb1 & 0xFFFF)) + p2 * h2f((uint16_t)(mb2 & 0xFFFF));
     const half2_t a2 = {(half_t)(p1 * h2f((uint16_t)(mb1 >> 16))), (half_t)(p2 * h2f((uint16_t)(mb2 >> 16)))};
