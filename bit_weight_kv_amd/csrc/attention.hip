@@ -52,30 +52,41 @@ __device__ inline float block_sum256(float v, float* red) {
 }
 
 // Codes of 8 consecutive channels (one word) as exact fp16 integers, 4 pairs
-// in natural channel order: byte j duplicated into both halves, the low nibble
-// kept under exponent 0x64 (1024 + c) and the high nibble, at bits 4..7, under
-// exponent 0x54 (64 + c), then an exact subtract of {1024, 64}.
-__device__ inline void codes8_f16(uint32_t w, half2_t out[4]) {
-  const half2_t bias = {(half_t)-1024.0f, (half_t)-64.0f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t sel = 0x0C000C00u | (uint32_t)j << 16 | (uint32_t)j;
-    const uint32_t p = (__builtin_amdgcn_perm(w, w, sel) & 0x00F0000Fu) | 0x54006400u;
-    out[j] = __builtin_bit_cast(half2_t, p) + bias;
-  }
+// in natural channel order, through the scaled fp8 conversion: the even
+// channels' nibbles masked into one byte word, the odd channels' into
+// another, two byte permutes pairing them in channel order, and each byte
+// read as an OCP e4m3 value (c * 2^-9 for c < 16) scaled by 2^9 -- 9
+// instructions per word.
+__device__ inline void codes8_cvt(uint32_t w, half2_t out[4]) {
+  const uint32_t t = w & 0x0F0F0F0Fu, u = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t p0 = __builtin_amdgcn_perm(u, t, 0x05010400u);  // bytes {c0, c1, c2, c3}
+  const uint32_t p1 = __builtin_amdgcn_perm(u, t, 0x07030602u);  // bytes {c4, c5, c6, c7}
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p0, 512.0f, false);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p0, 512.0f, true);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, 512.0f, false);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, 512.0f, true);
 }
 
 // Channel k of two positions as an exact fp16 pair {c1_k, c2_k}, for the 8
-// channels of code words w1 and w2 (even channels: low nibbles under
-// exponent 0x64; odd: high nibbles under 0x54).
+// channels of code words w1 and w2, through the scaled fp8 conversion: each
+// word's even and odd channels' nibbles masked into byte words, one byte
+// permute pairing two channels of both positions ({c1_k, c2_k, c1_k', c2_k'}),
+// and one conversion per pair -- 18 instructions for 16 codes.
 __device__ inline void codes8_pairs(uint32_t w1, uint32_t w2, half2_t out[8]) {
-  const half2_t lo_bias = {(half_t)-1024.0f, (half_t)-1024.0f}, hi_bias = {(half_t)-64.0f, (half_t)-64.0f};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t t = __builtin_amdgcn_perm(w2, w1, 0x0C000C00u | (uint32_t)(4 + q) << 16 | (uint32_t)q);
-    out[2 * q] = __builtin_bit_cast(half2_t, (t & 0x000F000Fu) | 0x64006400u) + lo_bias;
-    out[2 * q + 1] = __builtin_bit_cast(half2_t, (t & 0x00F000F0u) | 0x54005400u) + hi_bias;
-  }
+  const uint32_t t1 = w1 & 0x0F0F0F0Fu, u1 = (w1 >> 4) & 0x0F0F0F0Fu;  // channels {0,2,4,6} / {1,3,5,7}
+  const uint32_t t2 = w2 & 0x0F0F0F0Fu, u2 = (w2 >> 4) & 0x0F0F0F0Fu;
+  const uint32_t e01 = __builtin_amdgcn_perm(t2, t1, 0x05010400u);  // channels 0, 2 of both positions
+  const uint32_t e23 = __builtin_amdgcn_perm(t2, t1, 0x07030602u);  // channels 4, 6
+  const uint32_t o01 = __builtin_amdgcn_perm(u2, u1, 0x05010400u);  // channels 1, 3
+  const uint32_t o23 = __builtin_amdgcn_perm(u2, u1, 0x07030602u);  // channels 5, 7
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e01, 512.0f, false);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e01, 512.0f, true);
+  out[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e23, 512.0f, false);
+  out[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e23, 512.0f, true);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o01, 512.0f, false);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o01, 512.0f, true);
+  out[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o23, 512.0f, false);
+  out[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o23, 512.0f, true);
 }
 
 // F16 selects the fp16 cache (k16/v16): each position is then covered by D/8
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           half2_t cc[4];
-          codes8_f16(w[k], cc);
+          codes8_cvt(w[k], cc);
           const int base = (g * 64 + v4 * 32 + k * 8) / 2;
 #pragma unroll
           for (int u = 0; u < 4; ++u) dc = __builtin_amdgcn_fdot2(cc[u], qv[base + u], dc, false);
