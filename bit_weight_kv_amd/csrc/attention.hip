@@ -67,6 +67,15 @@ __device__ inline void codes8_cvt(uint32_t w, half2_t out[4]) {
   out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(p1, 512.0f, true);
 }
 
+// 8 codes (one word) -> the 8 fp16 values fp16(min + c * s), one rounding, as
+// 4 packed pairs in channel order: codes8_cvt, then one packed FMA per pair.
+__device__ inline void dequant8_cvt(uint32_t w, half2_t mn2, half2_t s2, uint32_t o[4]) {
+  half2_t c[4];
+  codes8_cvt(w, c);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c[p], s2, mn2));
+}
+
 // Channel k of two positions as an exact fp16 pair {c1_k, c2_k}, for the 8
 // channels of code words w1 and w2, through the scaled fp8 conversion: each
 // word's even and odd channels' nibbles masked into byte words, one byte
@@ -447,7 +456,6 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   const int t0 = blockIdx.x * 128 + wave * 32;     // first query of this wave
   const int64_t row0 = ((b0 + b) * H + h) * cap;   // first cache row of this (b, h)
   const int64_t nkeys = pos + min(T, (int)(blockIdx.x * 128 + 128));
-  const half2_t neg1024 = {(half_t)-1024.0f, (half_t)-1024.0f};
 
   // Q^T operand: lane (query l16 of q-block qb, d slice kd, chunk g4)
   half8_t qf[2][NKD];
@@ -517,14 +525,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
           const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
           const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
           const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-          const uint32_t code = rk[w];
-          const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
-            const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
-            o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
-          }
+          dequant8_cvt(rk[w], mn2, s2, o);
         }
         const int arr = d0 / 64, chunk = (d0 % 64) / 8;
         *reinterpret_cast<uint4*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -545,18 +546,11 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
             const uint4 r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + j) * D + dc * 8);
             vals[jj][0] = r4.x, vals[jj][1] = r4.y, vals[jj][2] = r4.z, vals[jj][3] = r4.w;
           } else {
-            const uint32_t code = rv[jj];
             const uint32_t mb = rvm[jj];
             const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
             const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
             const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-            const uint32_t lo = code & 0x0F0F0F0Fu, hi = (code >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const uint32_t sel = 0x0C000C00u | (uint32_t)(4 + p) << 16 | (uint32_t)p;
-              const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) + neg1024;
-              vals[jj][p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, mn2));
-            }
+            dequant8_cvt(rv[jj], mn2, s2, vals[jj]);
           }
         }
         // channel i of the 8: gather its 8 positions into one 16-byte chunk
