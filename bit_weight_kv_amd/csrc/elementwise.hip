@@ -52,21 +52,31 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* __restri
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * ldx;
-  float v[MAXC][8];
+  // the row stays in registers as loaded (fp16, converted exactly at each
+  // use): half the registers of an fp32 copy, so more rows are in flight per
+  // SIMD (the memory stream, not the arithmetic, bounds this kernel)
+  uint4 xv[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
+    if (e < h) {
+      xv[c] = *reinterpret_cast<const uint4*>(xr + e);
+    }
+  }
+  auto val = [&](int c, int j) {  // fp16 pair j (elements 2j, 2j+1) of chunk c
+    return j < 2 ? (j == 0 ? xv[c].x : xv[c].y) : (j == 2 ? xv[c].z : xv[c].w);
+  };
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
     const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
     if (e < h) {
-      const uint4 r = *reinterpret_cast<const uint4*>(xr + e);
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[c][2 * j] = h2f((uint16_t)(w[j] & 0xFFFF));
-        v[c][2 * j + 1] = h2f((uint16_t)(w[j] >> 16));
+        const uint32_t w = val(c, j);
+        s += h2f((uint16_t)(w & 0xFFFF));
+        s += h2f((uint16_t)(w >> 16));
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s += v[c][j];
     }
   }
   const float mean = block_sum256(s, red) / (float)h;
@@ -76,9 +86,11 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* __restri
     const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
     if (e < h) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = v[c][j] - mean;
-        q += d * d;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = val(c, j);
+        const float d0 = h2f((uint16_t)(w & 0xFFFF)) - mean, d1 = h2f((uint16_t)(w >> 16)) - mean;
+        q += d0 * d0;
+        q += d1 * d1;
       }
     }
   }
@@ -96,8 +108,11 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const uint16_t* __restri
       uint32_t o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a0 = (v[c][2 * j] - mean) * rstd * h2f((uint16_t)(gw[j] & 0xFFFF)) + h2f((uint16_t)(bw[j] & 0xFFFF));
-        const float a1 = (v[c][2 * j + 1] - mean) * rstd * h2f((uint16_t)(gw[j] >> 16)) + h2f((uint16_t)(bw[j] >> 16));
+        const uint32_t w = val(c, j);
+        const float a0 = (h2f((uint16_t)(w & 0xFFFF)) - mean) * rstd * h2f((uint16_t)(gw[j] & 0xFFFF)) +
+                         h2f((uint16_t)(bw[j] & 0xFFFF));
+        const float a1 = (h2f((uint16_t)(w >> 16)) - mean) * rstd * h2f((uint16_t)(gw[j] >> 16)) +
+                         h2f((uint16_t)(bw[j] >> 16));
         o[j] = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
       }
       *reinterpret_cast<uint4*>(yr + e) = make_uint4(o[0], o[1], o[2], o[3]);
