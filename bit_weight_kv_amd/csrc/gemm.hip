@@ -1842,6 +1842,216 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
   }
 }
 
+// The decode GEMM with the prefill kernel's arrangement: 4 waves side by
+// side in N (64 weight rows each, one wave per SIMD) over the batch's 16 MB
+// rows, K step 64, each A fragment feeding 4 MFMAs; the same copies as the
+// prefill kernel (scalar base + 32-bit lane offsets, unconditional, {min,
+// scale} 4 steps at a time) and split-K over ranges of a multiple of 4 steps.
+// Slot = 16-row block of one k slice (2 MB slots per step): copies in slots
+// 0..7, rebuilds (full, 13 instructions with 4 MFMAs) in the last 8 slots.
+// Slice ks gives lane group g the k chunk 2 g + ks (8 values), as the 8-wave
+// decode kernel does, so the two add the same products in the same order.
+template <int MB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_decode_w4_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int64_t lda, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ meta, int64_t N, int64_t K, int k_tiles_per_split, Epilogue epi,
+    float* __restrict__ partial) {
+  constexpr int ROWS = MB * 16, NSL = 2 * MB;        // A rows per block, row-block slots per step
+  constexpr int NQ = ROWS / 8;                       // A copies per step (8 rows of 128 B)
+  constexpr int A_MAX = (NQ + 3) / 4, EXTRA = NQ % 4 ? NQ % 4 : 4;  // waves below EXTRA issue A_MAX, others one fewer
+  constexpr int A_BYTES = ROWS * 128, C_BYTES = 256 * 32, M_BYTES = 256 * 16;
+  constexpr int SC = 3, FN = 4, TN = 64;
+  constexpr int RING = NSL % 4 == 0 ? 4 : 6;         // A fragment ring (divides NSL), read 3 slots ahead
+  static_assert(NSL % RING == 0 && NSL >= 8, "slot layout");
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[A_BYTES], a_lds1[A_BYTES], a_lds2[A_BYTES],
+      a_lds3[A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t c_lds[SC * C_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t m_lds[2 * M_BYTES];
+  auto a_st = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    return S == 0 ? a_lds0 : S == 1 ? a_lds1 : S == 2 ? a_lds2 : a_lds3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave, fr = lane & 15, fk = lane >> 4;
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t n0 = (int64_t)blockIdx.x * 256, m0 = (int64_t)blockIdx.z * ROWS;
+  const int KT = (int)(K / BK);
+  const int kt0 = blockIdx.y * k_tiles_per_split;
+  const int kt1 = min(KT, kt0 + k_tiles_per_split);  // kt1 - kt0: a positive multiple of 4 (host)
+
+  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+  const uint8_t* c_blk = codes + n0 * (K / 2);
+  const uint8_t* m_blk = reinterpret_cast<const uint8_t*>(meta + n0 * (K / 64) * 2);
+  // A: instruction q = w + 4t (q < NQ) fills rows 8q..8q+7; codes: instruction
+  // p = w, w + 4 fills rows 32p..32p+31; meta: wave w rows 64w..64w+63
+  uint32_t a_off[A_MAX], c_off[2];
+#pragma unroll
+  for (int t = 0; t < A_MAX; ++t) {
+    const int r = 8 * (wave + 4 * t) + (lane >> 3);
+    a_off[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * lda * 2 + ((lane & 7) ^ (r & 7)) * 16);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    c_off[t] = (uint32_t)((min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) - n0) * (K / 2) + (lane & 1) * 16);
+  const uint32_t m_off = (uint32_t)((min(n0 + 64 * wave + lane, N - 1) - n0) * (K / 64) * 4);
+  const uint32_t c_base = (uint32_t)(uintptr_t)c_lds, m_base = (uint32_t)(uintptr_t)m_lds;
+  auto issue_a = [&](auto s, int kt) {
+    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + swave * 1024;
+#pragma unroll
+    for (int t = 0; t < A_MAX; ++t)
+      if (t + 1 < A_MAX || swave < EXTRA) dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, dst + t * 4096);
+  };
+  auto issue_codes = [&](int kt) {
+    const uint32_t dst = c_base + (kt % SC) * C_BYTES;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dma_lds16_s(c_off[t], c_blk + (int64_t)kt * 32, dst + (swave + 4 * t) * 1024);
+  };
+  // {min, scale} of 4-step group g into buffer buf
+  auto issue_meta = [&](int g, int buf) {
+    dma_lds16_s(m_off, m_blk + (int64_t)g * 16, m_base + buf * M_BYTES + swave * 1024);
+  };
+  uint32_t cw[2][FN], cm[FN];
+  auto read_codes = [&](int kt) {
+    const uint8_t* slot = c_lds + (kt % SC) * C_BYTES;
+    const uint8_t* mrow = m_lds + ((kt >> 2) & 1) * M_BYTES + (kt & 3) * 4;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * TN + j * 16 + fr;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) cw[ks][j] = *reinterpret_cast<const uint32_t*>(slot + row * 32 + (2 * fk + ks) * 4);
+      cm[j] = *reinterpret_cast<const uint32_t*>(mrow + row * 16);
+    }
+  };
+  auto rebuild = [&](int ks, int j) {
+    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
+    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
+    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+    uint32_t o[4];
+    dequant8(cw[ks][j], mn2, s2, o);
+    return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+  auto a_frag = [&](const uint8_t* As_, int ks, int i) {
+    const int r = i * 16 + fr;
+    return *reinterpret_cast<const half8_t*>(As_ + r * 128 + (((2 * fk + ks) ^ (r & 7)) * 16));
+  };
+
+  float4_t acc[MB][FN];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  // prologue: codes and A of the split's first three steps, {min, scale} of
+  // its first 4-step group; operand of the first step rebuilt
+  issue_codes(kt0);
+  issue_codes(kt0 + 1);
+  issue_codes(kt0 + 2);
+  issue_meta(kt0 >> 2, (kt0 >> 2) & 1);
+  issue_a(I0{}, kt0);
+  issue_a(I1{}, kt0 + 1);
+  issue_a(I2{}, kt0 + 2);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  half8_t bA[2][FN], bB[2][FN];
+  read_codes(kt0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bA[ks][j] = rebuild(ks, j);
+  half8_t fa[RING];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) fa[t] = a_frag(a_lds0, t / MB, t % MB);
+
+  // step kt (S = (kt - kt0) % 4): as in the prefill kernel; per wave A_w + 2
+  // copies, + 1 {min, scale} copy when S == 0 (group kt/4 + 1)
+  auto step = [&](auto s, int kt) {
+    constexpr int S = decltype(s)::value;
+    constexpr int P = S & 1;
+    using S3 = std::integral_constant<int, (S + 3) % 4>;
+    using S1 = std::integral_constant<int, (S + 1) % 4>;
+    half8_t(&bcur)[2][FN] = P == 0 ? bA : bB;
+    half8_t(&bnxt)[2][FN] = P == 0 ? bB : bA;
+    const uint8_t* As_ = a_st(s);
+    read_codes(kt + 1);  // stale but harmless past the split's last step
+    const int kc = min(kt + 3, kt1 - 1);
+    const uint8_t* a_step = a_blk + (int64_t)kc * 128;
+    const uint8_t* c_step = c_blk + (int64_t)kc * 32;
+    const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
+    const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
+    const int gm = min((kt >> 2) + 1, (kt1 >> 2) - 1);
+    static_for<NSL>([&](auto sc) {
+      constexpr int SL = decltype(sc)::value;
+      constexpr int ks = SL / MB, i = SL % MB;
+      if constexpr (SL < A_MAX) {
+        if (SL + 1 < A_MAX || swave < EXTRA) dma_lds16_s(a_off[SL], a_step, a_dst + SL * 4096);
+      } else if constexpr (SL == 5 || SL == 6) {
+        dma_lds16_s(c_off[SL - 5], c_step, c_dst + (swave + 4 * (SL - 5)) * 1024);
+      } else if constexpr (SL == 7 && S == 0) {
+        // group kt/4 + 1 into its buffer; past the split's end the copy is
+        // clamped to the last group but still lands in the buffer no later
+        // step reads
+        issue_meta(gm, ((kt >> 2) + 1) & 1);
+      }
+      constexpr int NX = SL + 3;
+      fa[NX % RING] = NX < NSL ? a_frag(As_, NX / MB, NX % MB) : a_frag(a_st(S1{}), (NX - NSL) / MB, (NX - NSL) % MB);
+      __builtin_amdgcn_sched_barrier(0);
+      const half8_t& af = fa[SL % RING];
+      if constexpr (SL >= NSL - 8) {
+        constexpr int r = SL - (NSL - 8);
+        half8_t nb;
+        mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
+                         bcur[ks][2], bcur[ks][3], cw[r / FN][r % FN], cm[r % FN], nb);
+        bnxt[r / FN][r % FN] = nb;
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
+      }
+    });
+    if (swave < EXTRA) {
+      if constexpr (S == 0)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 3) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 2) : "memory");
+    } else {
+      if constexpr (S == 0)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 2) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 1) : "memory");
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), where the compiler sees it
+  };
+  for (int kt = kt0; kt < kt1; kt += 4) {
+    step(I0{}, kt);
+    step(I1{}, kt + 1);
+    step(I2{}, kt + 2);
+    step(I3{}, kt + 3);
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + fr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + i * 16 + 4 * fk + r;
+        if (m < M && n < N) {
+          if (partial)
+            partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
+          else
+            epilogue_store(epi, m, n, acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
                                                             int64_t N, Epilogue epi) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1951,7 +2161,14 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
   float* partial = nullptr;
   if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
   const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)splits, (unsigned)zb);
-  if (decode_four_waves()) {
+  // one wave per SIMD when the {min, scale} go 4 steps at a time; test hook:
+  // FQ_DECODE_W4=0 in the environment selects the 8-wave kernel instead
+  const char* ew = getenv("FQ_DECODE_W4");
+  if (meta4 && !(ew && ew[0] == '0') && !decode_four_waves()) {
+    gemm_decode_w4_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps,
+                                                          epi, partial);
+    FQ_TRY(launch_check("gemm_decode_w4_kernel"));
+  } else if (decode_four_waves()) {
     gemm_decode_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps, epi,
                                                        partial);
     FQ_TRY(launch_check("gemm_decode_kernel"));

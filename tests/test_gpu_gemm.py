@@ -63,26 +63,44 @@ def test_gemm_packed_shapes(M, N, K):
     _tol_check(got, ref, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("waves", ["4", "8"])
-@pytest.mark.parametrize("M", [64, 100, 144, 256])
+@pytest.mark.parametrize("waves", ["4", "8", "w4"])
+@pytest.mark.parametrize("M", [64, 90, 100, 144, 256])
 @pytest.mark.parametrize("K", [2048, 384])
 def test_gemm_decode_kernels(M, waves, K, monkeypatch):
-    """The two 4-bit decode kernels (4 waves x 64 weight rows, 8 waves x 32;
-    the library reads FQ_DECODE_WAVES at each call) over ragged N, split K;
-    K = 384 (6 steps) takes the 8-wave kernel's per-step {min, scale} copies,
-    K = 2048 the 4-step ones."""
+    """The 4-bit decode kernels (4 waves x 64 weight rows; 8 waves x 32; one
+    wave per SIMD x 64, the default where K is a multiple of 256; the library
+    reads FQ_DECODE_WAVES and FQ_DECODE_W4 at each call) over ragged N, split
+    K; K = 384 (6 steps) takes the 8-wave kernel's per-step {min, scale}
+    copies, K = 2048 the 4-step ones."""
     if waves == "4":
         monkeypatch.setenv("FQ_DECODE_WAVES", "4")
+    if waves == "8":
+        monkeypatch.setenv("FQ_DECODE_W4", "0")
     got, ref = _run(M, 1000, K, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, seed=M)
     _tol_check(got, ref, f"decode kernel waves={waves} M={M} K={K}")
+
+
+@pytest.mark.parametrize("M", [64, 90, 100, 144, 256])
+def test_gemm_decode_w4_equals_8wave(M, monkeypatch):
+    """The one-wave-per-SIMD decode kernel and the 8-wave one give lane group g
+    of k slice s the same k chunk (2 g + s) and split K alike: the same output,
+    bit for bit, at every row-block count (4, 6, 8, 9, two groups of 8)."""
+    log(f"gemm decode w4 vs 8-wave M={M}")
+    flags = fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL
+    got1, ref = _run(M, 1000, 2048, flags, seed=M)
+    monkeypatch.setenv("FQ_DECODE_W4", "0")
+    got2, _ = _run(M, 1000, 2048, flags, seed=M)
+    assert np.array_equal(got1, got2)
+    _tol_check(got1, ref, f"decode w4 M={M}")
 
 
 @pytest.mark.parametrize("M,N,K", [(144, 1000, 2048), (2100, 3900, 512)])
 def test_gemm_meta_alignment_fallback(M, N, K):
     """A {min, scale} array that is 4- but not 16-byte aligned takes the kernels
-    that copy it 4 bytes per row (the decode kernel's per-step copies, the
-    8-wave 256 x 256 kernel): the same output as the aligned array, bit for
-    bit (both paths add the same products in the same order)."""
+    that copy it 4 bytes per row (the 8-wave decode kernel's per-step copies,
+    the 8-wave 256 x 256 kernel): the same output as the aligned array (one
+    wave per SIMD kernels), bit for bit (both paths add the same products in
+    the same order)."""
     log(f"gemm meta alignment M={M} N={N} K={K}")
     a = synth.normal_f16(23, synth.STREAM["aux"] + 1, (M, K), 1.0)
     w = synth.normal_f16(23, synth.STREAM["aux"] + 2, (N, K), 0.02)
