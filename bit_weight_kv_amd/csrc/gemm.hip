@@ -2052,14 +2052,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Sum of the split-K partials ([split][M][N] fp32), in split order from
+// zero, then the epilogue: 8 columns of one row per thread, with 16-byte
+// loads when N is a multiple of 8 (every chunk whole and aligned).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
                                                             int64_t N, Epilogue epi) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * N) return;
-  float s = 0.f;
-  for (int z = 0; z < splits; ++z) s += partial[(int64_t)z * M * N + i];
-  epilogue_store(epi, i / N, i % N, s);
+  const int64_t nc = (N + 7) / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= M * nc) return;
+  const int64_t m = t / nc, n = (t - m * nc) * 8;
+  const int64_t mn = M * N;
+  const float* p = partial + m * N + n;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  if (N % 8 == 0) {
+    for (int z = 0; z < splits; ++z) {
+      const float4 a = *reinterpret_cast<const float4*>(p + z * mn);
+      const float4 b = *reinterpret_cast<const float4*>(p + z * mn + 4);
+      v[0] += a.x, v[1] += a.y, v[2] += a.z, v[3] += a.w;
+      v[4] += b.x, v[5] += b.y, v[6] += b.z, v[7] += b.w;
+    }
+  } else {
+    for (int z = 0; z < splits; ++z)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (n + k < N) v[k] += p[z * mn + k];
+  }
+  epilogue_store8(epi, m, n, v, N, epilogue_vec_ok(epi));
 }
+
+// Blocks of splitk_reduce_kernel for an M x N output.
+inline unsigned reduce_blocks(int64_t M, int64_t N) { return (unsigned)ceil_div(M * ((N + 7) / 8), 256); }
 
 // Split-K workspace, grown on demand and kept for the life of the process.
 struct Workspace {
@@ -2111,7 +2135,7 @@ fq_status run_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
                                                               partial);
   FQ_TRY(launch_check("gemm_skinny_kernel"));
   if (splits > 1) {
-    splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
+    splitk_reduce_kernel<<<dim3(reduce_blocks(M, N)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
     FQ_TRY(launch_check("splitk_reduce_kernel"));
   }
   return FQ_OK;
@@ -2182,7 +2206,7 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
     FQ_TRY(launch_check("gemm_decode8_kernel"));
   }
   if (splits > 1) {
-    splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
+    splitk_reduce_kernel<<<dim3(reduce_blocks(M, N)), dim3(256), 0, st>>>(partial, splits, M, N, epi);
     FQ_TRY(launch_check("splitk_reduce_kernel"));
   }
   return FQ_OK;
@@ -2232,7 +2256,7 @@ fq_status run_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W
                                                                epi, partial);
   FQ_TRY(launch_check("gemm_kernel"));
   if (splits > 1) {
-    splitk_reduce_kernel<<<dim3((unsigned)ceil_div(M * W->n, 256)), dim3(256), 0, st>>>(partial, splits, M, W->n, epi);
+    splitk_reduce_kernel<<<dim3(reduce_blocks(M, W->n)), dim3(256), 0, st>>>(partial, splits, M, W->n, epi);
     FQ_TRY(launch_check("splitk_reduce_kernel"));
   }
   return FQ_OK;

@@ -94,6 +94,15 @@ def test_gemm_decode_w4_equals_8wave(M, monkeypatch):
     _tol_check(got1, ref, f"decode w4 M={M}")
 
 
+@pytest.mark.parametrize("M,packed", [(5, True), (144, True), (37, False)])
+def test_gemm_splitk_ragged_n(M, packed):
+    """Split K with N not a multiple of 8: the reduction's scalar path, the
+    epilogue's ragged last chunk (bias, residual)."""
+    log(f"gemm split-K ragged N M={M} packed={packed}")
+    got, ref = _run(M, 1003, 2048, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, packed=packed, seed=M + 3)
+    _tol_check(got, ref, f"split-K ragged N M={M}")
+
+
 @pytest.mark.parametrize("M,N,K", [(144, 1000, 2048), (2100, 3900, 512)])
 def test_gemm_meta_alignment_fallback(M, N, K):
     """A {min, scale} array that is 4- but not 16-byte aligned takes the kernels
