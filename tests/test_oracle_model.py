@@ -9,7 +9,7 @@ import numpy as np
 
 import synth
 from oracle import (LayerConfig, ModelConfig, layer_params, pack_layer, new_cache, layer_step,
-                    generate, argmax_lowest, quantize, dequant_f64)
+                    generate, argmax_lowest, quantize, dequant_f64, dequant_f16)
 from oracle.model import model_params, embed, lm_head_logits
 
 CFG = LayerConfig(hidden=256, heads=4, ffn=1024)
@@ -171,3 +171,71 @@ def test_generate_matches_teacher_forced_prefill():
         lg = lm_head_logits(x[:, -1], mp["lnf_g"], mp["lnf_b"], mp["embed"])
         np.testing.assert_allclose(lg, out["logits"][t], rtol=1e-12, atol=1e-12)
         assert np.array_equal(argmax_lowest(lg), toks[:, t])
+
+
+def _torch_layer(x16, p, cfg, cache_codes, pos):
+    """The same pre-LN OPT layer assembled from torch float64 library routines
+    (F.layer_norm, F.linear over the reconstructed weights, F.relu and
+    F.scaled_dot_product_attention with its default 1/sqrt(d) scale over the
+    reconstructed cache), rounding to fp16 at the storage points the layer
+    defines.  x16 [B, T, h] at positions pos..pos+T-1; cache_codes holds the
+    quantised K/V of positions < pos and receives the new ones.  Quantisation
+    and reconstruction use the oracle's own (separately pinned) routines."""
+    import torch
+    import torch.nn.functional as F
+    B, T, h = x16.shape
+    H, d = cfg.heads, cfg.head_dim
+    # one rounding float64 -> fp16 (torch's own cast goes through float32 and
+    # can round twice)
+    f16 = lambda t: torch.from_numpy(t.numpy().astype(np.float16).astype(np.float64))
+    t64 = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    W = {n: t64(dequant_f16(*quantize(p[n]))) for n in ("w_qkv", "w_out", "w_fc1", "w_fc2")}
+    b = {n: t64(p[n].astype(np.float64)) for n in p if not n.startswith("w_")}
+    x = t64(x16.astype(np.float64))
+    h1 = f16(F.layer_norm(x, (h,), b["ln1_g"], b["ln1_b"], eps=1e-5))
+    qkv = F.linear(h1, W["w_qkv"], b["b_qkv"])
+    # The query is stored in fp16 after its d^-1/2 scaling; SDPA applies its own
+    # default scale, so it is handed the stored query in unscaled units
+    # (d is a power of four here, so the rescaling is exact).
+    c = d ** -0.5
+    q = f16(qkv[..., :h] * c) / c
+    k16 = qkv[..., h:2 * h].numpy().astype(np.float16)
+    v16 = qkv[..., 2 * h:].numpy().astype(np.float16)
+    heads = lambda a: np.ascontiguousarray(a.reshape(B, T, H, d).transpose(0, 2, 1, 3))
+    for name, a in (("k", k16), ("v", v16)):
+        cc, mm = quantize(heads(a))
+        cache_codes[name + "_codes"][:, :, pos:pos + T] = cc
+        cache_codes[name + "_meta"][:, :, pos:pos + T] = mm
+    n = pos + T
+    K = t64(dequant_f64(cache_codes["k_codes"][:, :, :n], cache_codes["k_meta"][:, :, :n]))
+    V = t64(dequant_f64(cache_codes["v_codes"][:, :, :n], cache_codes["v_meta"][:, :, :n]))
+    qh = q.reshape(B, T, H, d).transpose(1, 2)
+    mask = torch.arange(n)[None, :] <= (pos + torch.arange(T))[:, None]   # query t sees keys 0..pos+t
+    o = F.scaled_dot_product_attention(qh, K, V, attn_mask=mask)
+    o = f16(o.transpose(1, 2).reshape(B, T, h))
+    x1 = f16(x + F.linear(o, W["w_out"], b["b_out"]))
+    h2 = f16(F.layer_norm(x1, (h,), b["ln2_g"], b["ln2_b"], eps=1e-5))
+    f = f16(F.relu(F.linear(h2, W["w_fc1"], b["b_fc1"])))
+    return (x1 + F.linear(f, W["w_fc2"], b["b_fc2"])).numpy()
+
+
+def test_layer_step_against_torch_float64_layer():
+    """The oracle's layer (prefill of 12 tokens, then two decode steps) equals
+    the layer assembled from torch float64 routines -- LayerNorm, linear, ReLU
+    and scaled-dot-product attention with torch's default 1/sqrt(d) scale --
+    before the final rounding, with non-zero biases and non-unit LayerNorm
+    gains so that every term reaches the output.  This fixes the query scale
+    (d^-1/2), the ReLU, and where LN1 and LN2 sit (pre-LN on x and on x1)."""
+    B, P, T = 3, 12, 2
+    p = layer_params(7, CFG, 0, bias_sigma=0.02)
+    pk = pack_layer(p, CFG)
+    x = _x(B, P + T, 256, seed=7)
+    c_or = new_cache(CFG, B, P + T)
+    c_tr = new_cache(CFG, B, P + T)
+    steps = [(0, P)] + [(P + t, 1) for t in range(T)]
+    for pos, n in steps:
+        got = layer_step(x[:, pos:pos + n], p, pk, c_or, CFG, pos)["y64"]
+        ref = _torch_layer(x[:, pos:pos + n], p, CFG, c_tr, pos)
+        assert np.max(np.abs(got - ref)) <= 1e-12, f"step at {pos}: {np.max(np.abs(got - ref))}"
+        for key in c_or:
+            assert np.array_equal(c_or[key], c_tr[key])
