@@ -13,10 +13,17 @@ FFN 49152, vocab 50272) with 4-bit group-64 weights and 4-bit KV resident on
 one MI355X, batch 144, prompt 512, gen 32 -- the configuration of the pages'
 "FlexGen with Compression" OPT-175B figure (effective batch 144).
 
-Prints one JSON line.  Also measures, live over the timed region, the
-per-launch device time of every kernel class (HIP events on the launching
-stream) and reports the dominant kernel against its roofline, and times the
-CPU oracle on a bounded sample of the same workload on the host cores.
+Single-layer workloads (--config tiny-layer, opt6.7b-layer): one OPT-style
+layer over a batch of seeded hidden states, prefill of the prompt then T
+teacher-forced decode steps; throughput is the per-layer form of the same
+metric, B*T / (layer prefill + T decode steps).
+
+Prints one JSON line.  The warmup steps record every kernel launch's device
+time (HIP events on the launching stream) for the per-class kernel table;
+the timed steps record only the launches of the dominant kernel class, whose
+average launch time gives the roofline figure.  The CPU oracle is timed on
+the host cores: on a bounded sample of a full-model workload, or in full for
+the single-layer workloads.
 """
 import argparse
 import json
@@ -54,11 +61,18 @@ CONFIGS = {
                                                 "cache (2 bytes per element: 123 GB at batch 48), all in HBM"),
     "tiny-2layer": dict(hidden=256, heads=4, ffn=1024, layers=2, vocab=512, batch=8, prompt=64, gen=5,
                         compress_weight=True, desc="tiny OPT-style model for smoke benchmarking"),
+    "tiny-layer": dict(hidden=256, heads=4, ffn=1024, layers=1, vocab=0, batch=8, prompt=64, gen=4,
+                       compress_weight=True, layer_only=True,
+                       desc="tiny OPT-style layer (hidden 256, 4 heads x 64, FFN 1024), 4-bit g64 weights + 4-bit "
+                            "KV, batch 8, prompt 64, 4 teacher-forced decode steps"),
+    "opt6.7b-layer": dict(hidden=4096, heads=32, ffn=16384, layers=1, vocab=0, batch=64, prompt=512, gen=32,
+                          compress_weight=True, layer_only=True,
+                          desc="one OPT-6.7B-shaped layer (hidden 4096, 32 heads x 128, FFN 16384), 4-bit g64 "
+                               "weights + 4-bit KV, batch 64, prompt 512, 32 teacher-forced decode steps"),
 }
 METRIC = "generation tokens/s (prompt 512, gen 32) at batch 144-256; % HBM/MFMA roofline"
 PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak (published)
-PAGES_T4_TOKS = {"opt175b-4bit": 1.12}  # FlexGen with Compression, OPT-175B, T4 (context, other hardware)
 
 
 def log(msg):
@@ -81,7 +95,8 @@ def parse():
     ap.add_argument("--ceilings", action="store_true",
                     help="measure this GPU's practical ceilings (HBM copy stream, pinned host<->device copies, "
                          "the vendor library's fp16 GEMM at the prefill shape) and print them as one JSON line")
-    ap.add_argument("--kernel-only", choices=["gemm_prefill", "gemm_decode", "decode_attention"], default=None,
+    ap.add_argument("--kernel-only", choices=["gemm_prefill", "gemm_decode", "decode_attention", "prefill_attention",
+                                              "quantize"], default=None,
                     help="launch only this kernel class, as one layer of the workload launches it (a short program "
                          "for hardware-counter passes); prints the launch list instead of the JSON line")
     return ap.parse_args()
@@ -117,13 +132,13 @@ def measured_traffic(kernel):
     return int(t.group(1))
 
 
-def roofline(kstats, config):
-    """Dominant kernel class by device time, against its own roofline."""
-    name, st = max(kstats.items(), key=lambda kv: kv[1]["seconds"])
-    if st["seconds"] <= 0:
-        return None, {}
+def roofline(name, st, config):
+    """One kernel class's launches against that kernel's own roofline: algorithmic
+    work per launch / average launch duration."""
+    if not st or st["launches"] == 0 or st["seconds"] <= 0:
+        return None
     per_launch_s = st["seconds"] / st["launches"]
-    if name.startswith("gemm") or name == "lm_head":
+    if name.startswith("gemm") or name in ("lm_head", "prefill_attention"):
         achieved = st["flops"] / st["seconds"] / 1e12
         r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
              "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None}
@@ -137,7 +152,7 @@ def roofline(kstats, config):
     r["launches"] = st["launches"]
     r["avg_launch_ms"] = round(per_launch_s * 1e3, 4)
     r["work_per_launch"] = (st["flops"] if r["bound"] == "mfma" else st["bytes"]) / st["launches"]
-    return name, r
+    return r
 
 
 def kernel_table(kstats, config):
@@ -153,6 +168,8 @@ def kernel_table(kstats, config):
         if st["bytes"] > 0:
             e["gbs"] = round(st["bytes"] / st["seconds"] / 1e9, 1)
             e["hbm_frac"] = round(st["bytes"] / st["seconds"] / 1e9 / PEAK_HBM_GBS, 4)
+        if st.get("dropped"):
+            e["untimed_launches"] = st["dropped"]
         if config == "opt175b-4bit":
             t = measured_traffic(name)
             if t is not None:
@@ -161,84 +178,88 @@ def kernel_table(kstats, config):
     return out
 
 
-def cpu_baseline(cfg, seed):
-    """The CPU oracle on a bounded sample of the same workload: three sequences
-    through one layer of this shape -- prefill of the 512-token prompt, then the
-    31 decode steps -- timed on the host cores, scaled to the full workload
-    (every layer costs the same; cost is linear in the batch):
-    tokens/s = 3 * gen / (t * layers)."""
-    import numpy as np
-    from concurrent.futures import ThreadPoolExecutor
-
-    import oracle
-    import synth
-    from synth.gen import layer_stream
-
+def host_description():
+    """The host the oracle runs on: logical CPUs, the ones this process may use,
+    the CPU model, and the BLAS threads NumPy runs with."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        cores = min(16, os.cpu_count() or 1)
-    h, H, F = cfg["hidden"], cfg["heads"], cfg["ffn"]
-    lcfg = oracle.LayerConfig(h, H, F, compress_weight=cfg["compress_weight"],
+        blas = None
+    return {"nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "blas_threads": blas}
+
+
+def _oracle_layer_params(cfg, seed, workers):
+    """The oracle's layer 0 of this shape: seeded fp16 parameters (OPT-style init:
+    biases 0, LayerNorm gain 1) and the weights as the GEMMs read them."""
+    import oracle
+    lcfg = oracle.LayerConfig(cfg["hidden"], cfg["heads"], cfg["ffn"], compress_weight=cfg["compress_weight"],
                               compress_cache=cfg.get("compress_cache", True))
+    params = oracle.layer_params(seed, lcfg, 0, workers=workers)
+    return lcfg, params, oracle.pack_layer(params, lcfg, workers=workers)
+
+
+def _oracle_layer_run(lcfg, params, packed, x, P, T):
+    """Prefill of P tokens then T single-token steps of one layer; seconds taken."""
+    import oracle
+    cache = oracle.new_cache(lcfg, x.shape[0], P + T)
+    t = time.time()
+    oracle.layer_step(x[:, :P], params, packed, cache, lcfg, 0)
+    for i in range(T):
+        oracle.layer_step(x[:, P + i:P + i + 1], params, packed, cache, lcfg, P + i)
+    return time.time() - t
+
+
+def cpu_baseline(cfg, seed):
+    """The CPU oracle on the host cores.
+
+    Full-model workloads: a bounded sample -- three sequences through one layer
+    of this shape, prefill of the prompt and the gen-1 decode steps -- scaled to
+    the whole model (every layer costs the same; cost is linear in the batch):
+    tokens/s = 3 * gen / (t * layers).  Single-layer workloads: the whole
+    workload (every sequence, prefill and every decode step), and for the tiny
+    layer also on one thread."""
+    import synth
     workers = min(16, os.cpu_count() or 1)  # the host share of one GPU
     t0 = time.time()
-
-    def gen(name, shape, sigma):
-        n = int(np.prod(shape))
-        out = np.empty(n, np.float16)
-        step = max(1 << 22, n // (4 * workers) + 1)
-
-        def part(s):
-            e = min(n, s + step)
-            out[s:e] = synth.normal_f16(seed, layer_stream(0, name), sigma=sigma,
-                                        index=np.arange(s, e, dtype=np.uint64))
-        with ThreadPoolExecutor(workers) as ex:
-            list(ex.map(part, range(0, n, step)))
-        return out.reshape(shape)
-
-    params = {"w_qkv": gen("w_qkv", (3 * h, h), 0.02), "w_out": gen("w_out", (h, h), 0.02),
-              "w_fc1": gen("w_fc1", (F, h), 0.02), "w_fc2": gen("w_fc2", (h, F), 0.02)}
-    for name, n in (("b_qkv", 3 * h), ("b_out", h), ("b_fc1", F), ("b_fc2", h)):
-        params[name] = np.zeros(n, np.float16)
-    for name in ("ln1_g", "ln2_g"):
-        params[name] = np.ones(h, np.float16)
-    for name in ("ln1_b", "ln2_b"):
-        params[name] = np.zeros(h, np.float16)
-    # load-time weight packing (not part of the metric), row blocks in parallel
-    packed = {}
-    for name in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
-        w = params[name]
-        if not lcfg.compress_weight:
-            packed[name] = w.astype(np.float64)
-            continue
-        out = np.empty(w.shape, np.float64)
-        rows = max(64, w.shape[0] // (4 * workers))
-
-        def part(r0, w=w, out=out):
-            c, m = oracle.quantize(w[r0:r0 + rows])
-            out[r0:r0 + rows] = oracle.dequant_f16(c, m)
-        with ThreadPoolExecutor(workers) as ex:
-            list(ex.map(part, range(0, w.shape[0], rows)))
-        packed[name] = out
+    lcfg, params, packed = _oracle_layer_params(cfg, seed, workers)
     setup_s = time.time() - t0
-    P, G = cfg["prompt"], cfg["gen"]
+    h, P, G = cfg["hidden"], cfg["prompt"], cfg["gen"]
+    hostd = host_description()
+    if cfg.get("layer_only"):
+        B, T = cfg["batch"], G
+        x = synth.normal_f16(seed, synth.STREAM["hidden"], (B, P + T, h), 1.0)
+        t = _oracle_layer_run(lcfg, params, packed, x, P, T)
+        r = {"value": B * T / t, "unit": "tokens/s", "cores": hostd["blas_threads"], "kind": "oracle",
+             "sample": f"the whole workload: {B} sequences, prefill of {P} tokens + {T} decode steps of the layer, "
+                       f"{t:.2f} s on the host; tokens/s = B*T/t; weight generation and packing ({setup_s:.0f} s, "
+                       f"load-time) not timed",
+             "sample_seconds": round(t, 3), "host": hostd}
+        if B * (P + T) * h <= (1 << 22):  # small enough to repeat on one thread
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                t1 = _oracle_layer_run(lcfg, params, packed, x, P, T)
+            r["single_thread"] = {"value": B * T / t1, "sample_seconds": round(t1, 3), "cores": 1}
+        return r
     S = 3  # sequences in the sample (about 10-15 s of host time at the OPT-175B shape)
     x = synth.normal_f16(seed, synth.STREAM["hidden"], (S, P + G - 1, h), 1.0)
-    cache = oracle.new_cache(lcfg, S, P + G)
-    t1 = time.time()
-    oracle.layer_step(x[:, :P], params, packed, cache, lcfg, 0)
-    for t in range(G - 1):
-        oracle.layer_step(x[:, P + t:P + t + 1], params, packed, cache, lcfg, P + t)
-    t_sample = time.time() - t1
-    value = S * G / (t_sample * cfg["layers"])
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    t = _oracle_layer_run(lcfg, params, packed, x, P, G - 1)
+    value = S * G / (t * cfg["layers"])
+    return {"value": value, "unit": "tokens/s", "cores": hostd["blas_threads"], "kind": "oracle",
             "sample": f"{S} sequences x 1 layer of the {cfg['desc']} shape: prefill of {P} tokens + {G - 1} decode "
-                      f"steps, {t_sample:.1f} s on the host; scaled to the {cfg['layers']}-layer model (every layer "
+                      f"steps, {t:.1f} s on the host; scaled to the {cfg['layers']}-layer model (every layer "
                       f"costs the same, and the oracle's cost is linear in the batch): tokens/s = "
                       f"{S}*gen/(t*layers); weight generation and packing ({setup_s:.0f} s, load-time) not timed",
-            "sample_seconds": round(t_sample, 2)}
+            "sample_seconds": round(t, 2), "host": hostd}
 
 
 def ceilings(torch):
@@ -283,7 +304,50 @@ def kernel_only(fq, synth, torch, cfg, args):
         return kernel_only_gemm(fq, synth, torch, cfg, args, prefill=True)
     if args.kernel_only == "gemm_decode":
         return kernel_only_gemm(fq, synth, torch, cfg, args, prefill=False)
+    if args.kernel_only == "quantize":
+        return kernel_only_quantize(fq, synth, torch, cfg, args)
+    if args.kernel_only == "prefill_attention":
+        return kernel_only_prefill_attention(fq, synth, torch, cfg, args)
     return kernel_only_decode_attention(fq, synth, torch, cfg, args)
+
+
+def kernel_only_quantize(fq, synth, torch, cfg, args):
+    """Load-time quantisation of the largest weight of a layer (FC1, [ffn, hidden]
+    fp16 ~ N(0, 0.02) from the seeded generator), three launches."""
+    n, k = cfg["ffn"], cfg["hidden"]
+    w = torch.empty((n, k), dtype=torch.float16, device="cuda")
+    from synth.gen import layer_stream
+    fq.fq_synth_normal_f16(w, args.seed, layer_stream(0, "w_fc1"), 0.02)
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        fq.fq_quantize(w, codes, meta.view(torch.int16))
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": args.kernel_only, "launches": [[n, k]] * 3}), flush=True)
+
+
+def kernel_only_prefill_attention(fq, synth, torch, cfg, args):
+    """Causal attention of one prompt chunk as the prefill launches it: the
+    sequences of one --max-tokens chunk x all heads x the prompt, over a packed
+    cache (seeded random codes; the {min, scale} pairs are constant) -- three
+    launches."""
+    h, H, P, G = cfg["hidden"], cfg["heads"], cfg["prompt"], cfg["gen"]
+    d, S = h // H, P + G - 1
+    B = max(1, min(cfg["batch"], args.max_tokens // P))
+    gen = torch.Generator(device="cuda").manual_seed(args.seed)
+    kc = torch.randint(0, 256, (B, H, S, d // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    vc = torch.randint(0, 256, (B, H, S, d // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    km = torch.empty((B, H, S, d // 64, 2), dtype=torch.float16, device="cuda")
+    km[..., 0], km[..., 1] = -0.05, 0.006
+    vm = km.clone()
+    kv = fq.kv_layer_view(kc, km.view(torch.int16), vc, vm.view(torch.int16))
+    q = torch.empty((B * P, 3 * h), dtype=torch.float16, device="cuda")
+    fq.fq_synth_normal_f16(q, args.seed, synth.STREAM["aux"], 1.0)
+    out = torch.empty((B * P, h), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        fq.fq_prefill_attention(q, kv, 0, B, P, 0, out, ldq=3 * h)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": args.kernel_only, "launches": [[B, H, P, d]] * 3}), flush=True)
 
 
 def kernel_only_decode_attention(fq, synth, torch, cfg, args):
@@ -360,6 +424,80 @@ def kernel_only_gemm(fq, synth, torch, cfg, args, prefill):
     print(json.dumps({"kernel_only": args.kernel_only, "launches": [list(t) for t in launches]}), flush=True)
 
 
+class GenerationRun:
+    """One step = one greedy generation of the workload (fq_generate)."""
+
+    def __init__(self, fq, synth, torch, cfg, args):
+        self.fq, self.cfg = fq, cfg
+        B, P, G = cfg["batch"], cfg["prompt"], cfg["gen"]
+        self.model = fq.Model(cfg["hidden"], cfg["heads"], cfg["ffn"], cfg["layers"], vocab=cfg["vocab"],
+                              max_pos=P + G + 2, compress_weight=cfg["compress_weight"],
+                              resident_layers=cfg.get("resident_layers", -1), host_layers=cfg.get("host_layers", 0),
+                              overlap=True, max_tokens=args.max_tokens, compress_cache=cfg.get("compress_cache", True),
+                              cache_resident_layers=cfg.get("cache_resident_layers", -1))
+        self.model.init_random(args.seed)
+        self.kv = fq.KVCache(self.model, B, P + G)
+        self.ids = synth.token_ids(args.seed, synth.STREAM["prompt"], (B, P), cfg["vocab"])
+        self.tokens = B * G
+        last = [time.time()]
+
+        def progress(done, total):  # generations of several minutes report a completed token every ~20 s
+            if time.time() - last[0] > 20 or done == 1 and time.time() - last[0] > 5:
+                log(f"[bench] token {done}/{total} done")
+                last[0] = time.time()
+
+        fq.fq_set_progress(progress)
+
+    def step(self):
+        _, st = self.fq.fq_generate(self.model, self.kv, self.ids, self.cfg["gen"])
+        return {"prefill_s": st.prefill_s, "decode_s": st.decode_s, "h2d_bytes": st.h2d_bytes, "h2d_s": st.h2d_s,
+                "kv_h2d_bytes": st.kv_h2d_bytes, "kv_d2h_bytes": st.kv_d2h_bytes}
+
+    def close(self):
+        self.fq.fq_set_progress(None)
+        self.kv.close()
+        self.model.close()
+
+
+class LayerRun:
+    """One step = one layer over the batch: prefill of the prompt (all sequences in
+    one call), then `gen` decode steps, each consuming the next seeded hidden state
+    of every sequence (teacher-forced).  Timed with HIP events on the stream the
+    layer runs on."""
+
+    def __init__(self, fq, synth, torch, cfg, args):
+        self.fq, self.torch, self.cfg = fq, torch, cfg
+        B, P, T, h = cfg["batch"], cfg["prompt"], cfg["gen"], cfg["hidden"]
+        self.model = fq.Model(h, cfg["heads"], cfg["ffn"], 1, compress_weight=cfg["compress_weight"],
+                              max_tokens=B * P, compress_cache=cfg.get("compress_cache", True))
+        self.model.init_random(args.seed)
+        self.kv = fq.KVCache(self.model, B, P + T)
+        hidden = torch.empty((B, P + T, h), dtype=torch.float16, device="cuda")
+        fq.fq_synth_normal_f16(hidden, args.seed, synth.STREAM["hidden"], 1.0)
+        self.x = hidden[:, :P].reshape(B * P, h).contiguous()
+        self.xt = [hidden[:, P + t].contiguous() for t in range(T)]
+        self.y = torch.empty_like(self.x)
+        self.yt = torch.empty_like(self.xt[0])
+        self.tokens = B * T
+
+    def step(self):
+        torch, fq, c = self.torch, self.fq, self.cfg
+        B, P, T = c["batch"], c["prompt"], c["gen"]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        fq.fq_layer_step(self.model, 0, self.kv, 0, B, P, 0, self.x, self.y)
+        ev[1].record()
+        for t in range(T):
+            fq.fq_layer_step(self.model, 0, self.kv, 0, B, 1, P + t, self.xt[t], self.yt)
+        ev[2].record()
+        ev[2].synchronize()
+        return {"prefill_s": ev[0].elapsed_time(ev[1]) / 1e3, "decode_s": ev[1].elapsed_time(ev[2]) / 1e3}
+
+    def close(self):
+        self.kv.close()
+        self.model.close()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -394,66 +532,61 @@ def main():
     if args.kernel_only:
         kernel_only(fq, synth, torch, cfg, args)
         return
-    B, P, G = cfg["batch"], cfg["prompt"], cfg["gen"]
     t0 = time.time()
-    model = fq.Model(cfg["hidden"], cfg["heads"], cfg["ffn"], cfg["layers"], vocab=cfg["vocab"], max_pos=P + G + 2,
-                     compress_weight=cfg["compress_weight"], resident_layers=cfg.get("resident_layers", -1),
-                     host_layers=cfg.get("host_layers", 0), overlap=True, max_tokens=args.max_tokens,
-                     compress_cache=cfg.get("compress_cache", True),
-                     cache_resident_layers=cfg.get("cache_resident_layers", -1))
-    model.init_random(args.seed)
-    kv = fq.KVCache(model, B, P + G)
-    last = [time.time()]
-
-    def progress(done, total):  # generations of several minutes report each completed token every ~20 s
-        if time.time() - last[0] > 20 or done == 1 and time.time() - last[0] > 5:
-            log(f"[bench] token {done}/{total} done")
-            last[0] = time.time()
-
-    fq.fq_set_progress(progress)
-    ids = synth.token_ids(args.seed, synth.STREAM["prompt"], (B, P), cfg["vocab"])
+    run = (LayerRun if cfg.get("layer_only") else GenerationRun)(fq, synth, torch, cfg, args)
     torch.cuda.synchronize()
     log(f"[bench] {args.config}: model + cache ready in {time.time() - t0:.1f} s")
+    # warmup steps: every launch timed (the per-class table comes from the last one)
+    table = None
     for w in range(args.warmup):
-        out, st = fq.fq_generate(model, kv, ids, G)
-        log(f"[bench] warmup {w}: {st.tokens_per_s:.2f} tok/s (prefill {st.prefill_s:.2f} s, decode {st.decode_s:.2f} s)")
+        fq.fq_timing_start()
+        st = run.step()
+        table = fq.fq_timing_stop()
+        log(f"[bench] warmup {w}: {run.tokens / (st['prefill_s'] + st['decode_s']):.2f} tok/s "
+            f"(prefill {st['prefill_s']:.3f} s, decode {st['decode_s']:.3f} s)")
+    # timed steps: only the dominant class's launches carry events
+    dominant = max(table.items(), key=lambda kv: kv[1]["seconds"])[0] if table else "gemm_prefill"
     torch.cuda.synchronize()
-    fq.fq_timing_start()
+    fq.fq_timing_start([dominant])
     stats = []
     t_start = time.perf_counter()
-    for s in range(args.steps):
-        out, st = fq.fq_generate(model, kv, ids, G)
-        stats.append((st.prefill_s, st.decode_s, st.h2d_bytes, st.h2d_s, st.kv_h2d_bytes, st.kv_d2h_bytes))
-        log(f"[bench] step {s}: {st.tokens_per_s:.2f} tok/s (prefill {st.prefill_s:.2f} s, decode {st.decode_s:.2f} s)")
+    for s_ in range(args.steps):
+        st = run.step()
+        stats.append(st)
+        log(f"[bench] step {s_}: {run.tokens / (st['prefill_s'] + st['decode_s']):.2f} tok/s "
+            f"(prefill {st['prefill_s']:.3f} s, decode {st['decode_s']:.3f} s)")
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     kstats = fq.fq_timing_stop()
     ms_per_step = t_total / args.steps * 1e3
-    value = B * G * args.steps / t_total
-    _, roof = roofline(kstats, args.config)
+    value = run.tokens * args.steps / t_total
+    mean = lambda k: float(np.mean([st[k] for st in stats]))
+    phases = {"prefill_s": round(mean("prefill_s"), 4), "decode_s": round(mean("decode_s"), 4)}
+    if not cfg.get("layer_only"):
+        phases.update({"h2d_GB": round(mean("h2d_bytes") / 1e9, 2), "h2d_busy_s": round(mean("h2d_s"), 3),
+                       "kv_h2d_GB": round(mean("kv_h2d_bytes") / 1e9, 2),
+                       "kv_d2h_GB": round(mean("kv_d2h_bytes") / 1e9, 2)})
+    c = cfg
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 1), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": (round(value / PAGES_T4_TOKS[args.config], 1) if args.config in PAGES_T4_TOKS else None),
-        "dtype": "f16", "data": "synthetic (seeded random-init weights and uniform prompt ids)",
-        "config": {"workload": cfg["desc"], "config": args.config, "layers": cfg["layers"], "hidden": cfg["hidden"],
-                   "heads": cfg["heads"], "ffn": cfg["ffn"], "vocab": cfg["vocab"], "global_batch": B,
-                   "prompt": P, "gen": G, "group": 64, "parallelism": "single GPU"},
-        "phases": {"prefill_s": round(float(np.mean([s[0] for s in stats])), 3),
-                   "decode_s": round(float(np.mean([s[1] for s in stats])), 3),
-                   "h2d_GB": round(float(np.mean([s[2] for s in stats])) / 1e9, 2),
-                   "h2d_busy_s": round(float(np.mean([s[3] for s in stats])), 3),
-                   "kv_h2d_GB": round(float(np.mean([s[4] for s in stats])) / 1e9, 2),
-                   "kv_d2h_GB": round(float(np.mean([s[5] for s in stats])) / 1e9, 2)},
-        "roofline": roof,
-        "kernels": kernel_table(kstats, args.config),
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic (seeded random-init weights, uniform prompt ids / seeded hidden states)",
+        "config": {"workload": c["desc"], "config": args.config, "layers": c["layers"], "hidden": c["hidden"],
+                   "heads": c["heads"], "ffn": c["ffn"], "vocab": c["vocab"], "global_batch": c["batch"],
+                   "prompt": c["prompt"], ("decode_steps" if c.get("layer_only") else "gen"): c["gen"], "group": 64,
+                   "parallelism": "single GPU"},
+        "phases": phases,
+        "roofline": roofline(dominant, kstats.get(dominant), args.config),
+        "kernels": kernel_table(table, args.config) if table else None,
     }
-    kv.close()
-    model.close()
-    del kv, model
+    if c.get("layer_only"):
+        res["metric_form"] = "per layer: B*T / (layer prefill + T decode steps)"
+    run.close()
+    del run
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle sample")
+        log("[bench] timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(cfg, args.seed)
     print(json.dumps(res), flush=True)
 
