@@ -62,8 +62,13 @@ class fq_layer_weights(ctypes.Structure):
                                     "ln1_g", "ln1_b", "ln2_g", "ln2_b")]
 
 
+class fq_capture(ctypes.Structure):
+    _fields_ = [("layer", c_i32), ("b0", c_i64), ("nb", c_i64), ("capacity", c_i64), ("x_in", c_vp),
+                ("y_out", c_vp), ("k16", c_vp), ("v16", c_vp), ("x1", c_vp)]
+
+
 class fq_kernel_stats(ctypes.Structure):
-    _fields_ = [("launches", c_i64), ("seconds", c_f64), ("flops", c_f64), ("bytes", c_f64)]
+    _fields_ = [("launches", c_i64), ("seconds", c_f64), ("flops", c_f64), ("bytes", c_f64), ("dropped", c_i64)]
 
 
 KERNEL_CLASSES = ("gemm_prefill", "gemm_decode", "lm_head", "decode_attention", "prefill_attention", "kv_append",
@@ -95,6 +100,7 @@ _SIGS = {
     "fq_model_set_embeddings": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "fq_model_init_random": (c_i32, [c_vp, c_u64, c_f64, c_vp]),
     "fq_model_packed_weight": (c_i32, [c_vp, c_i32, c_i32, _P(fq_packed)]),
+    "fq_model_set_capture": (c_i32, [c_vp, _P(fq_capture), c_i32]),
     "fq_kv_create": (c_i32, [c_vp, c_i64, c_i64, _P(c_vp)]),
     "fq_kv_destroy": (c_i32, [c_vp]),
     "fq_kv_layer_view": (c_i32, [c_vp, c_i32, _P(fq_kv_layer)]),
@@ -103,7 +109,7 @@ _SIGS = {
     "fq_synth_normal_f16": (c_i32, [c_vp, c_i64, c_u64, c_u64, c_i64, c_f64, c_vp]),
     "fq_synth_token_ids": (c_i32, [c_vp, c_i64, c_u64, c_u64, c_i32, c_vp]),
     "fq_set_progress": (None, [c_vp, c_vp]),
-    "fq_timing_start": (c_i32, []),
+    "fq_timing_start": (c_i32, [c_u32]),
     "fq_timing_stop": (c_i32, [_P(fq_kernel_stats)]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -228,16 +234,21 @@ def fq_synth_token_ids(dst, seed, stream_id, vocab, stream=None):
     _check(_lib.fq_synth_token_ids(_ptr(dst), dst.numel(), seed, stream_id, vocab, _stream(stream)))
 
 
-def fq_timing_start():
-    _check(_lib.fq_timing_start())
+FQ_KC_ALL = 0xFF
+
+
+def fq_timing_start(classes=None):
+    """Record the launches of the named kernel classes (None: every class)."""
+    mask = FQ_KC_ALL if classes is None else sum(1 << KERNEL_CLASSES.index(c) for c in classes)
+    _check(_lib.fq_timing_start(mask))
 
 
 def fq_timing_stop():
-    """Returns {class name: dict(launches, seconds, flops, bytes)}."""
+    """Returns {class name: dict(launches, seconds, flops, bytes, dropped)}."""
     arr = (fq_kernel_stats * len(KERNEL_CLASSES))()
     _check(_lib.fq_timing_stop(arr))
     return {n: {"launches": arr[i].launches, "seconds": arr[i].seconds, "flops": arr[i].flops,
-                "bytes": arr[i].bytes} for i, n in enumerate(KERNEL_CLASSES)}
+                "bytes": arr[i].bytes, "dropped": arr[i].dropped} for i, n in enumerate(KERNEL_CLASSES)}
 
 
 class Model:
@@ -274,6 +285,18 @@ class Model:
     def set_embeddings(self, embed, pos, lnf_g, lnf_b, stream=None):
         _check(_lib.fq_model_set_embeddings(self.handle, _ptr(embed), _ptr(pos), _ptr(lnf_g), _ptr(lnf_b),
                                             _stream(stream)))
+
+    def set_capture(self, captures):
+        """captures: list of dict(layer, b0, nb, capacity, x_in, y_out, k16, v16, x1) with device fp16
+        tensors [nb, capacity, hidden] (or None) -- see fq_model_set_capture.  [] clears."""
+        arr = (fq_capture * max(1, len(captures)))()
+        keep = []
+        for i, c in enumerate(captures):
+            arr[i] = fq_capture(c["layer"], c["b0"], c["nb"], c["capacity"],
+                                *[_ptr(c.get(n)) for n in ("x_in", "y_out", "k16", "v16", "x1")])
+            keep += [c.get(n) for n in ("x_in", "y_out", "k16", "v16", "x1")]
+        _check(_lib.fq_model_set_capture(self.handle, arr if captures else None, len(captures)))
+        self._capture_keep = keep
 
     def packed_weight(self, layer, which):
         p = fq_packed()

@@ -425,11 +425,17 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* 
 
 // ---- causal prefill on the matrix cores ------------------------------------
 // Work-group = 4 waves x 32 queries of one (b, h); keys in chunks of 64.
-// Per chunk the work-group reconstructs K and V of 64 positions into LDS as
-// fp16 (fp16(min + code * s), one rounding), then each wave computes
+// Per chunk the work-group stages K and V of 64 positions in LDS as fp16,
+// then each wave computes
 //   S^T = K^ Q^T      (v_mfma_f32_16x16x32_f16; lane owns query lane % 16)
 //   online softmax    (per query, reduced over the 4 lane groups)
 //   O^T += V^T P^T    (P taken straight from the S^T registers)
+// With the 4-bit cache each reconstructed key k = min + code * s (exact in
+// fp32) is staged as two fp16 arrays, hi = fp16(k) and lo = fp16(k - hi), and
+// S^T accumulates the products with both: the scores carry the key to about
+// 22 bits instead of fp16's 11 (rounding k itself to fp16 was the largest
+// error of the layer at the OPT-175B shape).  V is staged the same way, as
+// hi and lo arrays, and O^T accumulates the products with both.
 // Transposing both products keeps every per-query value (scores, running
 // max/sum, output column) in the lanes of that query, so P never moves.
 // V is stored transposed ([d][position]) with the positions of each 32-wide
@@ -448,7 +454,9 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   constexpr int G = D / 64;        // quantisation groups per position
   constexpr int KHALF = D / 64;    // K stored as D/64 arrays of 64 d (128-byte rows)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[KHALF][KC * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t klo_lds[F16 ? 1 : KHALF][F16 ? 8 : KC * 64];  // 4-bit: k - hi
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t vlo_lds[F16 ? 8 : D * KC];  // 4-bit: v - hi
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -474,98 +482,104 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   constexpr float kL2e = 1.4426950408889634f;
 
+  // Staging: every thread stages part of K and part of V of each chunk.
+  //   K: key tid / 4, channels (tid % 4) * D/4 .. + D/4 - 1 (D/32 code words);
+  //   V: channels 8 * (tid / 16) .. + 7 of the 4 positions of quad tid % 16
+  //      (two quads make one 8-position storage chunk in slice order).
   // 4-bit cache: the raw codes and {min, scale} of the next chunk are loaded
   // into registers before the current chunk's products, so their latency
   // hides behind them; they are converted and stored at the next chunk's
-  // start.  K: thread -> (position tid / 2, half tid % 2: D/16 code words and
-  // one {min, scale}); V: thread -> (8 positions of storage chunk pc, channel
-  // word dc: one code word and one {min, scale} per position).
-  uint32_t rk[D / 16], rkm = 0, rv[8], rvm[8];
+  // start.
+  constexpr int KW = D / 32;  // K code words (8 channels each) per thread
+  const int kkey = tid >> 2, kq = tid & 3;
+  const int vdc = tid >> 4, vpq = tid & 15;
+  const int vpc = vpq >> 1, vhalf = vpq & 1;  // storage chunk, its first or second 4 positions
+  const bool vact = vdc < D / 8;
+  auto vkey = [&](int jj) { return (vpc >> 2) * 32 + vhalf * 16 + 4 * (vpc & 3) + jj; };
+  uint32_t rk[KW], rkm = 0, rv[4], rvm[4];
   auto load_raw = [&](int64_t k0) {
     if constexpr (!F16) {
-      if (tid < 128) {
-        const int key = tid >> 1, hf = tid & 1;
-        const int64_t j = min(k0 + key, nkeys - 1);
-        const uint32_t* cw = reinterpret_cast<const uint32_t*>(kc + (row0 + j) * (D / 2));
+      const int64_t j = min(k0 + kkey, nkeys - 1);
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(kc + (row0 + j) * (D / 2)) + kq * KW;
 #pragma unroll
-        for (int w = 0; w < D / 16; ++w) rk[w] = cw[hf * (D / 16) + w];
-        rkm = reinterpret_cast<const uint32_t*>(km)[(row0 + j) * G + hf * (D / 16) * 8 / 64];
-      } else {
-        const int u = tid - 128, pc = u & 7, dc = u >> 3;
-        if (dc < D / 8) {
-          const int sl = pc >> 2, qq = pc & 3;
+      for (int w = 0; w < KW; ++w) rk[w] = cw[w];
+      rkm = reinterpret_cast<const uint32_t*>(km)[(row0 + j) * G + (kq * KW * 8) / 64];
+      if (vact) {
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
-            const int64_t j = min(k0 + key, nkeys - 1);
-            rv[jj] = reinterpret_cast<const uint32_t*>(vc + (row0 + j) * (D / 2))[dc];
-            rvm[jj] = reinterpret_cast<const uint32_t*>(vm)[(row0 + j) * G + dc / 8];
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          const int64_t jv = min(k0 + vkey(jj), nkeys - 1);
+          rv[jj] = reinterpret_cast<const uint32_t*>(vc + (row0 + jv) * (D / 2))[vdc];
+          rvm[jj] = reinterpret_cast<const uint32_t*>(vm)[(row0 + jv) * G + vdc / 8];
         }
       }
+    }
+  };
+  // 8 codes (one word) with their {min, scale} -> hi = fp16(min + c * s) and
+  // lo = fp16((min + c * s) - hi), 4 packed pairs each; min + c * s is exact
+  // in fp32 (a 4-bit code times an 11-bit scale), and so is the difference.
+  auto hilo8 = [](uint32_t w, uint32_t mb, uint32_t hi[4], uint32_t lo[4]) {
+    const float mnf = (float)__builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
+    const float scf = (float)__builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
+    half2_t c[4];
+    codes8_cvt(w, c);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      half2_t h2, l2;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float v = __builtin_fmaf((float)c[pp][e], scf, mnf);
+        h2[e] = (half_t)v;
+        l2[e] = (half_t)(v - (float)h2[e]);
+      }
+      hi[pp] = __builtin_bit_cast(uint32_t, h2);
+      lo[pp] = __builtin_bit_cast(uint32_t, l2);
     }
   };
   load_raw(0);
   for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
     __syncthreads();
-    // ---- reconstruct K (threads 0..127) and V (threads 128..255) ----
-    if (tid < 128) {
-      const int key = tid >> 1, hf = tid & 1;  // 2 threads per position, D/2 channels each
-      const int64_t j = min(k0 + key, nkeys - 1);
+    // ---- stage K ----
+    {
+      const int64_t j = min(k0 + kkey, nkeys - 1);
 #pragma unroll
-      for (int w = 0; w < D / 16; ++w) {  // 8-channel words of this half
-        const int word = hf * (D / 16) + w;
-        const int d0 = word * 8;
-        uint32_t o[4];
-        if constexpr (F16) {
-          const uint4 r4 = *reinterpret_cast<const uint4*>(k16 + (row0 + j) * D + d0);
-          o[0] = r4.x, o[1] = r4.y, o[2] = r4.z, o[3] = r4.w;
-        } else {
-          const uint32_t mb = rkm;  // one group per half (D/2 = 64 channels at d = 128, 32 at d = 64)
-          const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
-          const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
-          const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-          dequant8_cvt(rk[w], mn2, s2, o);
-        }
+      for (int w = 0; w < KW; ++w) {
+        const int d0 = kq * KW * 8 + w * 8;
         const int arr = d0 / 64, chunk = (d0 % 64) / 8;
-        *reinterpret_cast<uint4*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]) = make_uint4(o[0], o[1], o[2], o[3]);
+        const int at = kkey * 64 + ((chunk ^ (kkey & 7)) * 8);
+        if constexpr (F16) {
+          *reinterpret_cast<uint4*>(&k_lds[arr][at]) = *reinterpret_cast<const uint4*>(k16 + (row0 + j) * D + d0);
+        } else {
+          uint32_t hi[4], lo[4];
+          hilo8(rk[w], rkm, hi, lo);
+          *reinterpret_cast<uint4*>(&k_lds[arr][at]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          *reinterpret_cast<uint4*>(&klo_lds[arr][at]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
       }
-    } else {
-      // 8 positions (one storage chunk) x 8 channels per thread, transposed
-      const int u = tid - 128;
-      const int pc = u & 7;          // storage chunk: positions 8*pc .. 8*pc+7 in slice order
-      const int dc = u >> 3;         // channels 8*dc .. 8*dc+7 (D/8 <= 16 groups of 8)
-      if (dc < D / 8) {
-        const int sl = pc >> 2, qq = pc & 3;  // 32-wide slice, lane group inside it
-        uint32_t vals[8][4];                  // [position][channel pair]
+    }
+    // ---- stage V, transposed: [d][positions in slice order] ----
+    if (vact) {
+      uint32_t hi[4][4], lo[4][4];  // [position][channel pair]
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          if constexpr (F16) {
-            const int key = sl * 32 + (jj < 4 ? 4 * qq + jj : 16 + 4 * qq + jj - 4);
-            const int64_t j = min(k0 + key, nkeys - 1);
-            const uint4 r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + j) * D + dc * 8);
-            vals[jj][0] = r4.x, vals[jj][1] = r4.y, vals[jj][2] = r4.z, vals[jj][3] = r4.w;
-          } else {
-            const uint32_t mb = rvm[jj];
-            const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
-            const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
-            const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-            dequant8_cvt(rv[jj], mn2, s2, vals[jj]);
-          }
+      for (int jj = 0; jj < 4; ++jj) {
+        if constexpr (F16) {
+          const int64_t jv = min(k0 + vkey(jj), nkeys - 1);
+          const uint4 r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + jv) * D + vdc * 8);
+          hi[jj][0] = r4.x, hi[jj][1] = r4.y, hi[jj][2] = r4.z, hi[jj][3] = r4.w;
+        } else {
+          hilo8(rv[jj], rvm[jj], hi[jj], lo[jj]);
         }
-        // channel i of the 8: gather its 8 positions into one 16-byte chunk
+      }
+      // channel i: its 4 positions as 8 bytes, the first or second half of a 16-byte chunk
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t w4[4];
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const uint32_t a = vals[2 * pp][i >> 1], c2 = vals[2 * pp + 1][i >> 1];
-            // low halves (even channel) or high halves (odd channel) of two positions
-            w4[pp] = (i & 1) ? ((a >> 16) | (c2 & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c2 << 16));
-          }
-          const int d = dc * 8 + i;
-          *reinterpret_cast<uint4*>(&v_lds[d * KC + ((pc ^ (d & 7)) * 8)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int d = vdc * 8 + i;
+        const int at = d * KC + ((vpc ^ (d & 7)) * 8) + vhalf * 4;
+        auto pick = [&](const uint32_t (*x)[4], int pp) {  // low halves (even channel) or high (odd)
+          const uint32_t a = x[2 * pp][i >> 1], c2 = x[2 * pp + 1][i >> 1];
+          return (i & 1) ? ((a >> 16) | (c2 & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c2 << 16));
+        };
+        *reinterpret_cast<uint2*>(&v_lds[at]) = make_uint2(pick(hi, 0), pick(hi, 1));
+        if constexpr (!F16) *reinterpret_cast<uint2*>(&vlo_lds[at]) = make_uint2(pick(lo, 0), pick(lo, 1));
       }
     }
     __syncthreads();
@@ -582,10 +596,17 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 #pragma unroll
       for (int kd = 0; kd < NKD; ++kd) {
         const int arr = kd / 2, chunk = (kd % 2) * 4 + g4;
-        const half8_t kf = *reinterpret_cast<const half8_t*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]);
+        const int at = key * 64 + ((chunk ^ (key & 7)) * 8);
+        const half8_t kf = *reinterpret_cast<const half8_t*>(&k_lds[arr][at]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
+        if constexpr (!F16) {
+          const half8_t kl = *reinterpret_cast<const half8_t*>(&klo_lds[arr][at]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
+        }
       }
     }
     // ---- online softmax per query (lane l16 of each query block) ----
@@ -651,9 +672,16 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         const int chunk = sl * 4 + g4;
-        const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[d * KC + ((chunk ^ (d & 7)) * 8)]);
+        const int at = d * KC + ((chunk ^ (d & 7)) * 8);
+        const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[at]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][sl], oacc[db][qb], 0, 0, 0);
+        if constexpr (!F16) {
+          const half8_t vl = *reinterpret_cast<const half8_t*>(&vlo_lds[at]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, pf[qb][sl], oacc[db][qb], 0, 0, 0);
+        }
       }
     }
   }
@@ -730,7 +758,7 @@ extern "C" fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const f
   const size_t lds = (size_t)((len + 3) & ~3) * sizeof(float) + (size_t)256 * 8 * sizeof(float);
   const dim3 grid((unsigned)kv->heads, (unsigned)B);
   hipStream_t st = as_stream(stream);
-  const int tk = timing_begin(st);
+  const int tk = timing_begin(FQ_KC_DECODE_ATTN, st);
   by_format(*kv, [&](auto d, auto f16) {
     decode_attention_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), lds, st>>>(
         q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)len, out, ldo,
@@ -757,7 +785,7 @@ extern "C" fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const 
   FQ_CHECK_ARG(q && out && (uintptr_t)q % 16 == 0 && (uintptr_t)out % 16 == 0,
                "fq_prefill_attention: q/out NULL or misaligned");
   hipStream_t st = as_stream(stream);
-  const int tk = timing_begin(st);
+  const int tk = timing_begin(FQ_KC_PREFILL_ATTN, st);
   if (!prefill_vector_only()) {
     const dim3 grid((unsigned)ceil_div(T, 128), (unsigned)kv->heads, (unsigned)B);
     by_format(*kv, [&](auto d, auto f16) {

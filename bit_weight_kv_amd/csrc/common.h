@@ -60,8 +60,9 @@ __device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(half_
 __device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (half_t)f); }
 
 // ---- per-launch timing (timing.hip) -----------------------------------------
-// timing_begin returns a token (or -1 when timing is off); timing_end closes it.
-int timing_begin(hipStream_t st);
+// timing_begin returns a token (or -1 when timing is off, the class is not
+// selected, or the event pool is exhausted); timing_end closes it.
+int timing_begin(int cls, hipStream_t st);
 void timing_end(int token, int cls, double flops, double bytes, hipStream_t st);
 
 // ---- internal launchers used across translation units ----------------------

@@ -290,7 +290,7 @@ extern "C" fq_status fq_layernorm(const uint16_t* x, int64_t M, int64_t h, int64
                "fq_layernorm: buffers must be 16-byte aligned");
   hipStream_t st = as_stream(stream);
   const dim3 grid((unsigned)M);
-  const int tk = timing_begin(st);
+  const int tk = timing_begin(FQ_KC_LAYERNORM, st);
   if (h <= 2048)
     layernorm_kernel<1><<<grid, dim3(256), 0, st>>>(x, h, ldx, gamma, beta, eps, y, ldy);
   else if (h <= 4096)

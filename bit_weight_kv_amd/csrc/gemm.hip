@@ -2326,7 +2326,8 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
   // Tile choice: enough tiles to fill 256 CUs, split-K when the grid is small.
   const int KT = (int)(K / 64);
   const bool small_tiles = small_tiles_only();
-  const int tk = timing_begin(st);
+  const int cls = (epilogue & FQ_EPI_F32OUT) ? FQ_KC_LM_HEAD : (M > 256 ? FQ_KC_GEMM_PREFILL : FQ_KC_GEMM_DECODE);
+  const int tk = timing_begin(cls, st);
   fq_status r;
   if (M <= 256 && !small_tiles) {
     r = dispatch_skinny(A, M, lda, W, epi, st);
@@ -2366,7 +2367,6 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     const double cbytes = (epilogue & FQ_EPI_F32OUT) ? 4.0 * M * N : 2.0 * M * N;
     const double bytes = 2.0 * M * K + wbytes + cbytes + ((epilogue & FQ_EPI_RESIDUAL) ? 2.0 * M * N : 0.0) +
                          ((epilogue & FQ_EPI_BIAS) ? 2.0 * N : 0.0);
-    const int cls = (epilogue & FQ_EPI_F32OUT) ? FQ_KC_LM_HEAD : (M > 256 ? FQ_KC_GEMM_PREFILL : FQ_KC_GEMM_DECODE);
     timing_end(tk, cls, 2.0 * M * N * K, bytes, st);
   }
   return r;
@@ -2409,7 +2409,7 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
   KvAppend kva{kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->k16, kv->v16, h, kv->capacity, b0, pos,
                (int)T, kv->heads, kv->head_dim, f16 ? 1 : 0};
   hipStream_t st = as_stream(stream);
-  const int tk = timing_begin(st);
+  const int tk = timing_begin(FQ_KC_GEMM_PREFILL, st);
   const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
   if (use_w4(K, lda, W)) {
     gemm_w4_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);

@@ -188,7 +188,7 @@ extern "C" fq_status fq_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
   FQ_CHECK_ARG((uintptr_t)out->codes % 4 == 0 && (uintptr_t)out->meta % 4 == 0,
                "fq_quantize: codes/meta must be 4-byte aligned");
   hipStream_t st = as_stream(stream);
-  const int tk = timing_begin(st);
+  const int tk = timing_begin(FQ_KC_QUANTIZE, st);
   FQ_TRY(launch_quantize_rows(x, rows, cols, ldx, out->codes, out->meta, st));
   timing_end(tk, FQ_KC_QUANTIZE, 0.0, (double)rows * cols * (2.0 + 0.5625), st);
   return FQ_OK;
@@ -228,7 +228,7 @@ extern "C" fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, cons
     const int cpd = kv->head_dim / 8;
     const int64_t n_items = B * T * 2 * kv->heads * cpd;
     const dim3 grid((unsigned)ceil_div(n_items, 256));
-    const int tk = timing_begin(st);
+    const int tk = timing_begin(FQ_KC_KV_APPEND, st);
     if (aligned)
       kv_append_f16_kernel<true><<<grid, dim3(256), 0, st>>>(k, v, ld, n_items, (int)T, kv->heads, cpd, b0,
                                                              kv->capacity, pos, kv->k16, kv->v16);
@@ -243,7 +243,7 @@ extern "C" fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, cons
   const int gpd = kv->head_dim / 64;
   const int64_t n_groups = B * T * 2 * kv->heads * gpd;
   const dim3 grid((unsigned)ceil_div(n_groups * 8, 256));
-  const int tk = timing_begin(st);
+  const int tk = timing_begin(FQ_KC_KV_APPEND, st);
   if (aligned)
     kv_append_kernel<true><<<grid, dim3(256), 0, st>>>(k, v, ld, n_groups, (int)T, kv->heads, gpd, b0, kv->capacity,
                                                        pos, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta);

@@ -75,6 +75,7 @@ struct fq_model {
   int32_t* ids = nullptr;
   size_t ids_bytes = 0;
   std::vector<void*> allocs;
+  std::vector<fq_capture> captures;  // parity-test hook (fq_model_set_capture)
 
   int64_t h() const { return cfg.hidden; }
   int64_t F() const { return cfg.ffn; }
@@ -188,6 +189,27 @@ fq_weight layer_weight(const fq_model* m, int l, int which, uint8_t* staged) {
   return w;
 }
 
+// Rows of sequences [b0, b0+B) x T tokens (row = b*T + t, stride `ld`
+// elements) copied to a capture buffer [nb, capacity, h] at positions
+// pos..pos+T-1, for the sequences the capture holds.
+fq_status capture_rows(const fq_capture& c, uint16_t* dst, const uint16_t* src, int64_t ld, int64_t h, int64_t b0,
+                       int64_t B, int64_t T, int64_t pos, hipStream_t st) {
+  if (!dst) return FQ_OK;
+  const int64_t s0 = std::max(b0, c.b0), s1 = std::min(b0 + B, c.b0 + c.nb);
+  if (s0 >= s1) return FQ_OK;
+  if (pos + T > c.capacity) return fail(FQ_ERR_INVALID, "capture: positions beyond the capture's capacity");
+  for (int64_t s = s0; s < s1; ++s)
+    FQ_HIP(hipMemcpy2DAsync(dst + ((s - c.b0) * c.capacity + pos) * h, (size_t)h * 2, src + (s - b0) * T * ld,
+                            (size_t)ld * 2, (size_t)h * 2, (size_t)T, hipMemcpyDeviceToDevice, st));
+  return FQ_OK;
+}
+
+const fq_capture* find_capture(const fq_model* m, int l) {
+  for (const fq_capture& c : m->captures)
+    if (c.layer == l) return &c;
+  return nullptr;
+}
+
 // The core of one decoder layer over M = B*T rows (see fq_layer_step).
 fq_status layer_compute(fq_model* m, int l, const fq_kv_layer& kv, int64_t b0, int64_t B, int64_t T, int64_t pos,
                         const uint16_t* x, uint16_t* y, uint8_t* staged, hipStream_t st) {
@@ -198,18 +220,32 @@ fq_status layer_compute(fq_model* m, int l, const fq_kv_layer& kv, int64_t b0, i
   const fq_weight wq = layer_weight(m, l, 0, staged), wo = layer_weight(m, l, 1, staged),
                   w1 = layer_weight(m, l, 2, staged), w2 = layer_weight(m, l, 3, staged);
   void* s = (void*)st;
+  const fq_capture* cap = find_capture(m, l);
+  if (cap) FQ_TRY(capture_rows(*cap, cap->x_in, x, h, h, b0, B, T, pos, st));
   FQ_TRY(fq_layernorm(x, M, h, h, ln1g, ln1b, 1e-5f, m->h1, h, s));
   const float qscale = 1.0f / std::sqrt((float)m->d());
-  // QKV projection; K/V go to the cache (quantised in the GEMM epilogue at prefill sizes)
-  FQ_TRY(fq_qkv_gemm_append(m->h1, M, h, &wq, b_qkv, qscale, &kv, b0, B, T, pos, m->qkv, 3 * h, s));
+  if (!cap) {
+    // QKV projection; K/V go to the cache (quantised in the GEMM epilogue at prefill sizes)
+    FQ_TRY(fq_qkv_gemm_append(m->h1, M, h, &wq, b_qkv, qscale, &kv, b0, B, T, pos, m->qkv, 3 * h, s));
+  } else {
+    // the same results in two calls (the fused call is defined as equal to
+    // them bit for bit), so that K and V exist in fp16 and can be recorded
+    FQ_TRY(fq_dequant_gemm(m->h1, M, h, &wq, b_qkv, nullptr, 0, FQ_EPI_BIAS | FQ_EPI_QSCALE, qscale, h, m->qkv,
+                           3 * h, s));
+    FQ_TRY(fq_kv_append(&kv, m->qkv + h, m->qkv + 2 * h, 3 * h, b0, B, T, pos, s));
+    FQ_TRY(capture_rows(*cap, cap->k16, m->qkv + h, 3 * h, h, b0, B, T, pos, st));
+    FQ_TRY(capture_rows(*cap, cap->v16, m->qkv + 2 * h, 3 * h, h, b0, B, T, pos, st));
+  }
   if (T == 1)
     FQ_TRY(fq_decode_attention(m->qkv, 3 * h, &kv, b0, B, pos + 1, m->att, h, s));
   else
     FQ_TRY(fq_prefill_attention(m->qkv, 3 * h, &kv, b0, B, T, pos, m->att, h, s));
   FQ_TRY(fq_dequant_gemm(m->att, M, h, &wo, b_out, x, h, FQ_EPI_BIAS | FQ_EPI_RESIDUAL, 1.f, 0, m->x1, h, s));
+  if (cap) FQ_TRY(capture_rows(*cap, cap->x1, m->x1, h, h, b0, B, T, pos, st));
   FQ_TRY(fq_layernorm(m->x1, M, h, h, ln2g, ln2b, 1e-5f, m->h1, h, s));
   FQ_TRY(fq_dequant_gemm(m->h1, M, h, &w1, b_fc1, nullptr, 0, FQ_EPI_BIAS | FQ_EPI_RELU, 1.f, 0, m->f, F, s));
   FQ_TRY(fq_dequant_gemm(m->f, M, F, &w2, b_fc2, m->x1, h, FQ_EPI_BIAS | FQ_EPI_RESIDUAL, 1.f, 0, y, h, s));
+  if (cap) FQ_TRY(capture_rows(*cap, cap->y_out, y, h, h, b0, B, T, pos, st));
   return FQ_OK;
 }
 
@@ -475,12 +511,15 @@ fq_status set_layer(fq_model* m, int l, const fq_layer_weights* w, hipStream_t s
   LayerStore& ls = m->layers[l];
   const uint16_t* src[4] = {w->w_qkv, w->w_out, w->w_fc1, w->w_fc2};
   fq_packed staged[4];
+  // The staging slots may hold a copy of this layer (or of another layer that
+  // shares its host blob): forget both, so that the next pass copies the new
+  // weights in.
+  m->staged[0] = m->staged[1] = -1;
   if (m->pol.compress_weight && ls.host_blob >= 0) {
     // quantise into staging slot 0 (no generation is running), then copy the
     // packed layer to its host blob
     FQ_HIP(hipDeviceSynchronize());
     packed_slices(m, m->stage[0], staged);
-    m->staged[0] = -1;
   }
   for (int k = 0; k < 4; ++k) {
     int64_t n, kk;
@@ -620,6 +659,21 @@ extern "C" fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, in
   if (m->layers[layer].host_blob >= 0)
     return fail(FQ_ERR_INVALID, "fq_model_packed_weight: layer is streamed from host memory");
   *out = m->layers[layer].w[which];
+  return FQ_OK;
+}
+
+extern "C" fq_status fq_model_set_capture(fq_model* m, const fq_capture* caps, int32_t n) {
+  clear_error();
+  FQ_CHECK_ARG(m != nullptr, "fq_model_set_capture: NULL model");
+  FQ_CHECK_ARG(n >= 0 && n <= 8 && (n == 0 || caps), "fq_model_set_capture: between 0 and 8 captures");
+  for (int32_t i = 0; i < n; ++i) {
+    const fq_capture& c = caps[i];
+    FQ_CHECK_ARG(c.layer >= 0 && c.layer < m->cfg.layers, "fq_model_set_capture: layer out of range");
+    FQ_CHECK_ARG(c.b0 >= 0 && c.nb > 0 && c.capacity > 0, "fq_model_set_capture: bad sequence range or capacity");
+    for (int32_t j = 0; j < i; ++j)
+      FQ_CHECK_ARG(caps[j].layer != c.layer, "fq_model_set_capture: one capture per layer");
+  }
+  m->captures.assign(caps, caps + n);
   return FQ_OK;
 }
 
@@ -801,6 +855,9 @@ extern "C" fq_status fq_generate(fq_model* m, fq_kv* kv, const int32_t* prompt_i
   m->h2d_bytes = 0;
   m->h2d_s = 0;
   m->n_copies = 0;
+  // staged copies are trusted within one generation only (the caller may
+  // replace layers between calls)
+  m->staged[0] = m->staged[1] = -1;
   kv->h2d_bytes = kv->d2h_bytes = 0;
 
   hipEvent_t ev[3];

@@ -115,7 +115,13 @@ enum {
 
 /* C[M, N] = epilogue(A[M, K] * W^T) with the weight reconstructed in
  * registers (fp16) and fp32 accumulation on the matrix cores: the
- * dequant-fused projection GEMM of the QKV, output and FFN layers.
+ * dequant-fused projection GEMM of the QKV, output and FFN layers.  The pages
+ * store the weights in 4 bits and compute on them (FlexGen README, "Extreme
+ * Compression", and its --compress-weight flag under "Handle Out-of-memory";
+ * the Manning "FlexGen technique" page, "Configuring an OPT model": weight
+ * compression is a policy switch); the projections of an OPT layer are the
+ * models the README benchmarks ("Benchmark Results": OPT-6.7B/30B/175B).
+ * Fusing the reconstruction into the product is this library's design.
  *   A:        device fp16, row stride lda (>= K)
  *   bias:     device fp16 [N] (FQ_EPI_BIAS) or NULL
  *   residual: device fp16, row stride ldr (FQ_EPI_RESIDUAL) or NULL; may alias C
@@ -170,7 +176,14 @@ fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, const uint16_t*
 /* Decode attention over the cache: for each sequence b and head h,
  * s_j = q . k^_j for j < len, p = softmax(s), o = sum_j p_j v^_j, with k^, v^
  * reconstructed in registers in fp32 (min + code * s) from a 4-bit cache, or
- * read as stored from an fp16 cache.
+ * read as stored from an fp16 cache.  The attention cache is the one the
+ * pages compress to 4 bits (FlexGen README, "Extreme Compression"; the
+ * paper's abstract on the pith.science record: weights and the attention
+ * cache compressed to 4 bits); one decode step is one generated token of the
+ * README's "Benchmark Results" workload (output length 32).  Scores and the
+ * softmax are fp32; the value pass multiplies each position's probability by
+ * its group scale and rounds that product to fp16 before the fp32 dot
+ * product with the exact codes.
  *   q:   device fp16 [B, heads*head_dim] row stride ldq, already scaled by
  *        head_dim^-1/2
  *   out: device fp16 [B, heads*head_dim] row stride ldo
@@ -258,14 +271,36 @@ typedef struct {
   const uint16_t* ln2_b;
 } fq_layer_weights;
 
+/* Create a model handle: device storage for every resident layer (packed
+ * 4-bit weights when the policy compresses them: 0.5625 byte per weight, the
+ * README's "around 70%" saving of --compress-weight under "Handle
+ * Out-of-memory"; else fp16), pinned host blobs for the streamed layers and
+ * their two device staging buffers (README, "Get Started": --percent places
+ * weights on the GPU or the CPU; the block schedule of "Benchmark Results"
+ * overlaps their copies with compute), and the activation workspace.  The
+ * parameters are uninitialised until fq_model_set_layer /
+ * fq_model_init_random.  The handle owns every allocation.  Errors:
+ * FQ_ERR_INVALID for bad sizes, FQ_ERR_UNSUPPORTED for a head_dim other
+ * than 64 or 128, FQ_ERR_OOM when device or pinned memory runs out (nothing
+ * is leaked). */
 fq_status fq_model_create(const fq_model_config* cfg, const fq_policy* policy, fq_model** out);
+/* Free everything the handle owns (waits for the device first).  NULL is a no-op. */
 fq_status fq_model_destroy(fq_model* m);
 
-/* Quantise (or copy) one layer's fp16 parameters into the model's store. */
+/* Quantise (or copy) one layer's fp16 parameters into the model's store:
+ * the load-time weight compression of the README's --compress-weight
+ * ("Handle Out-of-memory"; "Extreme Compression"), group-wise as fq_quantize.
+ * A streamed layer is packed on the device and copied to its pinned host blob
+ * (synchronous on `stream`); its staged copies are forgotten so that the next
+ * pass copies the new weights in.  Errors: FQ_ERR_INVALID for a layer out of
+ * range or a NULL parameter. */
 fq_status fq_model_set_layer(fq_model* m, int32_t layer, const fq_layer_weights* w, void* stream);
 
 /* Token embedding [V, h], position table [max_pos, h], final LN gamma/beta [h]
- * (device fp16).  The LM head is tied to the token embedding. */
+ * (device fp16; copied).  The LM head is tied to the token embedding, and
+ * position p reads row p + 2 of the position table (the OPT models of the
+ * README's "Benchmark Results").  FQ_ERR_INVALID for a layer-only model
+ * (vocab 0). */
 fq_status fq_model_set_embeddings(fq_model* m, const uint16_t* embed, const uint16_t* pos,
                                   const uint16_t* lnf_g, const uint16_t* lnf_b, void* stream);
 
@@ -279,26 +314,81 @@ fq_status fq_model_set_embeddings(fq_model* m, const uint16_t* embed, const uint
  * stored fp16 (resident or in pinned host memory).  Synchronous. */
 fq_status fq_model_init_random(fq_model* m, uint64_t seed, double bias_sigma, void* stream);
 
-/* Device view of one layer's packed weight (which: 0 qkv, 1 out, 2 fc1, 3 fc2). */
+/* Device view of one layer's packed weight (which: 0 qkv, 1 out, 2 fc1, 3 fc2),
+ * owned by the model.  FQ_ERR_INVALID if weights are not compressed or the
+ * layer is streamed from host memory. */
 fq_status fq_model_packed_weight(const fq_model* m, int32_t layer, int32_t which, fq_packed* out);
+
+/* Parity-test hook: record what one layer computes inside later calls
+ * (fq_layer_step, fq_generate), so that a test can feed the oracle the same
+ * inputs and the same fp16 K/V -- its quantisation of those K/V must then
+ * equal the cache bit for bit, and the layer's outputs are compared under
+ * teacher forcing.  Not part of the method; off unless set.
+ *   layer:   the layer whose values are recorded
+ *   b0, nb:  sequences b0..b0+nb-1
+ *   capacity: positions per sequence in each buffer
+ *   x_in, y_out, k16, v16, x1: device fp16 [nb, capacity, hidden] or NULL;
+ *     row (b - b0, p) receives the layer's input row, its output row, the
+ *     fp16 K and V it appends, and its residual after the output projection,
+ *     at position p of sequence b.
+ * While a capture is set for a layer, that layer's QKV projection runs as the
+ * two calls fq_qkv_gemm_append is defined to equal (projection, then
+ * append), so K and V exist in fp16.  The buffers must stay valid while the
+ * capture is set.  fq_model_set_capture(m, NULL, 0) clears every capture.
+ * Errors: FQ_ERR_INVALID for more than 8 captures, two on one layer, a layer
+ * out of range; a later call fails with FQ_ERR_INVALID if it reaches a
+ * position at or beyond `capacity` of a captured sequence. */
+typedef struct {
+  int32_t layer;
+  int64_t b0;
+  int64_t nb;
+  int64_t capacity;
+  uint16_t* x_in;
+  uint16_t* y_out;
+  uint16_t* k16;
+  uint16_t* v16;
+  uint16_t* x1; /* the residual after the output projection, x + o Wo^T + bo */
+} fq_capture;
+fq_status fq_model_set_capture(fq_model* m, const fq_capture* caps, int32_t n);
 
 /* KV cache for `batch` sequences of up to `capacity` positions, all layers:
  * 4-bit (0.5625 byte per cached element) when the policy compresses the
- * cache, else fp16 (2 bytes).  Layers at or beyond the policy's
- * cache_resident_layers live in pinned host memory (fq_kv_layer_view then
- * returns host pointers). */
+ * cache, else fp16 (2 bytes) -- the attention cache the pages compress to 4
+ * bits (FlexGen README, "Extreme Compression").  Layers at or beyond the
+ * policy's cache_resident_layers live in pinned host memory (README, "Get
+ * Started": the --percent pair for the cache places it on the GPU or the
+ * CPU); fq_kv_layer_view then returns host pointers.  The handle owns every
+ * allocation.  Errors: FQ_ERR_INVALID for bad sizes, FQ_ERR_OOM when memory
+ * runs out (nothing is leaked). */
 fq_status fq_kv_create(const fq_model* m, int64_t batch, int64_t capacity, fq_kv** out);
+/* Free everything the handle owns (waits for the device first).  NULL is a no-op. */
 fq_status fq_kv_destroy(fq_kv* kv);
+/* The buffers of one layer's cache (device pointers, or pinned host pointers
+ * for an offloaded layer), owned by the handle. */
 fq_status fq_kv_layer_view(const fq_kv* kv, int32_t layer, fq_kv_layer* out);
 
 /* One decoder layer over T new tokens of sequences b0..b0+B-1 at positions
  * pos..pos+T-1: LN1, QKV projection (+bias, query scaling), quantise-on-
  * append of K/V (or fp16 append), attention over the cache (causal for T > 1), output
  * projection (+bias, +residual), LN2, FC1 (+bias, ReLU), FC2 (+bias,
- * +residual).  fp16 storage points as in the header of the oracle's layer.
+ * +residual).  The layer is that of the OPT models the pages run (FlexGen
+ * README, "Get Started with a Single GPU" and "Benchmark Results":
+ * OPT-6.7B/30B/175B), pre-LayerNorm with a ReLU FFN, its weights and
+ * attention cache in 4 bits ("Extreme Compression").  T > 1 is the prompt
+ * pass, T == 1 one generation step; both count in the README's throughput
+ * ("Benchmark Results", Metric bullet).
+ * Each of these values is rounded once to fp16 (round to nearest even) from
+ * its fp32 accumulation, and nowhere else:
+ *   h1 = LN1(x);  q = (h1 Wq^T + bq) * head_dim^-1/2;  k = h1 Wk^T + bk;
+ *   v = h1 Wv^T + bv  (k, v then quantised into the cache, or kept fp16);
+ *   o = attention(q, cache);  x1 = x + o Wo^T + bo;  h2 = LN2(x1);
+ *   f = max(h2 W1^T + b1, 0);  y = x1 + f W2^T + b2.
+ * LayerNorm: eps 1e-5, biased variance, fp32 statistics.
  *   x, y: device fp16 [B*T, h] (may be the same buffer).
  * B*T must not exceed the policy's max_tokens.  Layers whose fp16 weights
- * live in host memory are copied in synchronously on `stream` first. */
+ * live in host memory are copied in synchronously on `stream` first.
+ * Errors: FQ_ERR_INVALID for a layer out of range, B*T above max_tokens,
+ * sequences or positions beyond the cache, NULL or misaligned x/y. */
 fq_status fq_layer_step(fq_model* m, int32_t layer, fq_kv* kv, int64_t b0, int64_t B, int64_t T, int64_t pos,
                         const uint16_t* x, uint16_t* y, void* stream);
 
@@ -341,7 +431,10 @@ void fq_set_progress(fq_progress_fn fn, void* user);
 /* Per-launch device timing (HIP events on the launching stream), grouped by
  * kernel class, with each launch's algorithmic work: flops of the
  * contraction and the bytes a single pass over its operands moves to or
- * from HBM (packed weights 0.5625 B/element, fp16 2 B, fp32 4 B). */
+ * from HBM (packed weights 0.5625 B/element, fp16 2 B, fp32 4 B).  Used by
+ * the benchmark to report each kernel against its roofline (FlexGen README,
+ * "Benchmark Results": the pages report only end-to-end throughput; the
+ * per-kernel split is this library's). */
 typedef enum {
   FQ_KC_GEMM_PREFILL = 0, /* projection GEMMs with M > 256 rows */
   FQ_KC_GEMM_DECODE = 1,  /* projection GEMMs with M <= 256 rows */
@@ -354,16 +447,25 @@ typedef enum {
   FQ_KC_COUNT = 8
 } fq_kernel_class;
 
+#define FQ_KC_ALL 0xFFu
+
 typedef struct {
   int64_t launches;
   double seconds; /* sum of per-launch device time */
   double flops;   /* sum of algorithmic flops */
   double bytes;   /* sum of algorithmic HBM bytes */
+  int64_t dropped; /* launches of this class not timed: the event pool
+                      (65536 launches per recording) was exhausted */
 } fq_kernel_stats;
 
-/* Start recording (clears earlier records).  Process-wide. */
-fq_status fq_timing_start(void);
-/* Stop, wait for the recorded events and fill out[FQ_KC_COUNT] (may be NULL). */
+/* Start recording the launches of the classes whose bit (1u << class) is set
+ * in class_mask (FQ_KC_ALL: every class); clears earlier records.  Launches
+ * of other classes record nothing.  Process-wide.  The event pool holds at
+ * most 65536 launches per recording; later launches are counted in
+ * `dropped` and not timed. */
+fq_status fq_timing_start(uint32_t class_mask);
+/* Stop, wait for the recorded events and fill out[FQ_KC_COUNT] (may be NULL).
+ * FQ_ERR_HIP if an event cannot be read. */
 fq_status fq_timing_stop(fq_kernel_stats* out);
 
 /* ------------------------------------------------------------------------ */

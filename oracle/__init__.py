@@ -33,11 +33,12 @@ fp16 rounding only at the storage points of the layer (see model.py).
 from .quant import quantize, dequant_f16, dequant_f64, pack_nibbles, unpack_nibbles, GROUP
 from .ops import gemm, layernorm, attention_decode, attention_prefill_causal, softmax
 from .model import (LayerConfig, ModelConfig, layer_params, pack_layer, new_cache, layer_step,
-                    generate, embed, lm_head_logits, argmax_lowest)
+                    layer_rows, cache_fill, generate, embed, lm_head_logits, argmax_lowest)
 
 __all__ = [
     "quantize", "dequant_f16", "dequant_f64", "pack_nibbles", "unpack_nibbles", "GROUP",
     "gemm", "layernorm", "attention_decode", "attention_prefill_causal", "softmax",
     "LayerConfig", "ModelConfig", "layer_params", "pack_layer", "new_cache", "layer_step",
+    "layer_rows", "cache_fill",
     "generate", "embed", "lm_head_logits", "argmax_lowest",
 ]

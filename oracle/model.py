@@ -63,19 +63,17 @@ class ModelConfig:
     max_pos: int          # rows of the position table (positions used: pos + 2)
 
 
-def layer_params(seed: int, cfg: LayerConfig, layer: int, bias_sigma: float = 0.0) -> dict:
+def layer_params(seed: int, cfg: LayerConfig, layer: int, bias_sigma: float = 0.0, workers: int = 1) -> dict:
     """fp16 parameters of one layer from the seeded generator.
 
     Weights ~ (bounded) N(0, 0.02).  bias_sigma == 0: OPT-style init (biases 0,
     LN gamma 1, beta 0).  bias_sigma > 0: biases and betas ~ N(0, bias_sigma),
-    gammas ~ N(0, 1), to exercise every term of the layer."""
+    gammas ~ N(0, 1), to exercise every term of the layer.  `workers` threads
+    generate the large tensors (same values)."""
     h, F = cfg.hidden, cfg.ffn
-    p = {
-        "w_qkv": synth.normal_f16(seed, layer_stream(layer, "w_qkv"), (3 * h, h), 0.02),
-        "w_out": synth.normal_f16(seed, layer_stream(layer, "w_out"), (h, h), 0.02),
-        "w_fc1": synth.normal_f16(seed, layer_stream(layer, "w_fc1"), (F, h), 0.02),
-        "w_fc2": synth.normal_f16(seed, layer_stream(layer, "w_fc2"), (h, F), 0.02),
-    }
+    w = lambda name, shape: synth.normal_f16(seed, layer_stream(layer, name), shape, 0.02, workers=workers)
+    p = {"w_qkv": w("w_qkv", (3 * h, h)), "w_out": w("w_out", (h, h)),
+         "w_fc1": w("w_fc1", (F, h)), "w_fc2": w("w_fc2", (h, F))}
     shapes = {"b_qkv": 3 * h, "b_out": h, "b_fc1": F, "b_fc2": h,
               "ln1_g": h, "ln1_b": h, "ln2_g": h, "ln2_b": h}
     for name, n in shapes.items():
@@ -87,17 +85,33 @@ def layer_params(seed: int, cfg: LayerConfig, layer: int, bias_sigma: float = 0.
     return p
 
 
-def pack_layer(params: dict, cfg: LayerConfig) -> dict:
+def pack_layer(params: dict, cfg: LayerConfig, workers: int = 1) -> dict:
     """Linear weights as used by the GEMMs: dequant_f16(quantize(W)) when weights are
     compressed, else W itself -- held as float64 (exact copies of the fp16 values)
     so that every GEMM reads them without a conversion.  Also returns the packed
-    codes/meta."""
+    codes/meta.  Quantisation groups lie within one row, so with `workers` > 1
+    blocks of rows are packed on that many threads (same values)."""
     out = {}
     for name in ("w_qkv", "w_out", "w_fc1", "w_fc2"):
         w = params[name]
         if cfg.compress_weight:
-            codes, meta = quantize(w, cfg.group)
-            out[name] = dequant_f16(codes, meta, cfg.group).astype(np.float64)
+            n, k = w.shape
+            codes = np.empty((n, k // 2), np.uint8)
+            meta = np.empty((n, k // cfg.group, 2), np.float16)
+            wd = np.empty((n, k), np.float64)
+            rows = max(1, n // (4 * workers)) if workers > 1 else n
+
+            def part(r0, w=w, codes=codes, meta=meta, wd=wd, rows=rows):
+                c, m = quantize(w[r0:r0 + rows], cfg.group)
+                codes[r0:r0 + rows], meta[r0:r0 + rows] = c, m
+                wd[r0:r0 + rows] = dequant_f16(c, m, cfg.group)
+            if workers > 1:
+                from concurrent.futures import ThreadPoolExecutor
+                with ThreadPoolExecutor(workers) as ex:
+                    list(ex.map(part, range(0, n, rows)))
+            else:
+                part(0)
+            out[name] = wd
             out[name + ".codes"], out[name + ".meta"] = codes, meta
         else:
             out[name] = w.astype(np.float64)
@@ -155,6 +169,29 @@ def _attend(q16, cache, cfg: LayerConfig, pos: int):
     return out
 
 
+def _qkv(xf, params, packed, cfg):
+    """LN1 and the QKV projection of rows xf [M, h]: h1, q (scaled), k, v at their
+    storage points, plus k and v in float64 before rounding."""
+    h, d = cfg.hidden, cfg.head_dim
+    h1 = layernorm(xf, params["ln1_g"], params["ln1_b"]).astype(np.float16)
+    qkv = gemm(h1, packed["w_qkv"], params["b_qkv"])
+    q = (qkv[:, :h] * (float(d) ** -0.5)).astype(np.float16)
+    k = qkv[:, h:2 * h].astype(np.float16)
+    v = qkv[:, 2 * h:].astype(np.float16)
+    return h1, q, k, v, qkv[:, h:2 * h], qkv[:, 2 * h:]
+
+
+def _after_attention(xf, o, params, packed):
+    """Output projection with residual, LN2, FFN with residual for rows xf [M, h]
+    and their attention output o (fp16).  Returns x1_64, x1, h2, f, y64."""
+    x1_64 = xf.astype(np.float64) + gemm(o, packed["w_out"], params["b_out"])
+    x1 = x1_64.astype(np.float16)
+    h2 = layernorm(x1, params["ln2_g"], params["ln2_b"]).astype(np.float16)
+    f = np.maximum(gemm(h2, packed["w_fc1"], params["b_fc1"]), 0.0).astype(np.float16)
+    y64 = x1.astype(np.float64) + gemm(f, packed["w_fc2"], params["b_fc2"])
+    return x1_64, x1, h2, f, y64
+
+
 def layer_step(x16: np.ndarray, params: dict, packed: dict, cache: dict, cfg: LayerConfig,
                pos: int, want: tuple = ()) -> dict:
     """One pre-LN decoder layer over T new tokens per sequence at positions pos..pos+T-1.
@@ -165,25 +202,62 @@ def layer_step(x16: np.ndarray, params: dict, packed: dict, cache: dict, cfg: La
     H, d = cfg.heads, cfg.head_dim
     r = {}
     xf = x16.reshape(B * T, h)
-    h1 = layernorm(xf, params["ln1_g"], params["ln1_b"]).astype(np.float16)
-    qkv = gemm(h1, packed["w_qkv"], params["b_qkv"])
-    q = (qkv[:, :h] * (float(d) ** -0.5)).astype(np.float16)
-    k = qkv[:, h:2 * h].astype(np.float16)
-    v = qkv[:, 2 * h:].astype(np.float16)
+    h1, q, k, v, k64, v64 = _qkv(xf, params, packed, cfg)
     to_bhtd = lambda a: a.reshape(B, T, H, d).transpose(0, 2, 1, 3)
     _cache_append(cache, cfg, to_bhtd(k), to_bhtd(v), pos)
     o64 = _attend(to_bhtd(q), cache, cfg, pos)                 # [B, H, T, d]
     o = o64.transpose(0, 2, 1, 3).reshape(B * T, h).astype(np.float16)
-    x1_64 = xf.astype(np.float64) + gemm(o, packed["w_out"], params["b_out"])
-    x1 = x1_64.astype(np.float16)
-    h2 = layernorm(x1, params["ln2_g"], params["ln2_b"]).astype(np.float16)
-    f = np.maximum(gemm(h2, packed["w_fc1"], params["b_fc1"]), 0.0).astype(np.float16)
-    y64 = x1.astype(np.float64) + gemm(f, packed["w_fc2"], params["b_fc2"])
+    x1_64, x1, h2, f, y64 = _after_attention(xf, o, params, packed)
     r["y"] = y64.astype(np.float16).reshape(B, T, h)
     r["y64"] = y64.reshape(B, T, h)
-    local = {"h1": h1, "q": q, "k": k, "v": v, "k64": qkv[:, h:2 * h], "v64": qkv[:, 2 * h:],
+    local = {"h1": h1, "q": q, "k": k, "v": v, "k64": k64, "v64": v64,
              "o": o, "o64": o64, "x1": x1, "x1_64": x1_64,
              "h2": h2, "f": f}
+    for name in want:
+        r[name] = local[name]
+    return r
+
+
+def cache_fill(cache: dict, cfg: LayerConfig, k16: np.ndarray, v16: np.ndarray, pos: int = 0) -> None:
+    """Put given fp16 K/V of tokens at positions pos..pos+T-1 into the cache, quantised
+    exactly as the layer appends its own (teacher forcing: K/V computed elsewhere).
+    k16, v16 [B, T, h]."""
+    B, T, h = k16.shape
+    H, d = cfg.heads, cfg.head_dim
+    to_bhtd = lambda a: np.ascontiguousarray(np.asarray(a, np.float16).reshape(B, T, H, d).transpose(0, 2, 1, 3))
+    _cache_append(cache, cfg, to_bhtd(k16), to_bhtd(v16), pos)
+
+
+def layer_rows(x16: np.ndarray, positions, params: dict, packed: dict, cache: dict, cfg: LayerConfig,
+               want: tuple = ()) -> dict:
+    """The layer applied to given rows under teacher forcing: row r of every sequence
+    is the token at position positions[r], and its query attends over cache positions
+    0..positions[r], which the cache must already hold (cache_fill).  Nothing is
+    appended.  The arithmetic is layer_step's; the row's own K/V are returned (for
+    comparison with those in the cache) but not used.
+
+    x16 fp16 [B, R, h].  Returns {"y", "y64"} [B, R, h] plus any names in `want`."""
+    B, R, h = x16.shape
+    H, d = cfg.heads, cfg.head_dim
+    positions = np.asarray(positions, np.int64)
+    assert positions.shape == (R,)
+    xf = x16.reshape(B * R, h)
+    h1, q, k, v, k64, v64 = _qkv(xf, params, packed, cfg)
+    qb = q.reshape(B, R, H, d).transpose(0, 2, 1, 3)           # [B, H, R, d]
+    n = int(positions.max()) + 1
+    mask = np.arange(n)[None, :] > positions[:, None]          # [R, n]
+    o64 = np.empty((B, H, R, d), np.float64)
+    for b in range(B):
+        kk, vv = _cache_read(cache, cfg, n, b)                 # [H, n, d]
+        sc = qb[b].astype(np.float64) @ np.swapaxes(kk, -1, -2)  # [H, R, n]
+        sc[:, mask] = -np.inf
+        o64[b] = softmax(sc, axis=-1) @ vv
+    o = o64.transpose(0, 2, 1, 3).reshape(B * R, h).astype(np.float16)
+    x1_64, x1, h2, f, y64 = _after_attention(xf, o, params, packed)
+    r = {"y": y64.astype(np.float16).reshape(B, R, h), "y64": y64.reshape(B, R, h)}
+    rows = lambda a: a.reshape(B, R, -1)
+    local = {"h1": rows(h1), "q": rows(q), "k": rows(k), "v": rows(v), "k64": rows(k64), "v64": rows(v64),
+             "o": rows(o), "o64": o64, "x1": rows(x1), "x1_64": rows(x1_64), "h2": rows(h2), "f": rows(f)}
     for name in want:
         r[name] = local[name]
     return r

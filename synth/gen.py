@@ -68,15 +68,28 @@ def normal_scale_f32(sigma: float) -> np.float32:
 
 
 def normal_f16(seed: int, stream: int, shape=None, sigma: float = 1.0, index=None,
-               chunk: int = 1 << 24) -> np.ndarray:
+               chunk: int = 1 << 24, workers: int = 1) -> np.ndarray:
     """fp16 variates with std ``sigma``: either a whole tensor of ``shape`` (flat
-    indices 0..n-1, row-major) or the elements at flat ``index``."""
+    indices 0..n-1, row-major) or the elements at flat ``index``.  A whole tensor
+    is produced in chunks of flat indices, on ``workers`` threads if more than one
+    (every element depends only on its own index, so the result is the same)."""
     if index is None:
         n = int(np.prod(shape))
         out = np.empty(n, dtype=np.float16)
-        for s in range(0, n, chunk):
+
+        def part(s):
             e = min(n, s + chunk)
             out[s:e] = normal_f16(seed, stream, sigma=sigma, index=np.arange(s, e, dtype=np.uint64))
+        if workers > 1:
+            chunk = min(chunk, 1 << 22)  # enough pieces to keep every thread busy
+        starts = range(0, n, chunk)
+        if workers > 1 and n > chunk:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(workers) as ex:
+                list(ex.map(part, starts))
+        else:
+            for s in starts:
+                part(s)
         return out.reshape(shape)
     u = raw_u64(seed, stream, index)
     m = np.uint64(0xFFFF)

@@ -193,3 +193,35 @@ def test_progress_callback_reports_every_token_in_order():
     # the report changes nothing: same tokens and logits without it
     _, out2, lg2, _ = _gpu_generate(L, B, P, G, seed=3)
     assert np.array_equal(out, out2) and np.array_equal(lg, lg2)
+
+
+@pytest.mark.parametrize("compress", [True, False])
+@pytest.mark.parametrize("replace", [1, 2])
+def test_replaced_streamed_layer_is_copied_again(compress, replace):
+    """Layers 1 and 2 streamed (staging slots 1 and 0).  After a generation the
+    slots still hold those layers; replacing one of them with fq_model_set_layer
+    must make the next generation copy the new weights in: its tokens and
+    logits equal those of an all-resident model holding the same weights."""
+    L, B, P, G = 3, 2, 10, 4
+    names = ("w_qkv", "w_out", "w_fc1", "w_fc2", "b_qkv", "b_out", "b_fc1", "b_fc2",
+             "ln1_g", "ln1_b", "ln2_g", "ln2_b")
+    new = oracle.layer_params(9, LayerConfig(H, NH, F), replace, bias_sigma=0.02)
+    new_dev = {n: dev(new[n]) for n in names}
+    ids = synth.token_ids(6, synth.STREAM["prompt"], (B, P), V)
+    results = []
+    for resident in (1, -1):
+        model = fq.Model(H, NH, F, L, vocab=V, max_pos=P + G + 2, compress_weight=compress,
+                         resident_layers=resident)
+        model.init_random(6)
+        kv = fq.KVCache(model, B, P + G)
+        if resident == 1:
+            fq.fq_generate(model, kv, ids, G)  # leaves layers 1 and 2 in the staging slots
+        model.set_layer(replace, new_dev)
+        torch.cuda.synchronize()
+        logits = torch.empty((G, B, V), dtype=torch.float32, device="cuda:0")
+        out, _ = fq.fq_generate(model, kv, ids, G, logits=logits)
+        results.append((out, host(logits)))
+        kv.close()
+        model.close()
+    (s_out, s_lg), (r_out, r_lg) = results
+    assert np.array_equal(s_out, r_out) and np.array_equal(s_lg, r_lg)

@@ -1,6 +1,8 @@
-"""fq_layer_step (prefill + decode of one OPT-style layer) against the oracle:
-the tiny configuration in full, the OPT-6.7B-shaped layer on sampled
-sequences, and the packed weights bit-exact."""
+"""fq_layer_step (prefill + decode of one OPT-style layer) against the oracle
+under teacher forcing (the oracle quantises the GPU's own fp16 K/V, so both
+caches hold the same codes): the tiny configuration in full, the
+OPT-6.7B-shaped layer on 8 of its 64 sequences at every position, and the
+packed weights bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -8,7 +10,8 @@ import torch
 import synth
 import oracle
 from oracle import LayerConfig
-from tests._util import dev, host, bits16, assert_close, log
+from tests._util import (dev, host, bits16, assert_close, log, gpu_cache, packed_to_host,
+                         assert_same_cache)
 
 pytestmark = pytest.mark.gpu
 fq = pytest.importorskip("bit_weight_kv_amd")
@@ -19,129 +22,21 @@ NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2", "b_qkv", "b_out", "b_fc1", "b_fc2",
 
 def _check_packed(model, layer, params, cfg):
     for i, name in enumerate(("w_qkv", "w_out", "w_fc1", "w_fc2")):
-        p = model.packed_weight(layer, i)
-        n, k = p.rows, p.cols
-        codes = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda:0")
-        meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device="cuda:0")
-        torch.cuda.synchronize()
-        _copy_dev(codes.data_ptr(), p.codes, n * k // 2)
-        _copy_dev(meta.data_ptr(), p.meta, n * (k // 64) * 4)
+        codes, meta = packed_to_host(model.packed_weight(layer, i))
         rc, rm = oracle.quantize(params[name], cfg.group)
-        gm = bits16(host(meta))
+        gm = bits16(meta)
         bad = np.argwhere(gm != bits16(rm))
         assert len(bad) == 0, f"{name}: {len(bad)} meta mismatches, first {bad[:4].tolist()} " \
                               f"gpu {[gm[tuple(i)] for i in bad[:4]]} oracle {[bits16(rm)[tuple(i)] for i in bad[:4]]}"
-        assert np.array_equal(host(codes), rc), name
+        assert np.array_equal(codes, rc), name
 
 
-def _validate_code_differences(gpu_codes, ref_codes, ref_kv16, cfg, what):
-    """GPU and oracle 4-bit caches of one sequence ([H, S, d/2] bytes each).
-    The two sides round their own fp16 K/V (fp32 accumulation on the GPU,
-    float64 in the oracle), so a value within an ulp of a code boundary may be
-    coded either way.  Every differing code must be such a near-tie: one level
-    apart, with the oracle's own (v - min) / s within 0.05 of the half-way point
-    between the two levels.  Returns the number of differing codes."""
-    H, S, half = gpu_codes.shape[0], ref_kv16.shape[0], gpu_codes.shape[2]
-    g = oracle.unpack_nibbles(gpu_codes[:, :S]).astype(np.int64)
-    o = oracle.unpack_nibbles(ref_codes[:, :S]).astype(np.int64)
-    diff = np.argwhere(g != o)
-    if len(diff) == 0:
-        return 0
-    d = cfg.head_dim
-    x = ref_kv16.reshape(S, H, d).transpose(1, 0, 2).astype(np.float32)  # [H, S, d]
-    _, meta = oracle.quantize(np.ascontiguousarray(x.astype(np.float16)))
-    for hh, t, c in diff:
-        gi = c // 64
-        mn, sc = meta[hh, t, gi].astype(np.float32)
-        frac = (x[hh, t, c] - mn) / sc if sc > 0 else 0.0
-        assert abs(g[hh, t, c] - o[hh, t, c]) == 1, f"{what}: code jump {o[hh, t, c]} -> {g[hh, t, c]}"
-        boundary = (g[hh, t, c] + o[hh, t, c]) / 2.0
-        assert abs(frac - boundary) < 0.05, f"{what}: code differs away from a tie (frac {frac}, boundary {boundary})"
-    log(f"{what}: {len(diff)} near-tie code differences of {g.size}")
-    return len(diff)
-
-
-def _assert_layer_output(got, ref, what, strict_max):
-    """Relative L2 <= 5e-3 always; max |err| <= 3e-2 where both caches hold the
-    same codes (a near-tie code difference moves one reconstructed K/V element by
-    a whole quantisation step, which the max-abs bound was not set for)."""
-    from tests._util import rel_l2, REL_L2, MAX_ABS
-    r = rel_l2(got, ref)
-    m = float(np.abs(np.asarray(got, np.float64) - ref).max())
-    assert r <= REL_L2, f"{what}: rel_l2={r:.3e}"
-    if strict_max:
-        assert m <= MAX_ABS, f"{what}: max_abs={m:.3e}"
-    elif m > MAX_ABS:
-        log(f"{what}: max_abs {m:.3e} above {MAX_ABS} after near-tie code differences (rel_l2 {r:.2e})")
-
-
-def _gpu_cache(kv, layer, B, H, cap, d):
-    v = kv.view(layer)
-    out = {}
-    if v.bits == 16:
-        items = (("k", v.k16, (B, H, cap, d), torch.float16), ("v", v.v16, (B, H, cap, d), torch.float16))
-    else:
-        items = (("k_codes", v.k_codes, (B, H, cap, d // 2), torch.uint8),
-                 ("v_codes", v.v_codes, (B, H, cap, d // 2), torch.uint8))
-    for name, ptr, shape, dt in items:
-        t = torch.empty(shape, dtype=dt, device="cuda:0")
-        _copy_dev(t.data_ptr(), ptr, t.numel() * t.element_size())
-        out[name] = host(t)
-    return out
-
-
-def _copy_dev(dst, src, nbytes):
-    import ctypes
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
-    # hipMemcpyDefault: the source may be device memory or pinned host memory (offloaded cache)
-    assert hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), ctypes.c_size_t(nbytes), 4) == 0
-
-
-def _validate_f16_differences(gpu, ref16, ref64, what):
-    """GPU and oracle fp16 caches of one sequence ([H, S, d] each; ref64 the
-    oracle's float64 K or V before rounding, [S, H*d]).  Each side computes K/V
-    from its own fp16 LayerNorm output (one-ulp differences at near-ties) with
-    its own accumulation (fp32 / float64), so the exact values differ by up to
-    about 1e-4 (fp16 ulps of O(1)-O(4) LayerNorm outputs times 0.02 weights)
-    and an element may round to another fp16 neighbour (for small values, a
-    few ulps away).  Every differing GPU value must lie within 1e-3 of the
-    oracle's exact value (30x below the layer-output max-abs bound), and at
-    most 2% of the elements may differ (rows whose LayerNorm output differs
-    somewhere cluster their differences)."""
-    H, S, d = gpu.shape[0], ref16.shape[0], gpu.shape[2]
-    g = gpu[:, :S].astype(np.float64)
-    o = ref16.reshape(S, H, d).transpose(1, 0, 2).astype(np.float64)
-    x = ref64.reshape(S, H, d).transpose(1, 0, 2)
-    diff = np.argwhere(g != o)
-    for idx in diff:
-        gv, ov, xv = g[tuple(idx)], o[tuple(idx)], x[tuple(idx)]
-        assert abs(gv - xv) <= 1e-3, f"{what}: {gv} is far from the exact {xv}"
-    frac = len(diff) / g.size
-    log(f"{what}: {len(diff)} rounding differences of {g.size} ({frac:.2%})")
-    assert frac <= 0.02, f"{what}: {frac:.2%} of the cache differs"
-    return len(diff)
-
-
-def _layer_case(cfg, B, P, T, seed, bias_sigma, check_seqs=None, chunk=None, via_init=False, cache_resident=-1):
-    h = cfg.hidden
-    model = fq.Model(h, cfg.heads, cfg.ffn, 1, max_tokens=max(B * P if chunk is None else chunk * P, B),
-                     compress_weight=cfg.compress_weight, compress_cache=cfg.compress_cache,
-                     cache_resident_layers=cache_resident)
-    params = oracle.layer_params(seed, cfg, 0, bias_sigma)
-    if via_init:
-        model.init_random(seed, bias_sigma)
-    else:
-        model.set_layer(0, {n: dev(params[n]) for n in NAMES})
-    torch.cuda.synchronize()
-    if cfg.compress_weight:
-        _check_packed(model, 0, params, cfg)
-    kv = fq.KVCache(model, B, P + T)
-    hidden = synth.normal_f16(seed, synth.STREAM["hidden"], (B, P + T, h), 1.0)
-    hd = dev(hidden)
+def _run_layer(model, kv, hd, B, P, T, cs):
+    """Prefill of P tokens in chunks of cs sequences, then T decode steps; returns
+    the layer outputs [B, P + T, h] on the host."""
+    h = hd.shape[-1]
     x = hd[:, :P].reshape(B * P, h).contiguous()
     y = torch.empty_like(x)
-    cs = B if chunk is None else chunk
     for b0 in range(0, B, cs):
         nb = min(cs, B - b0)
         fq.fq_layer_step(model, 0, kv, b0, nb, P, 0, x[b0 * P:(b0 + nb) * P], y[b0 * P:(b0 + nb) * P])
@@ -152,35 +47,66 @@ def _layer_case(cfg, B, P, T, seed, bias_sigma, check_seqs=None, chunk=None, via
         fq.fq_layer_step(model, 0, kv, 0, B, 1, P + t, xt, yt)
         ys.append(host(yt).reshape(B, 1, h))
     torch.cuda.synchronize()
-    # oracle on the checked sequences
-    seqs = list(range(B)) if check_seqs is None else check_seqs
-    packed = oracle.pack_layer(params, cfg)
-    gcache = _gpu_cache(kv, 0, B, cfg.heads, P + T, cfg.head_dim)
-    for b in seqs:
-        cache = oracle.new_cache(cfg, 1, P + T)
-        want = ("k", "v", "k64", "v64")
-        r = oracle.layer_step(hidden[b:b + 1, :P], params, packed, cache, cfg, 0, want=want)
-        kv16 = {"k": r["k"], "v": r["v"]}
-        kv64 = {"k": r["k64"], "v": r["v64"]}
-        steps = [(ys[0][b], r["y64"][0], f"prefill seq {b}", P)]
-        for t in range(T):
-            r = oracle.layer_step(hidden[b:b + 1, P + t:P + t + 1], params, packed, cache, cfg, P + t, want=want)
-            steps.append((ys[1 + t][b], r["y64"][0], f"decode step {t} seq {b}", P + t + 1))
-            for name in kv16:
-                kv16[name] = np.concatenate([kv16[name], r[name]], 0)
-                kv64[name] = np.concatenate([kv64[name], r[name + "64"]], 0)
-        n_flip = 0
-        for name in ("k", "v"):
-            if cfg.compress_cache:
-                n_flip += _validate_code_differences(gcache[name + "_codes"][b], cache[name + "_codes"][0],
-                                                     kv16[name], cfg, what=f"{name} codes seq {b}")
-            else:
-                n_flip += _validate_f16_differences(gcache[name][b], kv16[name], kv64[name], what=f"{name} seq {b}")
-        for got, ref, what, npos in steps:
-            exact_cache = n_flip == 0
-            _assert_layer_output(got, ref, what, strict_max=exact_cache)
-    kv.close()
+    return np.concatenate(ys, 1)
+
+
+def _layer_case(cfg, B, P, T, seed, bias_sigma, check=None, chunk=None, via_init=False, cache_resident=-1):
+    """The layer over a prefill of P tokens (in chunks of `chunk` sequences) and T
+    decode steps on the GPU, against the oracle under teacher forcing for the
+    sequences check = (b0, nb) (default: all):
+      - the GPU records the fp16 K/V it appends (fq_model_set_capture); the
+        oracle's quantisation of those values equals the GPU cache bit for bit;
+      - the GPU's fp16 K/V are within the layer tolerance of the oracle's own
+        float64 K/V (a storage point of the layer);
+      - every layer output (the prefill block and each decode step) is within
+        relative L2 5e-3 and max |err| 3e-2 of the oracle's float64 value, the
+        oracle attending over that same cache (layer_rows);
+      - a second GPU run without the capture (so with the K/V append fused into
+        the QKV projection at prefill sizes) gives bit-identical outputs and cache."""
+    h, H, d = cfg.hidden, cfg.heads, cfg.head_dim
+    model = fq.Model(h, cfg.heads, cfg.ffn, 1, max_tokens=max(B * P if chunk is None else chunk * P, B),
+                     compress_weight=cfg.compress_weight, compress_cache=cfg.compress_cache,
+                     cache_resident_layers=cache_resident)
+    params = oracle.layer_params(seed, cfg, 0, bias_sigma, workers=16)
+    if via_init:
+        model.init_random(seed, bias_sigma)
+    else:
+        model.set_layer(0, {n: dev(params[n]) for n in NAMES})
+    torch.cuda.synchronize()
+    if cfg.compress_weight:
+        _check_packed(model, 0, params, cfg)
+    S = P + T
+    b0, nb = check if check is not None else (0, B)
+    hidden = synth.normal_f16(seed, synth.STREAM["hidden"], (B, S, h), 1.0)
+    hd = dev(hidden)
+    cs = B if chunk is None else chunk
+    runs = []
+    for capture in (True, False):
+        kv = fq.KVCache(model, B, S)
+        cap = {n: torch.zeros((nb, S, h), dtype=torch.float16, device="cuda:0") for n in ("k16", "v16")}
+        model.set_capture([dict(layer=0, b0=b0, nb=nb, capacity=S, **cap)] if capture else [])
+        y = _run_layer(model, kv, hd, B, P, T, cs)
+        model.set_capture([])
+        runs.append((y, gpu_cache(kv.view(0), B, S), {n: host(t) for n, t in cap.items()}))
+        kv.close()
+    (y, gcache, kvg), (y2, gcache2, _) = runs
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "capture changed the layer's outputs"
+    for name in gcache:
+        assert np.array_equal(gcache[name].view(np.uint8), gcache2[name].view(np.uint8)), name
     model.close()
+    # the oracle's cache holds its quantisation of the GPU's fp16 K/V
+    cache = oracle.new_cache(cfg, nb, S)
+    oracle.cache_fill(cache, cfg, kvg["k16"], kvg["v16"], 0)
+    assert_same_cache({n: g[b0:b0 + nb] for n, g in gcache.items()}, cache, "cache")
+    packed = oracle.pack_layer(params, cfg, workers=16)
+    r = oracle.layer_rows(hidden[b0:b0 + nb], np.arange(S), params, packed, cache, cfg, want=("k64", "v64"))
+    assert_close(kvg["k16"], r["k64"], what="K (fp16 storage point)")
+    assert_close(kvg["v16"], r["v64"], what="V (fp16 storage point)")
+    yb = y[b0:b0 + nb]
+    rel, mx = assert_close(yb[:, :P], r["y64"][:, :P], what="prefill outputs")
+    log(f"prefill: rel_l2 {rel:.2e} max_abs {mx:.2e}")
+    for t in range(T):
+        assert_close(yb[:, P + t], r["y64"][:, P + t], what=f"decode step {t}")
 
 
 @pytest.mark.parametrize("bias_sigma", [0.0, 0.02])
@@ -219,16 +145,18 @@ def test_layer_weight_only_ragged_shapes():
 
 
 def test_layer_ragged_shapes():
-    """head_dim 128, prompt not a multiple of the 64-query tile, odd batch, prefill in chunks."""
+    """head_dim 128, prompt not a multiple of the 64-query tile, odd batch, prefill in
+    chunks of 2 sequences; sequences 1-3 (across chunks) checked."""
     log("layer ragged")
-    _layer_case(LayerConfig(512, 4, 1536), B=5, P=70, T=3, seed=3, bias_sigma=0.02, chunk=2)
+    _layer_case(LayerConfig(512, 4, 1536), B=5, P=70, T=3, seed=3, bias_sigma=0.02, chunk=2, check=(1, 3))
 
 
 @pytest.mark.slow
 def test_layer_opt67b_shape_sampled():
     """One OPT-6.7B-shaped layer (hidden 4096, 32 x 128, FFN 16384), batch 64,
-    prompt 512, 32 decode steps; every sequence runs on the GPU, sequences
-    0 and 45 are checked against the oracle at every position."""
+    prompt 512 (prefill in chunks of 16 sequences), 32 decode steps; every
+    sequence runs on the GPU, sequences 40-47 are checked against the oracle at
+    every position."""
     log("layer OPT-6.7B shape")
     _layer_case(LayerConfig(4096, 32, 16384), B=64, P=512, T=32, seed=0, bias_sigma=0.0,
-                check_seqs=[0, 45], chunk=16, via_init=True)
+                check=(40, 8), chunk=16, via_init=True)

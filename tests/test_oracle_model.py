@@ -239,3 +239,36 @@ def test_layer_step_against_torch_float64_layer():
         assert np.max(np.abs(got - ref)) <= 1e-12, f"step at {pos}: {np.max(np.abs(got - ref))}"
         for key in c_or:
             assert np.array_equal(c_or[key], c_tr[key])
+
+
+def test_layer_rows_teacher_forced_with_own_kv_equals_layer_step():
+    """Teacher forcing with the layer's own K/V reproduces the free-running
+    layer: fill a cache with the K/V that a prefill + decode run of layer_step
+    appended (as fp16, quantised again by cache_fill), then evaluate any
+    subset of rows at their positions -- outputs bit-identical, caches
+    identical, and the rows' own K/V equal to those filled in.  Holds for the
+    4-bit and the fp16 cache."""
+    from oracle import layer_rows, cache_fill
+    for cc in (True, False):
+        cfg = LayerConfig(hidden=256, heads=4, ffn=1024, compress_cache=cc)
+        B, P, T = 2, 9, 3
+        p = layer_params(8, cfg, 0, bias_sigma=0.02)
+        pk = pack_layer(p, cfg)
+        x = _x(B, P + T, 256, seed=8)
+        c = new_cache(cfg, B, P + T)
+        want = ("k", "v")
+        rs = [layer_step(x[:, :P], p, pk, c, cfg, 0, want=want)]
+        for t in range(T):
+            rs.append(layer_step(x[:, P + t:P + t + 1], p, pk, c, cfg, P + t, want=want))
+        y = np.concatenate([r["y"] for r in rs], 1)
+        k16 = np.concatenate([r["k"].reshape(B, -1, 256) for r in rs], 1)
+        v16 = np.concatenate([r["v"].reshape(B, -1, 256) for r in rs], 1)
+        c2 = new_cache(cfg, B, P + T)
+        cache_fill(c2, cfg, k16, v16, 0)
+        for key in c:
+            assert np.array_equal(c[key], c2[key])
+        for rows in (np.arange(P + T), np.array([0, 4, 8, 9, 11])):
+            r = layer_rows(x[:, rows], rows, p, pk, c2, cfg, want=("k", "v"))
+            assert np.array_equal(r["y"].view(np.uint16), y[:, rows].view(np.uint16))
+            assert np.array_equal(r["k"].view(np.uint16), k16[:, rows].view(np.uint16))
+            assert np.array_equal(r["v"].view(np.uint16), v16[:, rows].view(np.uint16))
