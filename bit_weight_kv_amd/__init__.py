@@ -88,6 +88,8 @@ _SIGS = {
     "fq_dequantize": (c_i32, [_P(fq_packed), c_vp, c_vp]),
     "fq_dequant_gemm": (c_i32, [c_vp, c_i64, c_i64, _P(fq_weight), c_vp, c_vp, c_i64, c_u32, c_f32, c_i64, c_vp,
                                 c_i64, c_vp]),
+    "fq_dequant_gemm_noalloc": (c_i32, [c_vp, c_i64, c_i64, _P(fq_weight), c_vp, c_vp, c_i64, c_u32, c_f32, c_i64,
+                                        c_vp, c_i64, c_vp]),
     "fq_kv_append": (c_i32, [_P(fq_kv_layer), c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "fq_decode_attention": (c_i32, [c_vp, c_i64, _P(fq_kv_layer), c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "fq_prefill_attention": (c_i32, [c_vp, c_i64, _P(fq_kv_layer), c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
@@ -181,6 +183,14 @@ def fq_dequant_gemm(A, W, C, bias=None, residual=None, epilogue=0, qscale=1.0, q
     ldr = residual.stride(0) if residual is not None else 0
     _check(_lib.fq_dequant_gemm(_ptr(A), M, A.stride(0), ctypes.byref(W), _ptr(bias), _ptr(residual), ldr,
                                 epilogue, qscale, qscale_cols, _ptr(C), C.stride(0), _stream(stream)))
+
+
+def fq_dequant_gemm_noalloc(A, W, C, bias=None, residual=None, epilogue=0, qscale=1.0, qscale_cols=0, stream=None):
+    """fq_dequant_gemm without any device allocation (split-K partials in the library's fixed scratch)."""
+    M = A.shape[0]
+    ldr = residual.stride(0) if residual is not None else 0
+    _check(_lib.fq_dequant_gemm_noalloc(_ptr(A), M, A.stride(0), ctypes.byref(W), _ptr(bias), _ptr(residual), ldr,
+                                        epilogue, qscale, qscale_cols, _ptr(C), C.stride(0), _stream(stream)))
 
 
 def kv_layer_view(k_codes, k_meta, v_codes, v_meta):

@@ -23,6 +23,8 @@
 // Split-K (grid.z) writes fp32 partials that a second kernel reduces and
 // passes through the epilogue; used when the M x N grid cannot fill 256 CUs.
 #include <cstdlib>
+#include <mutex>
+#include <string>
 #include <type_traits>
 #include <utility>
 
@@ -2093,7 +2095,23 @@ struct Workspace {
 };
 thread_local Workspace g_ws;
 
+// While fq_dequant_gemm_noalloc runs on this thread: the fixed buffer its
+// partials go to (nothing is allocated).
+struct FixedWorkspace {
+  float* ptr;
+  size_t bytes;
+};
+thread_local const FixedWorkspace* g_fixed_ws = nullptr;
+
 fq_status get_workspace(size_t bytes, float** out) {
+  if (g_fixed_ws) {
+    if (bytes > g_fixed_ws->bytes)
+      return fail(FQ_ERR_INVALID, "fq_dequant_gemm_noalloc: this shape needs " + std::to_string(bytes) +
+                                      " bytes of split-K partials, more than the " +
+                                      std::to_string(g_fixed_ws->bytes) + "-byte scratch");
+    *out = g_fixed_ws->ptr;
+    return FQ_OK;
+  }
   int dev = 0;
   FQ_HIP(hipGetDevice(&dev));
   if (g_ws.ptr && (g_ws.bytes < bytes || g_ws.device != dev)) {
@@ -2296,10 +2314,12 @@ static bool use_w4(int64_t K, int64_t lda, const fq_weight* W) {
 }
 
 
-extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
-                                     const uint16_t* bias, const uint16_t* residual, int64_t ldr, uint32_t epilogue,
-                                     float qscale, int64_t qscale_cols, void* C, int64_t ldc, void* stream) {
-  clear_error();
+// The projection GEMM behind both entry points; `timed`: record the launch
+// for fq_timing_* (event creation allocates, so the allocation-free entry
+// point never records).
+static fq_status dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const uint16_t* bias,
+                              const uint16_t* residual, int64_t ldr, uint32_t epilogue, float qscale,
+                              int64_t qscale_cols, void* C, int64_t ldc, void* stream, bool timed) {
   FQ_CHECK_ARG(W != nullptr, "fq_dequant_gemm: W is NULL");
   FQ_CHECK_ARG(W->kind == FQ_WEIGHT_PACKED4 || W->kind == FQ_WEIGHT_F16, "fq_dequant_gemm: unknown weight kind");
   const int64_t N = W->n, K = W->k;
@@ -2327,7 +2347,7 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
   const int KT = (int)(K / 64);
   const bool small_tiles = small_tiles_only();
   const int cls = (epilogue & FQ_EPI_F32OUT) ? FQ_KC_LM_HEAD : (M > 256 ? FQ_KC_GEMM_PREFILL : FQ_KC_GEMM_DECODE);
-  const int tk = timing_begin(cls, st);
+  const int tk = timed ? timing_begin(cls, st) : -1;
   fq_status r;
   if (M <= 256 && !small_tiles) {
     r = dispatch_skinny(A, M, lda, W, epi, st);
@@ -2370,6 +2390,64 @@ extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, 
     timing_end(tk, cls, 2.0 * M * N * K, bytes, st);
   }
   return r;
+}
+
+extern "C" fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
+                                     const uint16_t* bias, const uint16_t* residual, int64_t ldr, uint32_t epilogue,
+                                     float qscale, int64_t qscale_cols, void* C, int64_t ldc, void* stream) {
+  clear_error();
+  return dequant_gemm(A, M, lda, W, bias, residual, ldr, epilogue, qscale, qscale_cols, C, ldc, stream, true);
+}
+
+// ---- allocation-free projection GEMM ---------------------------------------
+// The split-K partials of fq_dequant_gemm_noalloc live in this array, one copy
+// per GPU (kept until the process ends).  Host code never uses its name as an
+// address: the device address of each GPU's copy is looked up once per device
+// (hipGetSymbolAddress, with that device current) and that pointer is what
+// the kernels receive.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+fq_status scratch_for_current_device(float** out) {
+  int dev = 0;
+  FQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FQ_ERR_UNSUPPORTED, "fq_dequant_gemm_noalloc: device index too large");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "fq_dequant_gemm_noalloc: hipGetSymbolAddress");
+    }
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FQ_OK;
+}
+
+// Points get_workspace at the scratch for the duration of one call.
+struct FixedWorkspaceScope {
+  FixedWorkspace ws;
+  explicit FixedWorkspaceScope(float* p) : ws{p, kScratchBytes} { g_fixed_ws = &ws; }
+  ~FixedWorkspaceScope() { g_fixed_ws = nullptr; }
+};
+}  // namespace
+
+extern "C" fq_status fq_dequant_gemm_noalloc(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
+                                             const uint16_t* bias, const uint16_t* residual, int64_t ldr,
+                                             uint32_t epilogue, float qscale, int64_t qscale_cols, void* C,
+                                             int64_t ldc, void* stream) {
+  clear_error();
+  float* ws = nullptr;
+  FQ_TRY(scratch_for_current_device(&ws));
+  FixedWorkspaceScope scope(ws);
+  return dequant_gemm(A, M, lda, W, bias, residual, ldr, epilogue, qscale, qscale_cols, C, ldc, stream, false);
 }
 
 extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,

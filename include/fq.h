@@ -133,6 +133,23 @@ fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_we
                           const uint16_t* residual, int64_t ldr, uint32_t epilogue, float qscale,
                           int64_t qscale_cols, void* C, int64_t ldc, void* stream);
 
+/* fq_dequant_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results (bit for bit), but the fp32
+ * split-K partials of the small-M kernels go to a fixed 64 MiB scratch
+ * array that the library holds in each GPU's memory from its load until the
+ * process ends, instead of a workspace grown with hipMalloc.  The call
+ * allocates nothing and records no fq_timing_* events.
+ *   Errors: those of fq_dequant_gemm, and FQ_ERR_INVALID when a shape would
+ *   need more than 64 MiB of partials (the message gives the size; the
+ *   decode shapes of the OPT-175B workloads need at most about 35 MB).
+ * Calls that overlap on one GPU (several streams or host threads) share that
+ * GPU's scratch and race; serialise them.  Nothing in the scratch needs to
+ * start at zero (every partial read is written first in the same call). */
+fq_status fq_dequant_gemm_noalloc(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W,
+                                  const uint16_t* bias, const uint16_t* residual, int64_t ldr, uint32_t epilogue,
+                                  float qscale, int64_t qscale_cols, void* C, int64_t ldc, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* One layer of KV cache (device memory; caller- or handle-owned).
  * 4-bit cache (bits 4, or 0 in a zero-initialised struct):
