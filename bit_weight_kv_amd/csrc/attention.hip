@@ -7,18 +7,21 @@
 // values are reconstructed in registers (fp32 min + code * scale) and never
 // written back; the kernel reads 0.5625 bytes per cached element.
 //
-// Decode, per (b, h) work-group of 256 threads:
-//   1. scores: thread t takes positions t, t+256, ...; for each it streams the
-//      key's codes (16-byte loads) and computes q . k^ group by group as
-//      s_g * (q . c) + min_g * sum(q_g), so the reconstruction costs no extra
-//      multiply per element;  scores go to LDS;
+// Decode, per (b, h) work-group of 256 threads: each position is covered by
+// D/32 lanes, 16 bytes (32 channels) each, in both passes; lane t takes the
+// positions t / (D/32) + u * 256 / (D/32), u < 9.  The whole first chunk of
+// keys and then of values (576 positions at D = 128) is requested at entry,
+// with nontemporal loads (the cache is read once), so one work-group has all
+// its bytes in flight at once instead of a few rows per pass iteration.
+//   1. scores: per lane s_g * (q . c) + min_g * sum(q) over its 32 channels
+//      (the reconstruction costs no multiply per element), summed over the
+//      position's lanes with DPP; scores go to LDS;
 //   2. softmax with block max / sum reductions (exp2 of log2(e)-scaled scores);
-//   3. values: 16 lanes cover one position's codes (4 bytes = 8 channels per
-//      lane), 16 positions are in flight per block; each lane accumulates
-//      sum_j (p_j s_jg) c_ji -- two positions at a time, as fp32 dot products
-//      of exact fp16 code pairs with the fp16 pair {p_1 s_1, p_2 s_2} -- and
-//      sum_j p_j min_jg in fp32, then the 16 partial sums are reduced through
-//      LDS.
+//   3. values: each lane accumulates sum_j (p_j s_jg) c_ji for its 32 channels
+//      -- two positions at a time, as fp32 dot products of exact fp16 code
+//      pairs with the fp16 pair {p_1 s_1, p_2 s_2} -- and sum_j p_j min_jg in
+//      fp32; the partial sums are reduced over each 16-lane row with DPP row
+//      rotations, then over the 16 rows through LDS.
 //
 // The fp16 cache (cache compression off, weights possibly still compressed)
 // goes through the same kernels instantiated with F16 = true: keys and values
@@ -49,6 +52,21 @@ __device__ inline float block_sum256(float v, float* red) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return red[0] + red[1] + red[2] + red[3];
+}
+
+// v + v from the lane that the DPP control CTRL selects (a lane whose source
+// is outside the row adds 0)
+template <int CTRL>
+__device__ inline float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// 16-byte load of data read once (cache codes): marked nontemporal so it
+// streams through the caches
+__device__ inline uint4 load_stream16(const uint4* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // Codes of 8 consecutive channels (one word) as exact fp16 integers, 4 pairs
@@ -175,87 +193,74 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
     return;
   }
 
-  // ---- query: fp16 pairs in registers, per-group sums of q ----
-  half2_t qv[D / 2];
+  // ---- 4-bit cache: LPP lanes per position in both passes, 16 bytes (32
+  // channels, half a group) each; position j = c0 + slot + u * SLOTS ----
+  constexpr int LPP4 = D / 32;
+  constexpr int SLOTS4 = 256 / LPP4;
+  constexpr int VPOS = 9;                 // positions per lane and chunk
+  constexpr int CH = VPOS * SLOTS4;       // positions per chunk (576 at D = 128)
+  const int slot4 = tid / LPP4, lq = tid % LPP4, grp = lq / 2;
+  uint4 kw[VPOS], vw[VPOS];
+  uint32_t kmeta[VPOS], vmeta[VPOS];
+  auto load_chunk = [&](const uint8_t* codes, const uint16_t* meta, uint4 (&w)[VPOS], uint32_t (&mt)[VPOS],
+                        int c0) {
 #pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    const uint4 r = *reinterpret_cast<const uint4*>(qp + i * 8);
+    for (int u = 0; u < VPOS; ++u) {
+      const int j = c0 + slot4 + u * SLOTS4;
+      if (j < len) {
+        w[u] = load_stream16(reinterpret_cast<const uint4*>(codes + (row0 + j) * (D / 2)) + lq);
+        mt[u] = reinterpret_cast<const uint32_t*>(meta)[(row0 + j) * G + grp];
+      } else {
+        w[u] = make_uint4(0, 0, 0, 0);
+        mt[u] = 0;
+      }
+    }
+  };
+  // the first chunk of keys, then of values, requested before anything else
+  load_chunk(kc, km, kw, kmeta, 0);
+  load_chunk(vc, vm, vw, vmeta, 0);
+
+  // this lane's 32 query channels as fp16 pairs, and their sum
+  half2_t qv[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 r = *reinterpret_cast<const uint4*>(qp + lq * 32 + i * 8);
     qv[4 * i + 0] = __builtin_bit_cast(half2_t, r.x);
     qv[4 * i + 1] = __builtin_bit_cast(half2_t, r.y);
     qv[4 * i + 2] = __builtin_bit_cast(half2_t, r.z);
     qv[4 * i + 3] = __builtin_bit_cast(half2_t, r.w);
   }
-  float qsum[G];
+  float qsum = 0.f;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s += (float)qv[g * 32 + i].x + (float)qv[g * 32 + i].y;
-    qsum[g] = s;
-  }
+  for (int i = 0; i < 16; ++i) qsum += (float)qv[i].x + (float)qv[i].y;
 
-  // ---- scores: two positions per thread and iteration, both positions'
-  // codes requested before either is used (the second clamped to a valid
-  // row and discarded when past the end) ----
+  // ---- scores: s_g (q . c) + min_g sum(q) over this lane's 32 channels,
+  // summed over the position's LPP lanes with DPP ----
   float lmax = -INFINITY;
-  auto score = [&](const uint4 (&c)[2 * G], const uint32_t (&mb)[G]) {
-    float s = 0.f;
+  for (int c0 = 0; c0 < len; c0 += CH) {
+    if (c0 > 0) load_chunk(kc, km, kw, kmeta, c0);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int u = 0; u < VPOS; ++u) {
+      const uint32_t w[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w};
       float dc = 0.f;
 #pragma unroll
-      for (int v4 = 0; v4 < 2; ++v4) {
-        const uint32_t w[4] = {c[g * 2 + v4].x, c[g * 2 + v4].y, c[g * 2 + v4].z, c[g * 2 + v4].w};
+      for (int wd = 0; wd < 4; ++wd) {
+        half2_t cc[4];
+        codes8_cvt(w[wd], cc);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          half2_t cc[4];
-          codes8_cvt(w[k], cc);
-          const int base = (g * 64 + v4 * 32 + k * 8) / 2;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) dc = __builtin_amdgcn_fdot2(cc[u], qv[base + u], dc, false);
-        }
+        for (int i = 0; i < 4; ++i) dc = __builtin_amdgcn_fdot2(cc[i], qv[wd * 4 + i], dc, false);
       }
-      s += h2f((uint16_t)(mb[g] >> 16)) * dc + h2f((uint16_t)(mb[g] & 0xFFFF)) * qsum[g];
-    }
-    return s * kLog2e;
-  };
-  for (int j = tid; j < len; j += 512) {
-    const int jb = min(j + 256, len - 1);
-    const uint4* crow1 = reinterpret_cast<const uint4*>(kc + (row0 + j) * (D / 2));
-    const uint4* crow2 = reinterpret_cast<const uint4*>(kc + (row0 + jb) * (D / 2));
-    uint4 c1[2 * G], c2[2 * G];
-    uint32_t m1[G], m2[G];
-#pragma unroll
-    for (int i = 0; i < 2 * G; ++i) c1[i] = crow1[i];
-#pragma unroll
-    for (int i = 0; i < 2 * G; ++i) c2[i] = crow2[i];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m1[g] = reinterpret_cast<const uint32_t*>(km)[(row0 + j) * G + g];
-      m2[g] = reinterpret_cast<const uint32_t*>(km)[(row0 + jb) * G + g];
-    }
-    const float s1 = score(c1, m1);
-    p[j] = s1;
-    lmax = fmaxf(lmax, s1);
-    if (j + 256 < len) {
-      const float s2 = score(c2, m2);
-      p[j + 256] = s2;
-      lmax = fmaxf(lmax, s2);
+      float sc = h2f((uint16_t)(kmeta[u] >> 16)) * dc + h2f((uint16_t)(kmeta[u] & 0xFFFF)) * qsum;
+      sc = dpp_add<0xB1>(sc);                              // quad_perm [1, 0, 3, 2]: lane pairs
+      if constexpr (LPP4 == 4) sc = dpp_add<0x4E>(sc);     // quad_perm [2, 3, 0, 1]: the quad
+      sc *= kLog2e;
+      const int j = c0 + slot4 + u * SLOTS4;
+      if (j < len) {
+        if (lq == 0) p[j] = sc;
+        lmax = fmaxf(lmax, sc);
+      }
     }
   }
-  // the value pass's first code words are requested before the softmax
-  // reductions (they do not depend on the probabilities), and each
-  // iteration below requests the next one's before its own arithmetic
-  const int g = wl / 8;  // group of this lane's 8 channels
-  uint32_t nw1 = 0, nm1 = 0, nw2 = 0, nm2 = 0;
-  auto load_v = [&](int j) {
-    const int j1 = min(j, len - 1), j2 = min(j + SLOTS, len - 1);  // clamped rows: read, never used
-    nw1 = reinterpret_cast<const uint32_t*>(vc + (row0 + j1) * (D / 2))[wl];
-    nm1 = reinterpret_cast<const uint32_t*>(vm)[(row0 + j1) * G + g];
-    nw2 = reinterpret_cast<const uint32_t*>(vc + (row0 + j2) * (D / 2))[wl];
-    nm2 = reinterpret_cast<const uint32_t*>(vm)[(row0 + j2) * G + g];
-  };
-  load_v(slot);
   const float mx = block_max256(lmax, red);
   float lsum = 0.f;
   for (int j = tid; j < len; j += 256) {
@@ -265,161 +270,55 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   }
   const float inv = 1.0f / block_sum256(lsum, red);  // also orders the p[] writes before the reads below
 
-  // ---- values ----
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // ---- values: positions in pairs, sum_j (p_j s_j) c_jk as fp32 dot
+  // products of the fp16 pairs {c_1k, c_2k} and {p_1 s_1, p_2 s_2}, and
+  // sum_j p_j min_j in fp32 ----
+  float acc[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) acc[k] = 0.f;
   float bsum = 0.f;
-  // two positions per iteration: sum_j (p_j s_j) c_jk as fp32 dot products of
-  // the fp16 pairs {c_1k, c_2k} and {p_1 s_1, p_2 s_2}
-  for (int j = slot; j < len; j += 2 * SLOTS) {
-    const int j2 = j + SLOTS;
-    const bool two = j2 < len;
-    const uint32_t w1 = nw1, mb1 = nm1, w2 = two ? nw2 : 0u, mb2 = two ? nm2 : 0u;
-    if (j + 2 * SLOTS < len) load_v(j + 2 * SLOTS);
-    const float p1 = p[j], p2 = two ? p[j2] : 0.f;
-    bsum += p1 * h2f((uint16_t)(mb1 & 0xFFFF)) + p2 * h2f((uint16_t)(mb2 & 0xFFFF));
-    const half2_t a2 = {(half_t)(p1 * h2f((uint16_t)(mb1 >> 16))), (half_t)(p2 * h2f((uint16_t)(mb2 >> 16)))};
-    half2_t c[8];
-    codes8_pairs(w1, w2, c);
+  for (int c0 = 0; c0 < len; c0 += CH) {
+    if (c0 > 0) load_chunk(vc, vm, vw, vmeta, c0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_fdot2(c[k], a2, acc[k], false);
+    for (int u = 0; u < VPOS; u += 2) {
+      const int j1 = c0 + slot4 + u * SLOTS4, j2 = j1 + SLOTS4;
+      const bool two = u + 1 < VPOS;
+      const float p1 = j1 < len ? p[j1] : 0.f;
+      const float p2 = two && j2 < len ? p[j2] : 0.f;
+      const uint32_t m1 = vmeta[u], m2 = two ? vmeta[u + 1] : 0u;
+      const uint4 w1 = vw[u], w2 = two ? vw[u + 1] : make_uint4(0, 0, 0, 0);
+      bsum += p1 * h2f((uint16_t)(m1 & 0xFFFF)) + p2 * h2f((uint16_t)(m2 & 0xFFFF));
+      const half2_t a2 = {(half_t)(p1 * h2f((uint16_t)(m1 >> 16))), (half_t)(p2 * h2f((uint16_t)(m2 >> 16)))};
+      const uint32_t x1[4] = {w1.x, w1.y, w1.z, w1.w}, x2[4] = {w2.x, w2.y, w2.z, w2.w};
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        half2_t cc[8];
+        codes8_pairs(x1[wd], x2[wd], cc);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[wd * 8 + k] = __builtin_amdgcn_fdot2(cc[k], a2, acc[wd * 8 + k], false);
+      }
+    }
   }
-  float* part = smem + ((len + 3) & ~3);
+  // sum over the slots of each 16-lane row (lanes l, l + LPP4, ... hold the
+  // same channels) with row rotations, then over the 16 rows through LDS
+  auto row_sum = [](float v) {
+    if constexpr (LPP4 == 2) v = dpp_add<0x122>(v);  // row_ror 2
+    v = dpp_add<0x124>(v);                           // row_ror 4
+    return dpp_add<0x128>(v);                        // row_ror 8
+  };
+  float* part = smem + ((len + 3) & ~3);  // [16 rows][D]
+  const int lane = tid & 63, row = (tid >> 6) * 4 + (lane >> 4);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) part[slot * D + wl * 8 + k] = acc[k] + bsum;
+  for (int k = 0; k < 32; ++k) {
+    const float v = row_sum(acc[k] + bsum);
+    if ((lane & 15) < LPP4) part[row * D + lq * 32 + k] = v;
+  }
   __syncthreads();
   if (tid < D) {
     float o = 0.f;
-#pragma unroll 4
-    for (int s2 = 0; s2 < SLOTS; ++s2) o += part[s2 * D + tid];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o += part[r * D + tid];
     out[(int64_t)b * ldo + (int64_t)h * D + tid] = f2h(o * inv);
-  }
-}
-
-// ---- causal prefill: flash-style online softmax on the vector units --------
-// Block = 64 queries of one (b, h); 4 lanes per query, each owning D/4
-// channels.  Keys/values are reconstructed chunk by chunk (64 positions) into
-// LDS as fp32 and read back as broadcasts.
-template <int D, bool F16>
-__global__ __launch_bounds__(256) void prefill_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
-                                                                const uint8_t* __restrict__ kc,
-                                                                const uint16_t* __restrict__ km,
-                                                                const uint8_t* __restrict__ vc,
-                                                                const uint16_t* __restrict__ vm, int H, int64_t cap,
-                                                                int64_t b0, int T, int64_t pos,
-                                                                uint16_t* __restrict__ out, int64_t ldo,
-                                                                const uint16_t* __restrict__ k16,
-                                                                const uint16_t* __restrict__ v16) {
-  constexpr int QT = 64, KC = 64, PART = D / 4, G = D / 64;
-  __shared__ __attribute__((aligned(16))) float Ks[KC][D + 4];
-  __shared__ __attribute__((aligned(16))) float Vs[KC][D + 4];
-
-  const int tid = threadIdx.x;
-  const int qi = tid >> 2, part = tid & 3;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int t0 = blockIdx.x * QT;
-  const int t = t0 + qi;
-  const bool qok = t < T;
-  const int64_t qpos = pos + t;  // absolute position of this query
-  const int64_t row0 = ((b0 + b) * H + h) * cap;
-
-  float qf[PART];
-  {
-    const uint16_t* qp = q + ((int64_t)b * T + (qok ? t : 0)) * ldq + (int64_t)h * D + part * PART;
-#pragma unroll
-    for (int i = 0; i < PART; i += 8) {
-      const uint4 r = *reinterpret_cast<const uint4*>(qp + i);
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        qf[i + 2 * k] = h2f((uint16_t)(w[k] & 0xFFFF)) * kLog2e;
-        qf[i + 2 * k + 1] = h2f((uint16_t)(w[k] >> 16)) * kLog2e;
-      }
-    }
-  }
-  float o[PART];
-#pragma unroll
-  for (int i = 0; i < PART; ++i) o[i] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  const int64_t last_q = pos + min(T, t0 + QT) - 1;  // largest query position in the tile
-  const int64_t nkeys = last_q + 1;
-  for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
-    __syncthreads();
-    // reconstruct KC positions x D channels of K and V: 2*KC*D/8 words over 256 threads
-    for (int wi = tid; wi < 2 * KC * (D / 8); wi += 256) {
-      const int which = wi / (KC * (D / 8));
-      const int r = (wi / (D / 8)) % KC, w8 = wi % (D / 8);
-      const int64_t j = k0 + r;
-      float* dst = which ? &Vs[r][w8 * 8] : &Ks[r][w8 * 8];
-      if constexpr (F16) {
-        if (j < nkeys) {
-          const uint4 r4 = *reinterpret_cast<const uint4*>((which ? v16 : k16) + (row0 + j) * D + w8 * 8);
-          const uint32_t w[4] = {r4.x, r4.y, r4.z, r4.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            dst[2 * k] = h2f((uint16_t)(w[k] & 0xFFFF));
-            dst[2 * k + 1] = h2f((uint16_t)(w[k] >> 16));
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) dst[k] = 0.f;
-        }
-      } else if (j < nkeys) {
-        const uint8_t* cbase = which ? vc : kc;
-        const uint16_t* mbase = which ? vm : km;
-        const uint32_t w = reinterpret_cast<const uint32_t*>(cbase + (row0 + j) * (D / 2))[w8];
-        const uint32_t mb = reinterpret_cast<const uint32_t*>(mbase)[(row0 + j) * G + w8 / 8];
-        const float mn = h2f((uint16_t)(mb & 0xFFFF)), s = h2f((uint16_t)(mb >> 16));
-#pragma unroll
-        for (int k = 0; k < 8; ++k) dst[k] = mn + (float)((w >> (4 * k)) & 0xF) * s;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) dst[k] = 0.f;
-      }
-    }
-    __syncthreads();
-    const int64_t kend = min((int64_t)KC, nkeys - k0);
-    for (int r = 0; r < kend; ++r) {
-      const int64_t j = k0 + r;
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < PART; i += 4) {
-        const float4 kv = *reinterpret_cast<const float4*>(&Ks[r][part * PART + i]);
-        s += qf[i] * kv.x + qf[i + 1] * kv.y + qf[i + 2] * kv.z + qf[i + 3] * kv.w;
-      }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      if (!qok || j > qpos) continue;  // causal mask (uniform across the 4 lanes of a query)
-      if (s > m) {
-        const float c = exp2f(m - s);
-        l *= c;
-#pragma unroll
-        for (int i = 0; i < PART; ++i) o[i] *= c;
-        m = s;
-      }
-      const float pj = exp2f(s - m);
-      l += pj;
-#pragma unroll
-      for (int i = 0; i < PART; i += 4) {
-        const float4 vv = *reinterpret_cast<const float4*>(&Vs[r][part * PART + i]);
-        o[i] += pj * vv.x;
-        o[i + 1] += pj * vv.y;
-        o[i + 2] += pj * vv.z;
-        o[i + 3] += pj * vv.w;
-      }
-    }
-  }
-  if (qok) {
-    const float inv = 1.0f / l;
-    uint16_t* op = out + ((int64_t)b * T + t) * ldo + (int64_t)h * D + part * PART;
-#pragma unroll
-    for (int i = 0; i < PART; i += 8) {
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = (uint32_t)f2h(o[i + 2 * k] * inv) | ((uint32_t)f2h(o[i + 2 * k + 1] * inv) << 16);
-      *reinterpret_cast<uint4*>(op + i) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
   }
 }
 
@@ -735,14 +634,6 @@ void by_format(const fq_kv_layer& kv, F&& launch) {
 
 using namespace fq;
 
-// Test hook: FQ_PREFILL_VECTOR=1 in the environment at the time of the call
-// selects the vector-unit prefill kernel (fp32 reconstruction) instead of the
-// matrix-core one.
-static bool prefill_vector_only() {
-  const char* e = getenv("FQ_PREFILL_VECTOR");
-  return e && e[0] == '1';
-}
-
 extern "C" fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
                                          int64_t len, uint16_t* out, int64_t ldo, void* stream) {
   clear_error();
@@ -786,23 +677,13 @@ extern "C" fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const 
                "fq_prefill_attention: q/out NULL or misaligned");
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(FQ_KC_PREFILL_ATTN, st);
-  if (!prefill_vector_only()) {
-    const dim3 grid((unsigned)ceil_div(T, 128), (unsigned)kv->heads, (unsigned)B);
-    by_format(*kv, [&](auto d, auto f16) {
-      prefill_attention_mfma_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), 0, st>>>(
-          q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos, out,
-          ldo, kv->k16, kv->v16);
-    });
-    FQ_TRY(launch_check("prefill_attention_mfma_kernel"));
-  } else {
-    const dim3 grid((unsigned)ceil_div(T, 64), (unsigned)kv->heads, (unsigned)B);
-    by_format(*kv, [&](auto d, auto f16) {
-      prefill_attention_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), 0, st>>>(
-          q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos, out,
-          ldo, kv->k16, kv->v16);
-    });
-    FQ_TRY(launch_check("prefill_attention_kernel"));
-  }
+  const dim3 grid((unsigned)ceil_div(T, 128), (unsigned)kv->heads, (unsigned)B);
+  by_format(*kv, [&](auto d, auto f16) {
+    prefill_attention_mfma_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), 0, st>>>(
+        q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos, out,
+        ldo, kv->k16, kv->v16);
+  });
+  FQ_TRY(launch_check("prefill_attention_mfma_kernel"));
   if (tk >= 0) {
     const double units = (double)B * kv->heads, d = kv->head_dim, epb = kv_is_f16(*kv) ? 2.0 : 0.5625;
     const double pairs = (double)T * pos + (double)T * (T + 1) / 2.0;  // (query, key) pairs under the causal mask

@@ -591,15 +591,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const uint16_t* __restric
 // falls back to waiting for all of them once a kernel has many copy sites.)
 // M0 holds the wave-uniform LDS base; each lane's data lands at
 // base + lane * size.  One wait state separates the M0 write from the copy.
-__device__ inline void dma_lds16(const void* g, uint32_t lds_base) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
-}
-__device__ inline void dma_lds4(const void* g, uint32_t lds_base) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
-}
-// The same copies addressed as a wave-uniform 64-bit base (SGPRs) plus a
+// The copies are addressed as a wave-uniform 64-bit base (SGPRs) plus a
 // 32-bit per-lane byte offset: half the per-lane address bytes, and a base
 // that advances with scalar adds only.
 __device__ inline void dma_lds16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
@@ -610,19 +602,27 @@ __device__ inline void dma_lds4_s(uint32_t voff, const void* sbase, uint32_t lds
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
-// acc += a * b (16x16x32 fp16 MFMA) with the accumulator pinned to AGPRs.
-// Through the builtin, a wave holding 256 accumulators gets part of them
-// assigned to VGPRs and copied around every MFMA.  Consumers of acc after the
-// last call must wait out the MFMA latency themselves.
-__device__ inline void mfma16x16x32_acc(float4_t& acc, const half8_t& a, const half8_t& b) {
-  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// The same, kept in program order relative to every other ordered MFMA (the
-// compiler's scheduler would otherwise reorder them and wait for all
-// fragment reads before the first one).
+// acc += a * b (16x16x32 fp16 MFMA) with the accumulator pinned to AGPRs
+// (through the builtin, a wave holding 256 accumulators gets part of them
+// assigned to VGPRs and copied around every MFMA), kept in program order
+// relative to every other such MFMA (the compiler's scheduler would otherwise
+// reorder them and wait for all fragment reads before the first one).  The
+// compiler does not see these as MFMAs, so it inserts no wait between the
+// last one and a read of its result: kernels end their MFMA chains with
+// mfma_results_ready.
 __device__ inline void mfma16x16x32_acc_ordered(float4_t& acc, const half8_t& a, const half8_t& b) {
   asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
+// After the last MFMA of a chain: wait out the MFMA write -> VALU read
+// latency (24 wait states, more than a 16x16x32 MFMA's 8 passes need) before
+// the accumulators are read.  Nothing ties a compiler-generated register read
+// to this statement, so the order is checked instead: a CPU test compiles
+// this file to assembly and requires that no accumulator read, write or move
+// lies between a kernel's first inline-asm MFMA and this wait, and that no
+// such kernel spills.  (Binding the accumulators to empty statements after
+// the wait made the register allocator move them before it.)
+__device__ inline void mfma_results_ready() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // Four MFMAs (acc_j += a * b_j) with the reconstruction of one 8-code word
 // interleaved between them: a wave's VALU work overlaps its own MFMAs only
@@ -730,12 +730,6 @@ __device__ inline void mfma4_rebuild_h2(float4_t& c0, float4_t& c1, float4_t& c2
   out = __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
 }
 
-__device__ inline void mfma4_rebuild(float4_t& c0, float4_t& c1, float4_t& c2, float4_t& c3, const half8_t& a,
-                                     const half8_t& b0, const half8_t& b1, const half8_t& b2, const half8_t& b3,
-                                     uint32_t w, uint32_t ms, half8_t& out) {
-  mfma4_rebuild_ab(c0, c1, c2, c3, a, a, a, a, b0, b1, b2, b3, w, ms, out);
-}
-
 // One row's 16 accumulators of a K or V group (columns nw + cs .. nw + cs + 15
 // of the 64-column group starting at nw): bias, one rounding to fp16 (the
 // value the unfused path stores in C), then the fp16 cache store or the 4-bit
@@ -785,251 +779,6 @@ __device__ inline void kv_append_epilogue(const Epilogue& e, const KvAppend& kv,
   if (cs == 0) reinterpret_cast<uint32_t*>(is_v ? kv.vm : kv.km)[row * (kv.d / 64) + ch / 64] = mb;
 }
 
-// ---- large-M kernel, 256 x 256 tiles (packed weights) ------------------------
-// 64-byte rows: chunk c of row r sits at slot c ^ swz4(r) (8 consecutive rows
-// read or written at one chunk hit 8 distinct 16-byte bank groups).
-__device__ inline int swz4(int r) { return (r >> 1) & 3; }
-
-// 8 waves in 2 x 4, each 128 x 64 (8 x 4 MFMA 16x16x32 tiles, 128 fp32
-// accumulators pinned to AGPRs): two waves per SIMD, so one wave's LDS
-// latency, reconstruction and barrier waits overlap the other wave's MFMAs.
-// K step 32 (one MFMA k slice).  Per flop this moves half the activation
-// bytes of the 256 x 128 tile.
-//   * A: four LDS stages of 256 rows x 64 bytes; step kt+3's copies are
-//     issued during step kt.  Per step each wave copies 2 KiB of A (two
-//     instructions), half a KiB of codes and 128 bytes of {min, scale} (one
-//     instruction each on lanes 0-31): 4 copies per wave per step, so one
-//     vmcnt value serves every wave.
-//   * codes: four slots of 256 rows x (16 code bytes + 4 {min, scale}
-//     bytes); step kt+4's copies are issued during step kt.  Step kt+1's
-//     codes are reconstructed into the other of two fp16 B stages between the
-//     MFMAs of step kt, half a weight row per thread.
-//   * one barrier per step; the wait before it leaves the copies of this step
-//     and the previous one in flight.
-//   * KVA: the K and V columns go to the cache (KvAppend) instead of C.
-template <bool KVA>
-__global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
-                                                         const uint8_t* __restrict__ codes,
-                                                         const uint16_t* __restrict__ meta, int64_t N, int64_t K,
-                                                         Epilogue epi, KvAppend kva) {
-  constexpr int BMx = 256, BNx = 256, TM = 128, TN = 64, FM = 8, FN = 4, BKx = 32;
-  constexpr int ROWB = BKx * 2;                   // 64 bytes per staged row
-  constexpr int A_BYTES = BMx * ROWB;             // 16 KiB
-  constexpr int B_BYTES = BNx * ROWB;             // 16 KiB
-  constexpr int CODE_BYTES = BNx * 16 + BNx * 4;  // 5 KiB
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds0[A_BYTES], a_lds1[A_BYTES], a_lds2[A_BYTES],
-      a_lds3[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t b_lds0[B_BYTES], b_lds1[B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t c_lds[4 * CODE_BYTES];
-  auto a_st = [&](auto s) -> uint8_t* {
-    constexpr int S = decltype(s)::value;
-    return S == 0 ? a_lds0 : S == 1 ? a_lds1 : S == 2 ? a_lds2 : a_lds3;
-  };
-  auto b_st = [&](auto s) -> uint8_t* {
-    constexpr int S = decltype(s)::value;
-    return S == 0 ? b_lds0 : b_lds1;
-  };
-  auto c_st = [&](auto s) -> uint8_t* { return c_lds + decltype(s)::value * CODE_BYTES; };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-
-  // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 4 M
-  // tiles x 8 N tiles
-  const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
-  const int64_t nblk = tiles_m * tiles_n;
-  const int64_t bid = blockIdx.x;
-  int64_t lid = bid;
-  {
-    const int64_t per_xcd = nblk / 8;
-    if (bid < per_xcd * 8) lid = (bid % 8) * per_xcd + bid / 8;
-  }
-  constexpr int GM = 4;
-  const int64_t group = lid / (GM * tiles_n);
-  const int64_t first_m = group * GM;
-  const int64_t gsize = min((int64_t)GM, tiles_m - first_m);
-  const int64_t in_group = lid - group * GM * tiles_n;
-  const int64_t m0 = (first_m + in_group % gsize) * BMx, n0 = (in_group / gsize) * BNx;
-  const int KT = (int)(K / BKx);
-
-  // A copies: instruction q (0..15) fills rows 16q..16q+15 (lane -> row
-  // lane >> 2, slot lane & 3, fetching chunk slot ^ swz4(row)); wave w
-  // issues q = w and q = w + 8
-  const int cp_r = lane >> 2, cp_c = lane & 3;
-  const uint16_t* a_src[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (8 * i + wave) + cp_r;
-    a_src[i] = A + min(m0 + r, M - 1) * lda + (cp_c ^ swz4(r)) * 8;
-  }
-  auto issue_a = [&](auto s, int kt) {
-    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + wave * 1024;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma_lds16(a_src[i] + (int64_t)kt * BKx, dst + i * 8192);
-  };
-  // codes: wave w copies rows 32w..32w+31 on lanes 0-31
-  const int64_t code_row = min(n0 + wave * 32 + (lane & 31), N - 1);
-  const uint8_t* code_src = codes + code_row * (K / 2);
-  const uint16_t* meta_src = meta + code_row * (K / 64) * 2;
-  auto issue_codes = [&](auto s, int kt) {
-    const uint32_t dst = (uint32_t)(uintptr_t)c_st(s);
-    if (lane < 32) {
-      dma_lds16(code_src + (int64_t)kt * 16, dst + wave * 512);
-      dma_lds4(meta_src + (int64_t)(kt >> 1) * 2, dst + BNx * 16 + wave * 128);
-    }
-  };
-  // reconstruction: thread -> (row tid / 2, chunks 2 (tid & 1) and +1)
-  const int b_row = tid >> 1, b_half = tid & 1;
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 cw = {0, 0};
-  uint32_t cm = 0;
-  auto read_codes = [&](auto s) {
-    const uint32_t base = (uint32_t)(uintptr_t)c_st(s);
-    const uint32_t ca = base + b_row * 16 + b_half * 8, ma = base + BNx * 16 + b_row * 4;
-    u32x2 v;
-    uint32_t mv;
-    asm volatile(
-        "ds_read_b64 %0, %2\n\t"
-        "ds_read_b32 %1, %3\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v), "=&v"(mv)
-        : "v"(ca), "v"(ma)
-        : "memory");
-    cw = v;
-    cm = mv;
-  };
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  auto store_b_word = [&](auto s, int q, const half8_t& v) {
-    const int c = b_half * 2 + q;
-    const uint32_t addr = (uint32_t)(uintptr_t)(b_st(s) + b_row * ROWB + ((c ^ swz4(b_row)) * 16));
-    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
-  };
-  auto store_b = [&](auto s, int q) {
-    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm & 0xFFFF));
-    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm >> 16));
-    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-    uint32_t o[4];
-    dequant8(cw[q], mn2, s2, o);
-    store_b_word(s, q, __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3])));
-  };
-
-  float4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  // prologue (K is a multiple of 128: KT >= 4 and a multiple of 4)
-  issue_codes(I0{}, 0);
-  issue_codes(I1{}, 1);
-  issue_codes(I2{}, 2);
-  issue_codes(I3{}, 3);
-  issue_a(I0{}, 0);
-  issue_a(I1{}, 1);
-  issue_a(I2{}, 2);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  read_codes(I0{});
-  store_b(I0{}, 0);
-  store_b(I0{}, 1);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  const int fr = lane & 15, fk = lane >> 4;
-  // step kt: A stage and code slot kt % 4 (S), B stage kt % 2.  Every step
-  // but the last four issues step kt+4's codes and step kt+3's A and leaves
-  // this step's and the previous step's copies in flight (8 per wave); step
-  // KT-4 issues step KT-1's A only; the last four wait for every copy.  The
-  // conditions are run-time branches around the copies and waits only: the
-  // MFMA chain is the same code in every step (a branch around MFMAs makes
-  // the register allocator copy accumulators at the join).
-  auto step = [&](auto s, int kt) {
-    constexpr int S = decltype(s)::value;
-    using SB = std::integral_constant<int, S % 2>;
-    using SB1 = std::integral_constant<int, (S + 1) % 2>;
-    using S1 = std::integral_constant<int, (S + 1) % 4>;
-    using S3 = std::integral_constant<int, (S + 3) % 4>;
-    read_codes(S1{});  // step kt+1 (stale but harmless past the last step)
-    if (kt + 4 < KT) issue_codes(s, kt + 4);
-    if (kt + 3 < KT) issue_a(S3{}, kt + 3);
-    const uint8_t* As_ = a_st(s);
-    const uint8_t* Bs_ = b_st(SB{});
-    half8_t bf[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = wn * TN + j * 16 + fr;
-      bf[j] = *reinterpret_cast<const half8_t*>(Bs_ + r * ROWB + ((fk ^ swz4(r)) * 16));
-    }
-    auto a_frag = [&](int i) {
-      const int r = wm * TM + i * 16 + fr;
-      return *reinterpret_cast<const half8_t*>(As_ + r * ROWB + ((fk ^ swz4(r)) * 16));
-    };
-    half8_t af = a_frag(0);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const half8_t an = a_frag(i + 1 < FM ? i + 1 : i);
-      if ((i & 3) == 1) {
-        // the MFMAs of this row block carry the reconstruction of code word
-        // q; past the last step it rewrites a stage nobody reads
-        const int q = i >> 2;
-        half8_t nb;
-        mfma4_rebuild(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, bf[0], bf[1], bf[2], bf[3], cw[q], cm, nb);
-        store_b_word(SB1{}, q, nb);
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bf[j]);
-      }
-      af = an;
-    }
-    if (kt + 4 < KT)
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(I0{}, kt);
-    step(I1{}, kt + 1);
-    step(I2{}, kt + 2);
-    step(I3{}, kt + 3);
-  }
-  // the last MFMAs' results are read by VALU instructions below: wait out
-  // the MFMA write -> VALU read latency the compiler cannot see
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-
-  // epilogue staged through LDS, 16 rows x 64 columns per wave at a time
-  // (row stride 68 floats), wave w in half (w & 1) of A stage w / 2
-  {
-    constexpr int SROW = 68;
-    uint8_t* region = (wave >> 1) == 0 ? a_lds0 : (wave >> 1) == 1 ? a_lds1 : (wave >> 1) == 2 ? a_lds2 : a_lds3;
-    float* stg = reinterpret_cast<float*>(region + (wave & 1) * 8192);
-    const bool vec = epilogue_vec_ok(epi);
-    const int rr = lane >> 2, cs = (lane & 3) * 16;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) stg[(4 * (lane >> 4) + r) * SROW + j * 16 + (lane & 15)] = acc[i][j][r];
-      __syncthreads();
-      const int64_t m = m0 + wm * TM + i * 16 + rr;
-      const int64_t nw = n0 + wn * TN;  // this wave's 64 columns: one quantisation group of one head
-      if (KVA && nw >= kva.h && nw < N) {
-        if (m < M) kv_append_epilogue(epi, kva, stg + rr * SROW + cs, m, nw, cs);
-      } else if (m < M) {
-        for (int c = 0; c < 16; c += 8) {
-          const float4 lo = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c);
-          const float4 hi = *reinterpret_cast<const float4*>(stg + rr * SROW + cs + c + 4);
-          const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          epilogue_store8(epi, m, nw + cs + c, v, N, vec);
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // ---- large-M kernel, one wave per SIMD, weight operand rebuilt in registers --
 // 256 x 256 block tile, 4 waves side by side in N, each 256 x 64 (16 x 4 MFMA
 // 16x16x32 tiles, 256 fp32 accumulators pinned to AGPRs), K step 64 (two
@@ -1048,9 +797,9 @@ __global__ __launch_bounds__(512) void gemm_wide8_kernel(const uint16_t* __restr
 //   * one barrier per step; the wait before it leaves this step's copies in
 //     flight, so the next step's A stage is complete one step early and its
 //     first fragments are read before the barrier.
-// Against the 8-wave kernel: the same order of additions (identical
-// outputs), no fp16 B tile in LDS, and half the reconstruction work per
-// flop of a 2 x 2 arrangement of the same waves.
+// No fp16 B tile in LDS (an earlier 8-wave design staged one, written once and
+// read by every wave), and half the reconstruction work per flop of a 2 x 2
+// arrangement of the same waves.
 //
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): an
 // unrolled loop whatever the optimiser decides (an array indexed by the loop
@@ -1282,9 +1031,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   // the last steps' copies land in stages the epilogue reuses
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  // the last MFMAs' results are read by VALU instructions below: wait out
-  // the MFMA write -> VALU read latency the compiler cannot see
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // the last MFMAs' results are read by VALU instructions below
+  mfma_results_ready();
 
   // epilogue staged through LDS, 16 rows x 64 columns per wave at a time
   // (row stride 68 floats), wave w in half (w & 1) of A stage w / 2
@@ -1466,186 +1214,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* __rest
   }
 }
 
-// ---- 4-bit decode GEMM (M <= 256) --------------------------------------------
-// A block owns 256 weight rows (64 per wave) and every row of A (16*MB).
-// The weight stream is the traffic, so it is kept deep in flight: per K step
-// (64 = one quantisation group) the block copies the step's A tile (swizzled
-// 128-byte rows), its codes (256 rows x 32 B) and {min, scale} (256 x 4 B)
-// global -> LDS with direct copies into a ring of S stages, issued S-1 steps
-// ahead (every wave issues the same PER copies per step: its share of the A
-// tile, and the codes/meta of its own 64 rows).  Each lane reconstructs its
-// own MFMA B operand from 8 code bytes per weight row (the 16 k values it
-// contributes to the step's two 32-wide slices, chunk 2g+ks of lane group g),
-// one step ahead: step kt+1's operand is rebuilt between step kt's MFMAs.
-// One barrier per step; the wait before it leaves S-3 steps of copies in
-// flight.  Split-K across blocks (grid.y) with fp32 partials as before.
-template <int MB>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(const uint16_t* __restrict__ A, int64_t M, int64_t lda,
-                                                          const uint8_t* __restrict__ codes,
-                                                          const uint16_t* __restrict__ meta, int64_t N, int64_t K,
-                                                          int k_tiles_per_split, Epilogue epi,
-                                                          float* __restrict__ partial) {
-  constexpr int ROWS = MB * 16, ROWS_PAD = (ROWS + 31) / 32 * 32;
-  constexpr int A_INSTR = ROWS_PAD / 32;  // A copies per wave per step (8 rows of 128 B each)
-  constexpr int PER = A_INSTR + 3;        // + two codes copies + one {min, scale} copy
-  constexpr int A_BYTES = ROWS_PAD * 128, C_BYTES = 256 * 32, STAGE = A_BYTES + C_BYTES + 256 * 4;
-  constexpr int S = 5;
-  static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
-  static_assert(MB >= 4, "at least 8 MFMA groups per step carry the 8 reconstructions");
-  static_assert((S - 3) * PER <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int64_t n_blk = (int64_t)blockIdx.x * 256;
-  const int64_t m_base = (int64_t)blockIdx.z * ROWS;
-  const int KT = (int)(K / BK);
-  const int kt0 = blockIdx.y * k_tiles_per_split;
-  const int kt1 = min(KT, kt0 + k_tiles_per_split);
-
-  // A copies: instruction q = wave + 4t fills rows 8q..8q+7 (lane -> row
-  // 8q + lane / 8, slot lane % 8 holding chunk slot ^ (row % 8)); rows past M
-  // are clamped (read, never stored)
-  const uint16_t* a_src[A_INSTR];
-#pragma unroll
-  for (int t = 0; t < A_INSTR; ++t) {
-    const int r = 8 * (wave + 4 * t) + (lane >> 3);
-    a_src[t] = A + min(m_base + r, M - 1) * lda + ((lane & 7) ^ (r & 7)) * 8;
-  }
-  const uint8_t* c_src[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    c_src[i] = codes + min(n_blk + wave * 64 + i * 32 + (lane >> 1), N - 1) * (K / 2) + (lane & 1) * 16;
-  const uint16_t* m_src = meta + min(n_blk + wave * 64 + lane, N - 1) * (K / 64) * 2;
-  auto issue = [&](int kt, int slot) {
-    const uint32_t st = lds_base + slot * STAGE;
-#pragma unroll
-    for (int t = 0; t < A_INSTR; ++t) dma_lds16(a_src[t] + (int64_t)kt * BK, st + (wave + 4 * t) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma_lds16(c_src[i] + (int64_t)kt * 32, st + A_BYTES + (wave * 64 + i * 32) * 32);
-    dma_lds4(m_src + (int64_t)kt * 2, st + A_BYTES + C_BYTES + wave * 256);
-  };
-  // this lane's weight rows: wave * 64 + 16 j + l16
-  uint2 cw[4];
-  uint32_t cm[4];
-  auto read_codes = [&](int slot) {
-    const uint8_t* st = lds + slot * STAGE + A_BYTES;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wave * 64 + j * 16 + l16;
-      cw[j] = *reinterpret_cast<const uint2*>(st + row * 32 + g4 * 8);
-      cm[j] = *reinterpret_cast<const uint32_t*>(st + C_BYTES + row * 4);
-    }
-  };
-  auto rebuild = [&](int e, half8_t (&b)[2][4]) {  // e = 4 * word + row
-    const int j = e & 3, w = e >> 2;
-    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
-    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
-    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-    uint32_t o[4];
-    dequant8(w ? cw[j].y : cw[j].x, mn2, s2, o);
-    b[w][j] = __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
-  };
-
-  float4_t acc[MB][4];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  if (kt0 < kt1) {
-    for (int t = 0; t < S - 1 && kt0 + t < kt1; ++t) issue(kt0 + t, t);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    half8_t bA[2][4], bB[2][4];
-    read_codes(0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rebuild(e, bA);
-    // One K step: MFMAs on `bcur`, step kt+1's operand rebuilt into `bnxt`
-    // (interleaved with the MFMAs: reconstruction d goes with MFMA group
-    // d * 2MB / 8 of the 2MB groups).  Steps alternate the
-    // two operand buffers, so no register copy sits before an MFMA.
-    auto step = [&](int kt, half8_t (&bcur)[2][4], half8_t (&bnxt)[2][4]) {
-      const int it = kt - kt0, slot = it % S;
-      if (kt > kt0) {
-        // steps kt and kt+1 complete in every wave; step kt-1's slot free
-        if (kt + S - 2 < kt1)
-          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 3) * PER) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      }
-      if (kt + S - 1 < kt1) issue(kt + S - 1, (it + S - 1) % S);
-      const bool ahead = kt + 1 < kt1;
-      if (ahead) read_codes((it + 1) % S);
-      const uint8_t* As_ = lds + slot * STAGE;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // the slice's A fragments requested up front, in the order the MFMAs
-        // use them (LDS reads complete in order, so each MFMA group waits
-        // only for its own fragment)
-        half8_t af[MB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int r = i * 16 + l16, ch = 2 * g4 + ks;
-          af[i] = *reinterpret_cast<const half8_t*>(As_ + r * 128 + ((ch ^ (r & 7)) * 16));
-          __builtin_amdgcn_sched_barrier(0);  // issue in use order
-        }
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int g = ks * MB + i;
-          int d = -1;  // the reconstruction carried by group g, if any
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e * 2 * MB / 8 == g) d = e;
-          // (past the last step this rebuilds stale codes into an unused
-          // buffer: a runtime condition here would split the MFMA chain)
-          if (d >= 0) {
-            const int j = d & 3, w = d >> 2;
-            mfma4_rebuild(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af[i], bcur[ks][0], bcur[ks][1], bcur[ks][2],
-                          bcur[ks][3], w ? cw[j].y : cw[j].x, cm[j], bnxt[w][j]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) mfma16x16x32_acc_ordered(acc[i][j], af[i], bcur[ks][j]);
-          }
-        }
-      }
-    };
-    // pairs of steps: every split has an even number of steps (the host
-    // guarantees it), so the MFMA chain is one piece of code -- a separate
-    // odd last step makes the register allocator move the accumulators
-    // through VGPRs next to MFMAs it cannot see
-    for (int kt = kt0; kt < kt1; kt += 2) {
-      step(kt, bA, bB);
-      step(kt + 1, bB, bA);
-    }
-    // the last MFMAs' results are read by VALU instructions below
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  }
-
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n_blk + wave * 64 + j * 16 + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m_base + i * 16 + 4 * g4 + r;
-        if (m < M && n < N) {
-          if (partial)
-            partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
-          else
-            epilogue_store(epi, m, n, acc[i][j][r]);
-        }
-      }
-    }
-  }
-}
-
 // ---- 4-bit decode GEMM, two waves per SIMD ----------------------------------
-// The same block tile and copy ring as gemm_decode_kernel (256 weight rows x
-// every row of A, K step 64), with 8 waves of 32 weight rows each: two waves
-// share a SIMD, so one wave's LDS and barrier waits overlap the other's
-// MFMAs.  Per K step a wave runs 2 slices x MB row blocks x 2 MFMAs and
+// The fallback of the one-wave-per-SIMD decode kernel below, for K-step
+// counts that are not a multiple of 4 or a {min, scale} array that is not
+// 16-byte aligned.  A block owns 256 weight rows and every row of A (16*MB);
+// per K step (64 = one quantisation group) it copies the step's A tile
+// (swizzled 128-byte rows), its codes (256 rows x 32 B) and {min, scale}
+// global -> LDS with direct copies into a ring of stages issued ahead, and
+// each lane rebuilds its own MFMA B operand from 8 code bytes per weight row
+// one step ahead.  8 waves of 32 weight rows each: two waves share a SIMD, so
+// one wave's LDS and barrier waits overlap the other's MFMAs.  Per K step a wave runs 2 slices x MB row blocks x 2 MFMAs and
 // rebuilds 4 operand words for the next step (its 2 rows x 2 slices), each
 // carried by the 4 MFMAs of a pair of row blocks.
 //
@@ -1822,7 +1400,7 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
       }
     }
     // the last MFMAs' results are read by VALU instructions below
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    mfma_results_ready();
   }
 
 #pragma unroll
@@ -1851,8 +1429,9 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
 // scale} 4 steps at a time) and split-K over ranges of a multiple of 4 steps.
 // Slot = 16-row block of one k slice (2 MB slots per step): copies in slots
 // 0..7, rebuilds (full, 13 instructions with 4 MFMAs) in the last 8 slots.
-// Slice ks gives lane group g the k chunk 2 g + ks (8 values), as the 8-wave
-// decode kernel does, so the two add the same products in the same order.
+// Slice ks gives lane group g the k chunk 2 g + ks (8 values), as the
+// two-waves-per-SIMD decode kernel does, so the two add the same products in
+// the same order (outputs identical bit for bit).
 template <int MB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_decode_w4_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t lda, const uint8_t* __restrict__ codes,
@@ -2033,7 +1612,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     step(I3{}, kt + 3);
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  mfma_results_ready();  // the last MFMAs' results are read below
 
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -2181,12 +1760,6 @@ int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB) {
   return best;
 }
 
-// Test/benchmark hook: FQ_DECODE_WAVES=4 selects the 4-wave decode kernel.
-static bool decode_four_waves() {
-  const char* e = getenv("FQ_DECODE_WAVES");
-  return e && e[0] == '4';
-}
-
 template <int MB>
 fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W, const Epilogue& epi,
                      hipStream_t st) {
@@ -2203,24 +1776,15 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
   float* partial = nullptr;
   if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
   const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)splits, (unsigned)zb);
-  // one wave per SIMD when the {min, scale} go 4 steps at a time; test hook:
-  // FQ_DECODE_W4=0 in the environment selects the 8-wave kernel instead
-  const char* ew = getenv("FQ_DECODE_W4");
-  if (meta4 && !(ew && ew[0] == '0') && !decode_four_waves()) {
+  // one wave per SIMD when the {min, scale} go 4 steps at a time, else the
+  // two-waves-per-SIMD kernel
+  if (meta4) {
     gemm_decode_w4_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps,
                                                           epi, partial);
     FQ_TRY(launch_check("gemm_decode_w4_kernel"));
-  } else if (decode_four_waves()) {
-    gemm_decode_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps, epi,
-                                                       partial);
-    FQ_TRY(launch_check("gemm_decode_kernel"));
   } else {
-    if (meta4)
-      gemm_decode8_kernel<MB, true><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,
-                                                                kps, epi, partial);
-    else
-      gemm_decode8_kernel<MB, false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,
-                                                                 kps, epi, partial);
+    gemm_decode8_kernel<MB, false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,
+                                                               kps, epi, partial);
     FQ_TRY(launch_check("gemm_decode8_kernel"));
   }
   if (splits > 1) {
@@ -2285,32 +1849,15 @@ fq_status run_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_weight* W
 
 using namespace fq;
 
-// Shapes the 256 x 256 kernels take: packed weights, K a multiple of 128 and
-// enough tiles to fill the chip.
-static bool tile256_fits(int64_t M, int64_t N, int64_t K, const fq_weight* W) {
-  return M >= 1024 && N >= 1024 && K % 128 == 0 && ceil_div(M, 256) * ceil_div(N, 256) >= 128 &&
-         W->kind == FQ_WEIGHT_PACKED4;
-}
-
-// Test hook: FQ_GEMM_SMALL_TILES=1 in the environment at the time of the call
-// routes every GEMM to the 128x128 kernel (lets the tests compare the kernels).
-static bool small_tiles_only() {
-  const char* e = getenv("FQ_GEMM_SMALL_TILES");
-  return e && e[0] == '1';
-}
-
-// Among shapes the 256 x 256 tiles take: the one-wave-per-SIMD kernel where
-// its K loop applies (K a multiple of 256), its 32-bit per-lane copy offsets
-// cannot overflow (up to 255 rows of lda or K / 2 bytes past the block's
-// first row) and the {min, scale} array is 16-byte aligned (copied 16 bytes
-// per row), else the 8-wave kernel.  Test hook: FQ_GEMM_W4=0 in the
-// environment at the time of the call selects the 8-wave kernel for every
-// shape (the two accumulate in the same order, so their outputs are
-// identical).
-static bool use_w4(int64_t K, int64_t lda, const fq_weight* W) {
-  const char* e = getenv("FQ_GEMM_W4");
-  return K % 256 == 0 && lda <= (int64_t{1} << 22) && K <= (int64_t{1} << 24) &&
-         (uintptr_t)W->packed.meta % 16 == 0 && !(e && e[0] == '0');
+// Shapes the 256 x 256 one-wave-per-SIMD kernel takes: packed weights, enough
+// tiles to fill the chip, K a multiple of 256 (its K loop), 32-bit per-lane
+// copy offsets that cannot overflow (up to 255 rows of lda or K / 2 bytes past
+// the block's first row) and a 16-byte aligned {min, scale} array (copied 16
+// bytes per row).
+static bool tile256_fits(int64_t M, int64_t N, int64_t K, int64_t lda, const fq_weight* W) {
+  return M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 256) >= 128 && W->kind == FQ_WEIGHT_PACKED4 &&
+         K % 256 == 0 && lda <= (int64_t{1} << 22) && K <= (int64_t{1} << 24) &&
+         (uintptr_t)W->packed.meta % 16 == 0;
 }
 
 
@@ -2345,32 +1892,17 @@ static fq_status dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const f
   hipStream_t st = as_stream(stream);
   // Tile choice: enough tiles to fill 256 CUs, split-K when the grid is small.
   const int KT = (int)(K / 64);
-  const bool small_tiles = small_tiles_only();
   const int cls = (epilogue & FQ_EPI_F32OUT) ? FQ_KC_LM_HEAD : (M > 256 ? FQ_KC_GEMM_PREFILL : FQ_KC_GEMM_DECODE);
   const int tk = timed ? timing_begin(cls, st) : -1;
   fq_status r;
-  if (M <= 256 && !small_tiles) {
+  if (M <= 256) {
     r = dispatch_skinny(A, M, lda, W, epi, st);
-  } else if (M <= 32) {
-    const int64_t tiles = ceil_div(N, 64);
-    const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
-    r = run_gemm<32, 64, 1, 4>(A, M, lda, W, epi, splits, st);
-  } else if (M <= 256) {
-    const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
-    const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(KT / 4, 512 / std::max<int64_t>(1, tiles)));
-    r = run_gemm<64, 64, 2, 2>(A, M, lda, W, epi, splits, st);
-  } else if (tile256_fits(M, N, K, W) && !small_tiles) {
+  } else if (tile256_fits(M, N, K, lda, W)) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-    if (use_w4(K, lda, W)) {
-      gemm_w4_kernel<false><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
-                                                        KvAppend{});
-      r = launch_check("gemm_w4_kernel");
-    } else {
-      gemm_wide8_kernel<false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
-                                                           KvAppend{});
-      r = launch_check("gemm_wide8_kernel");
-    }
-  } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256 && !small_tiles) {
+    gemm_w4_kernel<false><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi,
+                                                      KvAppend{});
+    r = launch_check("gemm_w4_kernel");
+  } else if (M >= 1024 && N >= 1024 && ceil_div(M, 256) * ceil_div(N, 128) >= 256) {
     const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 128)));
     if (W->kind == FQ_WEIGHT_PACKED4)
       gemm_big_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, nullptr, N, K, epi);
@@ -2469,7 +2001,7 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
                             : (kv->k_codes && kv->v_codes && kv->k_meta && kv->v_meta &&
                                (uintptr_t)kv->k_codes % 8 == 0 && (uintptr_t)kv->v_codes % 8 == 0 &&
                                (uintptr_t)kv->k_meta % 4 == 0 && (uintptr_t)kv->v_meta % 4 == 0);
-  const bool fused = M > 0 && tile256_fits(M, W->n, W->k, W) && !small_tiles_only() && cache_ok &&
+  const bool fused = M > 0 && tile256_fits(M, W->n, W->k, lda, W) && cache_ok &&
                      (!bias || (uintptr_t)bias % 16 == 0) && kv->group == FQ_GROUP;
   if (!fused) {
     // unfused: the projection into C, then the append kernel reads K and V back
@@ -2489,13 +2021,8 @@ extern "C" fq_status fq_qkv_gemm_append(const uint16_t* A, int64_t M, int64_t ld
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(FQ_KC_GEMM_PREFILL, st);
   const dim3 grid((unsigned)(ceil_div(M, 256) * ceil_div(N, 256)));
-  if (use_w4(K, lda, W)) {
-    gemm_w4_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
-    FQ_TRY(launch_check("gemm_w4_kernel"));
-  } else {
-    gemm_wide8_kernel<true><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
-    FQ_TRY(launch_check("gemm_wide8_kernel"));
-  }
+  gemm_w4_kernel<true><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, K, epi, kva);
+  FQ_TRY(launch_check("gemm_w4_kernel"));
   if (tk >= 0) {
     const double bytes = 2.0 * M * K + 0.5625 * N * K + 2.0 * M * h + (f16 ? 2.0 : 0.5625) * 2.0 * M * h + 2.0 * N;
     timing_end(tk, FQ_KC_GEMM_PREFILL, 2.0 * M * N * K, bytes, st);

@@ -35,7 +35,11 @@ __device__ inline uint32_t quant_group_lane(const uint4 raw, uint32_t& meta_bits
 }
 
 __device__ inline uint4 load8(const uint16_t* p, bool aligned) {
-  if (aligned) return *reinterpret_cast<const uint4*>(p);
+  if (aligned) {  // read once: a non-temporal load
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
   uint4 r;
   r.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
   r.y = (uint32_t)p[2] | ((uint32_t)p[3] << 16);
@@ -44,25 +48,43 @@ __device__ inline uint4 load8(const uint16_t* p, bool aligned) {
   return r;
 }
 
-// Row-major matrix [rows, cols] (row stride ldx) -> packed codes/meta.
-template <bool ALIGNED>
+// Row-major matrix [rows, cols] (row stride ldx) -> packed codes/meta.  Each
+// wave takes QG x 8 consecutive groups: load i of the wave covers groups
+// 8 (QG w + i) .. +7 (1 KiB of contiguous input when rows are contiguous), and
+// every lane issues its QG loads before quantising, so QG loads per lane are
+// in flight.  CONTIG: ldx == cols, so group g starts at element 64 g.
+template <bool ALIGNED, bool CONTIG, int QG>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t n_groups,
                                                             int64_t gpr, int64_t ldx, uint8_t* __restrict__ codes,
                                                             uint16_t* __restrict__ meta) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t g = t >> 3;
-  const int sub = (int)(t & 7);
-  const bool ok = g < n_groups;
-  uint4 raw = make_uint4(0, 0, 0, 0);
-  if (ok) {
-    const int64_t r = g / gpr, c = g - r * gpr;
-    raw = load8(x + r * ldx + c * 64 + sub * 8, ALIGNED);
+  const int64_t wave = t >> 6;
+  const int seg = (int)((t >> 3) & 7), sub = (int)(t & 7);
+  uint4 raw[QG];
+#pragma unroll
+  for (int i = 0; i < QG; ++i) {
+    const int64_t g = (wave * QG + i) * 8 + seg;
+    raw[i] = make_uint4(0, 0, 0, 0);
+    if (g < n_groups) {
+      const uint16_t* src;
+      if (CONTIG) {
+        src = x + g * 64 + sub * 8;
+      } else {
+        const int64_t r = g / gpr, c = g - r * gpr;
+        src = x + r * ldx + c * 64 + sub * 8;
+      }
+      raw[i] = load8(src, ALIGNED);
+    }
   }
-  uint32_t mb;
-  const uint32_t packed = quant_group_lane(raw, mb);
-  if (ok) {
-    reinterpret_cast<uint32_t*>(codes + g * 32)[sub] = packed;
-    if (sub == 0) reinterpret_cast<uint32_t*>(meta)[g] = mb;
+#pragma unroll
+  for (int i = 0; i < QG; ++i) {
+    const int64_t g = (wave * QG + i) * 8 + seg;
+    uint32_t mb;
+    const uint32_t packed = quant_group_lane(raw[i], mb);
+    if (g < n_groups) {
+      reinterpret_cast<uint32_t*>(codes + g * 32)[sub] = packed;
+      if (sub == 0) reinterpret_cast<uint32_t*>(meta)[g] = mb;
+    }
   }
 }
 
@@ -161,12 +183,16 @@ fq_status launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, in
   const int64_t gpr = cols / 64;
   const int64_t n_groups = rows * gpr;
   if (n_groups == 0) return FQ_OK;
-  const int64_t blocks = ceil_div(n_groups * 8, 256);
+  constexpr int QG = 8;  // groups per 8-lane segment
+  const int64_t blocks = ceil_div(ceil_div(n_groups, 8 * QG), 4);  // 4 waves per block
   const bool aligned = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0);
-  if (aligned)
-    quantize_rows_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n_groups, gpr, ldx, codes, meta);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (aligned && ldx == cols)
+    quantize_rows_kernel<true, true, QG><<<grid, block, 0, st>>>(x, n_groups, gpr, ldx, codes, meta);
+  else if (aligned)
+    quantize_rows_kernel<true, false, QG><<<grid, block, 0, st>>>(x, n_groups, gpr, ldx, codes, meta);
   else
-    quantize_rows_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n_groups, gpr, ldx, codes, meta);
+    quantize_rows_kernel<false, false, QG><<<grid, block, 0, st>>>(x, n_groups, gpr, ldx, codes, meta);
   return launch_check("quantize_rows_kernel");
 }
 

@@ -36,12 +36,6 @@ def test_fused_append_equals_two_calls(H, d, B, T, pos, b0, fmt):
     _fused_vs_two_calls(H, d, B, T, pos, b0, fmt)
 
 
-@pytest.mark.parametrize("H,d,B,T,pos,b0,fmt", CASES[:3])
-def test_fused_append_equals_two_calls_8wave_kernel(H, d, B, T, pos, b0, fmt, monkeypatch):
-    """The same through the 8-wave 256 x 256 kernel (FQ_GEMM_W4=0)."""
-    monkeypatch.setenv("FQ_GEMM_W4", "0")
-    _fused_vs_two_calls(H, d, B, T, pos, b0, fmt)
-
 
 def _fused_vs_two_calls(H, d, B, T, pos, b0, fmt):
     h = H * d
