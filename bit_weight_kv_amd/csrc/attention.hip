@@ -17,11 +17,12 @@
 //      (the reconstruction costs no multiply per element), summed over the
 //      position's lanes with DPP; scores go to LDS;
 //   2. softmax with block max / sum reductions (exp2 of log2(e)-scaled scores);
-//   3. values: each lane accumulates sum_j (p_j s_jg) c_ji for its 32 channels
-//      -- two positions at a time, as fp32 dot products of exact fp16 code
-//      pairs with the fp16 pair {p_1 s_1, p_2 s_2} -- and sum_j p_j min_jg in
-//      fp32; the partial sums are reduced over each 16-lane row with DPP row
-//      rotations, then over the 16 rows through LDS.
+//   3. values: each lane accumulates sum_j (p_j s_jg 2^-E) c_ji for its 32
+//      channels -- two positions at a time, as fp32 dot products of exact
+//      fp16 code pairs with the fp16 pair {p_1 s_1 2^-E, p_2 s_2 2^-E}, 2^E
+//      the power of two just above the lane's largest value scale -- and
+//      sum_j p_j min_jg in fp32; 2^E acc + that sum is reduced over each
+//      16-lane row with DPP row rotations, then over the 16 rows through LDS.
 //
 // The fp16 cache (cache compression off, weights possibly still compressed)
 // goes through the same kernels instantiated with F16 = true: keys and values
@@ -120,7 +121,7 @@ __device__ inline void codes8_pairs(uint32_t w1, uint32_t w2, half2_t out[8]) {
 // lanes in both passes, 16 bytes per lane, and the scores are reduced across
 // those lanes with xor shuffles.
 template <int D, bool F16>
-__global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_attention_kernel(const uint16_t* __restrict__ q, int64_t ldq,
                                                                const uint8_t* __restrict__ kc,
                                                                const uint16_t* __restrict__ km,
                                                                const uint8_t* __restrict__ vc,
@@ -270,15 +271,38 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   }
   const float inv = 1.0f / block_sum256(lsum, red);  // also orders the p[] writes before the reads below
 
-  // ---- values: positions in pairs, sum_j (p_j s_j) c_jk as fp32 dot
-  // products of the fp16 pairs {c_1k, c_2k} and {p_1 s_1, p_2 s_2}, and
-  // sum_j p_j min_j in fp32 ----
+  // ---- values: positions in pairs, sum_j (p_j s_j 2^-E) c_jk as fp32 dot
+  // products of the fp16 pairs {c_1k, c_2k} and {p_1 s_1 2^-E, p_2 s_2 2^-E},
+  // and sum_j p_j min_j in fp32.  2^E: the power of two just above the
+  // largest value scale among this lane's positions so far (the products are
+  // then at most 1 and fall below fp16's normal range only when 2^-14 below
+  // the largest possible one); when a later chunk raises it, the sums so far
+  // are rescaled (exactly) ----
   float acc[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) acc[k] = 0.f;
   float bsum = 0.f;
+  int vexp = 0;
+  bool vset = false;  // a nonzero value scale seen
   for (int c0 = 0; c0 < len; c0 += CH) {
     if (c0 > 0) load_chunk(vc, vm, vw, vmeta, c0);
+    float smx = 0.f;
+#pragma unroll
+    for (int u = 0; u < VPOS; ++u) smx = fmaxf(smx, h2f((uint16_t)(vmeta[u] >> 16)));  // unused slots hold 0
+    int e = 0;
+    (void)frexpf(smx, &e);  // smx = f * 2^e, f in [0.5, 1) (smx = 0: e = 0)
+    if (smx > 0.f) {
+      if (!vset) {
+        vexp = e;
+        vset = true;
+      } else if (e > vexp) {
+        const float r = ldexpf(1.0f, vexp - e);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) acc[k] *= r;
+        vexp = e;
+      }
+    }
+    const float vsh = ldexpf(1.0f, -vexp);  // 1 until a nonzero scale is seen
 #pragma unroll
     for (int u = 0; u < VPOS; u += 2) {
       const int j1 = c0 + slot4 + u * SLOTS4, j2 = j1 + SLOTS4;
@@ -288,7 +312,8 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
       const uint32_t m1 = vmeta[u], m2 = two ? vmeta[u + 1] : 0u;
       const uint4 w1 = vw[u], w2 = two ? vw[u + 1] : make_uint4(0, 0, 0, 0);
       bsum += p1 * h2f((uint16_t)(m1 & 0xFFFF)) + p2 * h2f((uint16_t)(m2 & 0xFFFF));
-      const half2_t a2 = {(half_t)(p1 * h2f((uint16_t)(m1 >> 16))), (half_t)(p2 * h2f((uint16_t)(m2 >> 16)))};
+      const half2_t a2 = {(half_t)(p1 * (h2f((uint16_t)(m1 >> 16)) * vsh)),
+                          (half_t)(p2 * (h2f((uint16_t)(m2 >> 16)) * vsh))};
       const uint32_t x1[4] = {w1.x, w1.y, w1.z, w1.w}, x2[4] = {w2.x, w2.y, w2.z, w2.w};
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
@@ -299,6 +324,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
       }
     }
   }
+  const float vsc_back = ldexpf(1.0f, vexp);  // 2^E, exact (1 when no nonzero scale)
   // sum over the slots of each 16-lane row (lanes l, l + LPP4, ... hold the
   // same channels) with row rotations, then over the 16 rows through LDS
   auto row_sum = [](float v) {
@@ -310,7 +336,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
   const int lane = tid & 63, row = (tid >> 6) * 4 + (lane >> 4);
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const float v = row_sum(acc[k] + bsum);
+    const float v = row_sum(acc[k] * vsc_back + bsum);
     if ((lane & 15) < LPP4) part[row * D + lq * 32 + k] = v;
   }
   __syncthreads();
@@ -324,17 +350,23 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const uint16_t* _
 
 // ---- causal prefill on the matrix cores ------------------------------------
 // Work-group = 4 waves x 32 queries of one (b, h); keys in chunks of 64.
-// Per chunk the work-group stages K and V of 64 positions in LDS as fp16,
-// then each wave computes
+// Per chunk the work-group stages the chunk's K and V codes in LDS as exact
+// fp16 integers (the fp16 cache: the stored values) and, for the 4-bit cache,
+// each key's fp32 {min, scale} per group; then each wave computes
 //   S^T = K^ Q^T      (v_mfma_f32_16x16x32_f16; lane owns query lane % 16)
 //   online softmax    (per query, reduced over the 4 lane groups)
 //   O^T += V^T P^T    (P taken straight from the S^T registers)
-// With the 4-bit cache each reconstructed key k = min + code * s (exact in
-// fp32) is staged as two fp16 arrays, hi = fp16(k) and lo = fp16(k - hi), and
-// S^T accumulates the products with both: the scores carry the key to about
-// 22 bits instead of fp16's 11 (rounding k itself to fp16 was the largest
-// error of the layer at the OPT-175B shape).  V is staged the same way, as
-// hi and lo arrays, and O^T accumulates the products with both.
+// 4-bit cache, without rounding the reconstructed cache to fp16:
+//   scores: per group g, T_g = C_g Q_g^T over the group's 64 channels (exact
+//     products of fp16 queries and integer codes, fp32 sums), then
+//     s = sum_g (scale_g * T_g + min_g * sum(q_g)) in fp32;
+//   values: per group g, O_g^T += C_g^T P'_g^T with P'_g = p * scale_g *
+//     2^-E_g split into fp16 hi + lo (two products per code fragment, about
+//     22 bits), 2^E_g the power of two just above the largest value scale of
+//     group g among the work-group's keys (so P' <= 256 and hi and lo leave
+//     fp16's normal range only for terms far below the largest one), plus
+//     sum_j p_j min_jg in fp32; the output is
+//     (2^E_g O_g + sum_j p_j min_jg) / sum_j p_j.
 // Transposing both products keeps every per-query value (scores, running
 // max/sum, output column) in the lanes of that query, so P never moves.
 // V is stored transposed ([d][position]) with the positions of each 32-wide
@@ -351,11 +383,13 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   constexpr int NKD = D / 32;      // 32-wide d slices
   constexpr int NDB = D / 16;      // 16-wide d blocks
   constexpr int G = D / 64;        // quantisation groups per position
-  constexpr int KHALF = D / 64;    // K stored as D/64 arrays of 64 d (128-byte rows)
+  constexpr int KHALF = D / 64;    // K stored as D/64 arrays of 64 d (128-byte rows): array g = group g
+  constexpr int MG = F16 ? 1 : G;  // {min, scale} arrays (unused with the fp16 cache)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[KHALF][KC * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t klo_lds[F16 ? 1 : KHALF][F16 ? 8 : KC * 64];  // 4-bit: k - hi
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * KC];
-  __shared__ __attribute__((aligned(16))) uint16_t vlo_lds[F16 ? 8 : D * KC];  // 4-bit: v - hi
+  __shared__ __attribute__((aligned(16))) float kmin_lds[MG][KC], ksc_lds[MG][KC], vmin_lds[MG][KC],
+      vsc_lds[MG][KC];
+  __shared__ float red[4][G];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -373,18 +407,64 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) qf[qb][kd] = *reinterpret_cast<const half8_t*>(qp + kd * 32 + g4 * 8);
   }
+  // 4-bit cache: sum of each group's query channels (query l16 of block qb)
+  float qsum[2][G];
+  // and 2^-E_g per value group (in LDS: read at staging and at the end)
+  __shared__ float vmul[G];
+  if constexpr (!F16) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sq = 0.f;
+#pragma unroll
+        for (int kd = 2 * g; kd < 2 * g + 2; ++kd)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sq += (float)qf[qb][kd][e];
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        qsum[qb][g] = sq;
+      }
+    float smax[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) smax[g] = 0.f;
+    for (int64_t j = tid; j < nkeys; j += 256)
+#pragma unroll
+      for (int g = 0; g < G; ++g) smax[g] = fmaxf(smax[g], h2f(vm[((row0 + j) * G + g) * 2 + 1]));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) smax[g] = fmaxf(smax[g], __shfl_xor(smax[g], o));
+      if (lane == 0) red[wave][g] = smax[g];
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int g = tid;
+      const float m = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+      int e = 0;
+      (void)frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1) (m = 0: e = 0)
+      vmul[g] = m > 0.f ? ldexpf(1.0f, -e) : 1.0f;
+    }
+    // (the first chunk's barrier orders these writes before any read)
+  }
   float4_t oacc[NDB][2];
 #pragma unroll
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) oacc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  float msum[2][G];  // this lane's share of sum_j p_j min_jg (4-bit cache)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int g = 0; g < G; ++g) msum[qb][g] = 0.f;
   constexpr float kL2e = 1.4426950408889634f;
 
   // Staging: every thread stages part of K and part of V of each chunk.
   //   K: key tid / 4, channels (tid % 4) * D/4 .. + D/4 - 1 (D/32 code words);
   //   V: channels 8 * (tid / 16) .. + 7 of the 4 positions of quad tid % 16
-  //      (two quads make one 8-position storage chunk in slice order).
+  //      (two quads make one 8-position storage chunk in slice order);
+  //   {min, scale}: thread t < 64 G, key t % 64, group t / 64, K and V.
   // 4-bit cache: the raw codes and {min, scale} of the next chunk are loaded
   // into registers before the current chunk's products, so their latency
   // hides behind them; they are converted and stored at the next chunk's
@@ -394,45 +474,35 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   const int vdc = tid >> 4, vpq = tid & 15;
   const int vpc = vpq >> 1, vhalf = vpq & 1;  // storage chunk, its first or second 4 positions
   const bool vact = vdc < D / 8;
+  const int mkey = tid % KC, mg = tid / KC;
+  const bool mact = !F16 && tid < KC * G;
   auto vkey = [&](int jj) { return (vpc >> 2) * 32 + vhalf * 16 + 4 * (vpc & 3) + jj; };
-  uint32_t rk[KW], rkm = 0, rv[4], rvm[4];
+  uint32_t rk[KW], rv[4], rkm = 0, rvm = 0;
   auto load_raw = [&](int64_t k0) {
     if constexpr (!F16) {
       const int64_t j = min(k0 + kkey, nkeys - 1);
       const uint32_t* cw = reinterpret_cast<const uint32_t*>(kc + (row0 + j) * (D / 2)) + kq * KW;
 #pragma unroll
       for (int w = 0; w < KW; ++w) rk[w] = cw[w];
-      rkm = reinterpret_cast<const uint32_t*>(km)[(row0 + j) * G + (kq * KW * 8) / 64];
       if (vact) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int64_t jv = min(k0 + vkey(jj), nkeys - 1);
           rv[jj] = reinterpret_cast<const uint32_t*>(vc + (row0 + jv) * (D / 2))[vdc];
-          rvm[jj] = reinterpret_cast<const uint32_t*>(vm)[(row0 + jv) * G + vdc / 8];
         }
+      }
+      if (mact) {
+        const int64_t jm = min(k0 + mkey, nkeys - 1);
+        rkm = reinterpret_cast<const uint32_t*>(km)[(row0 + jm) * G + mg];
+        rvm = reinterpret_cast<const uint32_t*>(vm)[(row0 + jm) * G + mg];
       }
     }
   };
-  // 8 codes (one word) with their {min, scale} -> hi = fp16(min + c * s) and
-  // lo = fp16((min + c * s) - hi), 4 packed pairs each; min + c * s is exact
-  // in fp32 (a 4-bit code times an 11-bit scale), and so is the difference.
-  auto hilo8 = [](uint32_t w, uint32_t mb, uint32_t hi[4], uint32_t lo[4]) {
-    const float mnf = (float)__builtin_bit_cast(half_t, (uint16_t)(mb & 0xFFFF));
-    const float scf = (float)__builtin_bit_cast(half_t, (uint16_t)(mb >> 16));
+  auto code_words = [](uint32_t w) {  // 8 codes -> 4 exact fp16 pairs, as one 16-byte word
     half2_t c[4];
     codes8_cvt(w, c);
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      half2_t h2, l2;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float v = __builtin_fmaf((float)c[pp][e], scf, mnf);
-        h2[e] = (half_t)v;
-        l2[e] = (half_t)(v - (float)h2[e]);
-      }
-      hi[pp] = __builtin_bit_cast(uint32_t, h2);
-      lo[pp] = __builtin_bit_cast(uint32_t, l2);
-    }
+    return make_uint4(__builtin_bit_cast(uint32_t, c[0]), __builtin_bit_cast(uint32_t, c[1]),
+                      __builtin_bit_cast(uint32_t, c[2]), __builtin_bit_cast(uint32_t, c[3]));
   };
   load_raw(0);
   for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
@@ -445,40 +515,46 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
         const int d0 = kq * KW * 8 + w * 8;
         const int arr = d0 / 64, chunk = (d0 % 64) / 8;
         const int at = kkey * 64 + ((chunk ^ (kkey & 7)) * 8);
-        if constexpr (F16) {
+        if constexpr (F16)
           *reinterpret_cast<uint4*>(&k_lds[arr][at]) = *reinterpret_cast<const uint4*>(k16 + (row0 + j) * D + d0);
-        } else {
-          uint32_t hi[4], lo[4];
-          hilo8(rk[w], rkm, hi, lo);
-          *reinterpret_cast<uint4*>(&k_lds[arr][at]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-          *reinterpret_cast<uint4*>(&klo_lds[arr][at]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        }
+        else
+          *reinterpret_cast<uint4*>(&k_lds[arr][at]) = code_words(rk[w]);
       }
     }
     // ---- stage V, transposed: [d][positions in slice order] ----
     if (vact) {
-      uint32_t hi[4][4], lo[4][4];  // [position][channel pair]
+      uint32_t x[4][4];  // [position][channel pair]
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
+        uint4 r4;
         if constexpr (F16) {
           const int64_t jv = min(k0 + vkey(jj), nkeys - 1);
-          const uint4 r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + jv) * D + vdc * 8);
-          hi[jj][0] = r4.x, hi[jj][1] = r4.y, hi[jj][2] = r4.z, hi[jj][3] = r4.w;
+          r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + jv) * D + vdc * 8);
         } else {
-          hilo8(rv[jj], rvm[jj], hi[jj], lo[jj]);
+          r4 = code_words(rv[jj]);
         }
+        x[jj][0] = r4.x, x[jj][1] = r4.y, x[jj][2] = r4.z, x[jj][3] = r4.w;
       }
       // channel i: its 4 positions as 8 bytes, the first or second half of a 16-byte chunk
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int d = vdc * 8 + i;
         const int at = d * KC + ((vpc ^ (d & 7)) * 8) + vhalf * 4;
-        auto pick = [&](const uint32_t (*x)[4], int pp) {  // low halves (even channel) or high (odd)
+        auto pick = [&](int pp) {  // low halves (even channel) or high (odd)
           const uint32_t a = x[2 * pp][i >> 1], c2 = x[2 * pp + 1][i >> 1];
           return (i & 1) ? ((a >> 16) | (c2 & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c2 << 16));
         };
-        *reinterpret_cast<uint2*>(&v_lds[at]) = make_uint2(pick(hi, 0), pick(hi, 1));
-        if constexpr (!F16) *reinterpret_cast<uint2*>(&vlo_lds[at]) = make_uint2(pick(lo, 0), pick(lo, 1));
+        *reinterpret_cast<uint2*>(&v_lds[at]) = make_uint2(pick(0), pick(1));
+      }
+    }
+    // ---- stage {min, scale} as fp32; value scales times 2^-E_g ----
+    if constexpr (!F16) {
+      if (mact) {
+        const float vmg = vmul[mg];
+        kmin_lds[mg][mkey] = h2f((uint16_t)(rkm & 0xFFFF));
+        ksc_lds[mg][mkey] = h2f((uint16_t)(rkm >> 16));
+        vmin_lds[mg][mkey] = h2f((uint16_t)(rvm & 0xFFFF));
+        vsc_lds[mg][mkey] = h2f((uint16_t)(rvm >> 16)) * vmg;  // exact: a power of two
       }
     }
     __syncthreads();
@@ -489,23 +565,47 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     float4_t sacc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = (float4_t){0.f, 0.f, 0.f, 0.f};
       const int key = kb * 16 + l16;
+      if constexpr (F16) {
 #pragma unroll
-      for (int kd = 0; kd < NKD; ++kd) {
-        const int arr = kd / 2, chunk = (kd % 2) * 4 + g4;
-        const int at = key * 64 + ((chunk ^ (key & 7)) * 8);
-        const half8_t kf = *reinterpret_cast<const half8_t*>(&k_lds[arr][at]);
+        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
-        if constexpr (!F16) {
-          const half8_t kl = *reinterpret_cast<const half8_t*>(&klo_lds[arr][at]);
+        for (int kd = 0; kd < NKD; ++kd) {
+          const int arr = kd / 2, chunk = (kd % 2) * 4 + g4;
+          const half8_t kf = *reinterpret_cast<const half8_t*>(&k_lds[arr][key * 64 + ((chunk ^ (key & 7)) * 8)]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
-            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
+            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
         }
+      } else {
+        // group by group: t = codes . q over the group's 64 channels, then
+        // s += scale * t + min * sum(q_g) for keys kb*16 + 4*g4 + r of this lane
+        const int kbase = kb * 16 + 4 * g4;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float4_t tg[2] = {(float4_t){0.f, 0.f, 0.f, 0.f}, (float4_t){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int kd = 2 * g; kd < 2 * g + 2; ++kd) {
+            const int chunk = (kd % 2) * 4 + g4;
+            const half8_t kf = *reinterpret_cast<const half8_t*>(&k_lds[g][key * 64 + ((chunk ^ (key & 7)) * 8)]);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) tg[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], tg[qb], 0, 0, 0);
+          }
+          const float4 mn = *reinterpret_cast<const float4*>(&kmin_lds[g][kbase]);
+          const float4 sc = *reinterpret_cast<const float4*>(&ksc_lds[g][kbase]);
+          const float mnr[4] = {mn.x, mn.y, mn.z, mn.w}, scr[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[kb][qb][r] += scr[r] * tg[qb][r] + mnr[r] * qsum[qb][g];
+        }
+        // the scores of this key block are formed here: the empty asm keeps
+        // the compiler from sinking the combination into the softmax (which
+        // would hold every block's products and {min, scale} at once)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) asm volatile("" : "+v"(sacc[kb][qb]));
       }
     }
     // ---- online softmax per query (lane l16 of each query block) ----
@@ -516,7 +616,6 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     // wave-uniform branch).  Chunks wholly below the wave's first query and
     // inside the keys need no mask.
     const bool unmasked = k0 + KC - 1 <= pos + t0 && k0 + KC <= nkeys;
-    half8_t pf[2][2];  // [query block][32-wide key slice], B operand of O^T
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qpos = (int)(pos + t0) + qb * 16 + l16;
@@ -542,6 +641,8 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
         mrun[qb] = mnew;
 #pragma unroll
         for (int i = 0; i < NDB; ++i) oacc[i][qb] *= alpha;
+#pragma unroll
+        for (int g = 0; g < G; ++g) msum[qb][g] *= alpha;
       }
       const float mb = mrun[qb] == -INFINITY ? 0.f : mrun[qb];  // a row with no key yet: every p is 0
       float sum = 0.f;
@@ -556,30 +657,71 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       lrun[qb] += sum;
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pf[qb][sl][r] = (half_t)sacc[2 * sl][qb][r];
-          pf[qb][sl][4 + r] = (half_t)sacc[2 * sl + 1][qb][r];
-        }
     }
     // ---- O^T += V^T P^T ----
+    // lane's keys of slice sl: e < 4 -> block 2 sl, e >= 4 -> block 2 sl + 1 (key kb*16 + 4*g4 + r)
+    if constexpr (F16) {
+      half8_t pf[2][2];  // [query block][32-wide key slice], B operand of O^T
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 16 + l16;
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const int chunk = sl * 4 + g4;
-        const int at = d * KC + ((chunk ^ (d & 7)) * 8);
-        const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[at]);
+        for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][sl], oacc[db][qb], 0, 0, 0);
-        if constexpr (!F16) {
-          const half8_t vl = *reinterpret_cast<const half8_t*>(&vlo_lds[at]);
+          for (int r = 0; r < 4; ++r) {
+            pf[qb][sl][r] = (half_t)sacc[2 * sl][qb][r];
+            pf[qb][sl][4 + r] = (half_t)sacc[2 * sl + 1][qb][r];
+          }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 16 + l16;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int chunk = sl * 4 + g4;
+          const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[d * KC + ((chunk ^ (d & 7)) * 8)]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, pf[qb][sl], oacc[db][qb], 0, 0, 0);
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][sl], oacc[db][qb], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        // P'_g = p * scale * 2^-E_g as fp16 hi + lo (x - hi is exact in fp32),
+        // one 32-key slice at a time
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          half8_t ph[2], pl[2];
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const int kb = 2 * sl + kh, kbase = kb * 16 + 4 * g4;
+            const float4 vs = *reinterpret_cast<const float4*>(&vsc_lds[g][kbase]);
+            const float4 vn = *reinterpret_cast<const float4*>(&vmin_lds[g][kbase]);
+            const float vsr[4] = {vs.x, vs.y, vs.z, vs.w}, vnr[4] = {vn.x, vn.y, vn.z, vn.w};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float pv = sacc[kb][qb][r];
+                const float x = pv * vsr[r];
+                const half_t xh = (half_t)x;
+                ph[qb][kh * 4 + r] = xh;
+                pl[qb][kh * 4 + r] = (half_t)(x - (float)xh);
+                msum[qb][g] += pv * vnr[r];
+              }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one slice's P' at a time
+          const int chunk = sl * 4 + g4;
+#pragma unroll
+          for (int db = 4 * g; db < 4 * g + 4; ++db) {
+            const int d = db * 16 + l16;
+            const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[d * KC + ((chunk ^ (d & 7)) * 8)]);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[qb], oacc[db][qb], 0, 0, 0);
+              oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qb], oacc[db][qb], 0, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -587,14 +729,27 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   // ---- normalise and store: lane holds channels db*16 + 4*g4 + r of its query ----
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
+    float mtot[G], scale[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = msum[qb][g];
+      m += __shfl_xor(m, 16);
+      m += __shfl_xor(m, 32);
+      mtot[g] = F16 ? 0.f : m;
+      scale[g] = F16 ? 1.f : 1.0f / vmul[g];  // 2^E_g, exact
+    }
     const int t = t0 + qb * 16 + l16;
     if (t >= T) continue;
     const float inv = 1.0f / lrun[qb];
     uint16_t* op = out + ((int64_t)b * T + t) * ldo + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint32_t w0 = (uint32_t)f2h(oacc[db][qb][0] * inv) | ((uint32_t)f2h(oacc[db][qb][1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)f2h(oacc[db][qb][2] * inv) | ((uint32_t)f2h(oacc[db][qb][3] * inv) << 16);
+      const int g = db / 4;
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = (oacc[db][qb][r] * scale[g] + mtot[g]) * inv;
+      const uint32_t w0 = (uint32_t)f2h(o[0]) | ((uint32_t)f2h(o[1]) << 16);
+      const uint32_t w1 = (uint32_t)f2h(o[2]) | ((uint32_t)f2h(o[3]) << 16);
       *reinterpret_cast<uint2*>(op + db * 16 + 4 * g4) = make_uint2(w0, w1);
     }
   }

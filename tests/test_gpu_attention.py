@@ -15,12 +15,12 @@ pytestmark = pytest.mark.gpu
 fq = pytest.importorskip("bit_weight_kv_amd")
 
 
-def _cache(B, H, d, n, cap, seed, b_off=0, fmt="q4"):
+def _cache(B, H, d, n, cap, seed, b_off=0, fmt="q4", v_sigma=1.0):
     """fp16 K/V [B, n, H*d] from the generator -> GPU cache (appended) and the
     oracle's reading of the same cache (fmt "q4": 4-bit, "f16": fp16)."""
     h = H * d
     k = synth.normal_f16(seed, synth.STREAM["aux"] + 20, (B * n, h), 1.0)
-    v = synth.normal_f16(seed, synth.STREAM["aux"] + 21, (B * n, h), 1.0)
+    v = synth.normal_f16(seed, synth.STREAM["aux"] + 21, (B * n, h), v_sigma)
     if fmt == "q4":
         kc = torch.zeros((B + b_off, H, cap, d // 2), dtype=torch.uint8, device="cuda:0")
         km = torch.zeros((B + b_off, H, cap, d // 64, 2), dtype=torch.float16, device="cuda:0")
@@ -93,6 +93,37 @@ def test_prefill_attention_causal(d, T, pos, fmt):
     ref = ref.transpose(0, 2, 1, 3).reshape(B * T, H * d)
     r, m = assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill {kernel} {fmt} d={d} T={T} pos={pos}")
     log(f"prefill {kernel} {fmt} d={d} T={T} pos={pos}: rel_l2 {r:.2e} max_abs {m:.2e}")
+
+
+@pytest.mark.parametrize("v_sigma", [2.0 ** -8, 64.0])
+def test_attention_value_scale_range(v_sigma):
+    """Values far below and above unit size: the value pass rounds p * scale
+    (times a power of two chosen from the largest scale) to fp16; the outputs
+    keep the same relative accuracy as at unit size, in decode and prefill,
+    over a cache long enough to span several chunks of the decode kernel."""
+    B, H, d = 2, 3, 128
+    n = 1300
+    log(f"value scale range sigma={v_sigma}")
+    view, keep, kh, vh = _cache(B, H, d, n, n, seed=77, v_sigma=v_sigma)
+    q = (synth.normal_f16(0, synth.STREAM["aux"] + 22, (B, H * d), 1.0).astype(np.float32)
+         * d ** -0.5).astype(np.float16)
+    out = torch.empty((B, H * d), dtype=torch.float16, device="cuda:0")
+    fq.fq_decode_attention(dev(q), view, 0, B, n, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention_decode(q.reshape(B, H, d), kh, vh).reshape(B, H * d)
+    assert_close(host(out), ref, rel=2e-3, abs_=4e-3 * v_sigma, what=f"decode sigma={v_sigma}")
+    T, pos = 200, n - 200
+    qp = (synth.normal_f16(1, synth.STREAM["aux"] + 23, (B * T, H * d), 1.0).astype(np.float32)
+          * d ** -0.5).astype(np.float16)
+    outp = torch.empty((B * T, H * d), dtype=torch.float16, device="cuda:0")
+    fq.fq_prefill_attention(dev(qp), view, 0, B, T, pos, outp)
+    torch.cuda.synchronize()
+    q4 = qp.reshape(B, T, H, d).transpose(0, 2, 1, 3).astype(np.float64)
+    refp = np.empty((B, H, T, d))
+    for t in range(T):
+        refp[:, :, t] = oracle.attention_decode(q4[:, :, t], kh[:, :, :pos + t + 1], vh[:, :, :pos + t + 1])
+    refp = refp.transpose(0, 2, 1, 3).reshape(B * T, H * d)
+    assert_close(host(outp), refp, rel=2e-3, abs_=4e-3 * v_sigma, what=f"prefill sigma={v_sigma}")
 
 
 def test_decode_full_size_sampled():
