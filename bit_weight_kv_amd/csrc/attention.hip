@@ -360,13 +360,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 //   scores: per group g, T_g = C_g Q_g^T over the group's 64 channels (exact
 //     products of fp16 queries and integer codes, fp32 sums), then
 //     s = sum_g (scale_g * T_g + min_g * sum(q_g)) in fp32;
-//   values: per group g, O_g^T += C_g^T P'_g^T with P'_g = p * scale_g *
-//     2^-E_g split into fp16 hi + lo (two products per code fragment, about
-//     22 bits), 2^E_g the power of two just above the largest value scale of
-//     group g among the work-group's keys (so P' <= 256 and hi and lo leave
-//     fp16's normal range only for terms far below the largest one), plus
-//     sum_j p_j min_jg in fp32; the output is
-//     (2^E_g O_g + sum_j p_j min_jg) / sum_j p_j.
+//   values: with the codes centred (c' = c - 8, exact in fp16) and
+//     min' = min + 8 scale, per group g, O_g^T += C'_g^T P'_g^T with
+//     P'_g = fp16(p * scale_g * 2^-E_g), 2^E_g the power of two just above the
+//     largest value scale of group g among the work-group's keys (so P' <= 256
+//     and leaves fp16's normal range only for terms far below the largest
+//     one), plus sum_j p_j min'_jg in fp32; the output is
+//     (2^E_g O_g + sum_j p_j min'_jg) / sum_j p_j.  The rounding of P' then
+//     weighs |scale * c'| <= 8 scale, about the distance of the value from the
+//     middle of its group's range.
 // Transposing both products keeps every per-query value (scores, running
 // max/sum, output column) in the lanes of that query, so P never moves.
 // V is stored transposed ([d][position]) with the positions of each 32-wide
@@ -504,6 +506,13 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     return make_uint4(__builtin_bit_cast(uint32_t, c[0]), __builtin_bit_cast(uint32_t, c[1]),
                       __builtin_bit_cast(uint32_t, c[2]), __builtin_bit_cast(uint32_t, c[3]));
   };
+  auto code_words_centered = [](uint32_t w) {  // 8 codes -> 4 exact fp16 pairs of c - 8
+    half2_t c[4];
+    codes8_cvt(w, c);
+    const half2_t eight = {(half_t)8.0f, (half_t)8.0f};
+    return make_uint4(__builtin_bit_cast(uint32_t, c[0] - eight), __builtin_bit_cast(uint32_t, c[1] - eight),
+                      __builtin_bit_cast(uint32_t, c[2] - eight), __builtin_bit_cast(uint32_t, c[3] - eight));
+  };
   load_raw(0);
   for (int64_t k0 = 0; k0 < nkeys; k0 += KC) {
     __syncthreads();
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
           const int64_t jv = min(k0 + vkey(jj), nkeys - 1);
           r4 = *reinterpret_cast<const uint4*>(v16 + (row0 + jv) * D + vdc * 8);
         } else {
-          r4 = code_words(rv[jj]);
+          r4 = code_words_centered(rv[jj]);
         }
         x[jj][0] = r4.x, x[jj][1] = r4.y, x[jj][2] = r4.z, x[jj][3] = r4.w;
       }
@@ -553,8 +562,9 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
         const float vmg = vmul[mg];
         kmin_lds[mg][mkey] = h2f((uint16_t)(rkm & 0xFFFF));
         ksc_lds[mg][mkey] = h2f((uint16_t)(rkm >> 16));
-        vmin_lds[mg][mkey] = h2f((uint16_t)(rvm & 0xFFFF));
-        vsc_lds[mg][mkey] = h2f((uint16_t)(rvm >> 16)) * vmg;  // exact: a power of two
+        const float vsf = h2f((uint16_t)(rvm >> 16));
+        vmin_lds[mg][mkey] = h2f((uint16_t)(rvm & 0xFFFF)) + 8.0f * vsf;  // min + 8 s: the centre of the codes
+        vsc_lds[mg][mkey] = vsf * vmg;  // exact: a power of two
       }
     }
     __syncthreads();
@@ -686,11 +696,10 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        // P'_g = p * scale * 2^-E_g as fp16 hi + lo (x - hi is exact in fp32),
-        // one 32-key slice at a time
+        // P'_g = fp16(p * scale * 2^-E_g), one 32-key slice at a time
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
-          half8_t ph[2], pl[2];
+          half8_t ph[2];
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh) {
             const int kb = 2 * sl + kh, kbase = kb * 16 + 4 * g4;
@@ -702,10 +711,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float pv = sacc[kb][qb][r];
-                const float x = pv * vsr[r];
-                const half_t xh = (half_t)x;
-                ph[qb][kh * 4 + r] = xh;
-                pl[qb][kh * 4 + r] = (half_t)(x - (float)xh);
+                ph[qb][kh * 4 + r] = (half_t)(pv * vsr[r]);
                 msum[qb][g] += pv * vnr[r];
               }
           }
@@ -716,10 +722,8 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
             const int d = db * 16 + l16;
             const half8_t vf = *reinterpret_cast<const half8_t*>(&v_lds[d * KC + ((chunk ^ (d & 7)) * 8)]);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < 2; ++qb)
               oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[qb], oacc[db][qb], 0, 0, 0);
-              oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qb], oacc[db][qb], 0, 0, 0);
-            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
