@@ -126,6 +126,48 @@ def test_attention_value_scale_range(v_sigma):
     assert_close(host(outp), refp, rel=2e-3, abs_=4e-3 * v_sigma, what=f"prefill sigma={v_sigma}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_value_scale_growing_along_the_cache(d):
+    """Value magnitudes that grow along the cache (x 2^-6 for the first 600
+    positions, x 4 after): the decode kernel's per-lane power-of-two value scale
+    is raised by a later chunk of positions and the sums so far are rescaled;
+    the prefill kernel takes its power of two from every key it reads.  Both
+    against the oracle's float64 attention over the same cache."""
+    B, H, n = 2, 3, 1500
+    h = H * d
+    k = synth.normal_f16(3, synth.STREAM["aux"] + 24, (B * n, h), 1.0)
+    v = synth.normal_f16(3, synth.STREAM["aux"] + 25, (B * n, h), 1.0).astype(np.float32)
+    grow = np.where(np.arange(n) < 600, 2.0 ** -6, 4.0).astype(np.float32)
+    v = (v.reshape(B, n, h) * grow[None, :, None]).reshape(B * n, h).astype(np.float16)
+    kc = torch.zeros((B, H, n, d // 2), dtype=torch.uint8, device="cuda:0")
+    km = torch.zeros((B, H, n, d // 64, 2), dtype=torch.float16, device="cuda:0")
+    vc, vm = torch.zeros_like(kc), torch.zeros_like(km)
+    view = fq.kv_layer_view(kc, km, vc, vm)
+    fq.fq_kv_append(view, dev(k), dev(v), h, 0, B, n, 0)
+    torch.cuda.synchronize()
+    to4 = lambda a: np.ascontiguousarray(a.reshape(B, n, H, d).transpose(0, 2, 1, 3))
+    kh = oracle.dequant_f64(*oracle.quantize(to4(k)))
+    vh = oracle.dequant_f64(*oracle.quantize(to4(v)))
+    q = (synth.normal_f16(0, synth.STREAM["aux"] + 26, (B, h), 1.0).astype(np.float32) * d ** -0.5).astype(np.float16)
+    out = torch.empty((B, h), dtype=torch.float16, device="cuda:0")
+    fq.fq_decode_attention(dev(q), view, 0, B, n, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention_decode(q.reshape(B, H, d), kh, vh).reshape(B, h)
+    assert_close(host(out), ref, rel=2e-3, abs_=1.6e-2, what=f"decode d={d} growing values")
+    T, pos = 130, n - 130
+    qp = (synth.normal_f16(1, synth.STREAM["aux"] + 27, (B * T, h), 1.0).astype(np.float32)
+          * d ** -0.5).astype(np.float16)
+    outp = torch.empty((B * T, h), dtype=torch.float16, device="cuda:0")
+    fq.fq_prefill_attention(dev(qp), view, 0, B, T, pos, outp)
+    torch.cuda.synchronize()
+    q4 = qp.reshape(B, T, H, d).transpose(0, 2, 1, 3).astype(np.float64)
+    refp = np.empty((B, H, T, d))
+    for t in range(T):
+        refp[:, :, t] = oracle.attention_decode(q4[:, :, t], kh[:, :, :pos + t + 1], vh[:, :, :pos + t + 1])
+    refp = refp.transpose(0, 2, 1, 3).reshape(B * T, h)
+    assert_close(host(outp), refp, rel=2e-3, abs_=1.6e-2, what=f"prefill d={d} growing values")
+
+
 def test_decode_full_size_sampled():
     """OPT-175B shape at decode: batch 144, 96 heads x 128, 543 cached positions;
     the cache is filled for all sequences, sampled (b, h) pairs are checked."""
