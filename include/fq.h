@@ -199,18 +199,34 @@ fq_status fq_kv_append(const fq_kv_layer* kv, const uint16_t* k, const uint16_t*
  * cache compressed to 4 bits); one decode step is one generated token of the
  * README's "Benchmark Results" workload (output length 32).  Scores and the
  * softmax are fp32; the value pass multiplies each position's probability by
- * its group scale and rounds that product to fp16 before the fp32 dot
- * product with the exact codes.
+ * its group scale and a power of two (2^-E, 2^E just above the largest such
+ * scale the lane has seen) and rounds that product to fp16 before the fp32
+ * dot product with the exact codes; the group minima enter in fp32.  Error of
+ * that rounding per output element: at most 2^-11 * sum_j p_j s_j |c_j| /
+ * sum_j p_j, plus 2^-25 * 2^E * 15 per term below fp16's normal range.
  *   q:   device fp16 [B, heads*head_dim] row stride ldq, already scaled by
  *        head_dim^-1/2
  *   out: device fp16 [B, heads*head_dim] row stride ldo
- *   uses cache sequences b0..b0+B-1, positions 0..len-1 (1 <= len <= capacity). */
+ *   uses cache sequences b0..b0+B-1, positions 0..len-1 (1 <= len <= capacity).
+ * Errors: FQ_ERR_INVALID if b0+B > batch, len outside [1, capacity] or above
+ * 30000 (the scores are held in LDS), strides below heads*head_dim or ldq
+ * not a multiple of 8, or q/out NULL or q not 16-byte aligned;
+ * FQ_ERR_UNSUPPORTED for a group other than 64 or head_dim other than 64/128. */
 fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
                               int64_t len, uint16_t* out, int64_t ldo, void* stream);
 
 /* Causal attention of T new tokens at positions pos..pos+T-1 (already
- * appended to the cache): query t sees cache positions 0..pos+t.
- *   q: device fp16 rows b*T + t, stride ldq (scaled);  out: same layout, ldo. */
+ * appended to the cache): query t sees cache positions 0..pos+t -- the
+ * prompt pass of the README's "Benchmark Results" workload (input length 512)
+ * over the 4-bit attention cache ("Extreme Compression").  On the matrix
+ * cores with the codes as exact fp16 integers: per quantisation group g the
+ * scores are s_g (q . c) + min_g sum(q_g) in fp32; the values take the codes
+ * centred (c - 8) against fp16(p * s_g * 2^-E_g) (2^E_g just above the
+ * largest value scale of the group among the keys read), the minima (+ 8 s)
+ * in fp32.  An fp16 cache is read as stored.
+ *   q: device fp16 rows b*T + t, stride ldq (scaled);  out: same layout, ldo.
+ * Errors: FQ_ERR_INVALID if b0+B > batch, pos+T > capacity, strides below
+ * heads*head_dim or not multiples of 8, or q/out NULL or not 16-byte aligned. */
 fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer* kv, int64_t b0, int64_t B,
                                int64_t T, int64_t pos, uint16_t* out, int64_t ldo, void* stream);
 
