@@ -1614,22 +1614,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   mfma_results_ready();  // the last MFMAs' results are read below
 
+  if (partial) {
+    // fp32 split-K partials: one element per store, 16 consecutive columns
+    // per 16 lanes (staging them through LDS first was slower here)
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + wn * TN + j * 16 + fr;
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * TN + j * 16 + fr;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + i * 16 + 4 * fk + r;
-        if (m < M && n < N) {
-          if (partial)
-            partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
-          else
-            epilogue_store(epi, m, n, acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + i * 16 + 4 * fk + r;
+          if (m < M && n < N) partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
         }
       }
-    }
+    return;
+  }
+  // Final outputs: staged through LDS (the code slots, free now), 16 rows x 64
+  // columns per wave at a time (row stride 68 floats), so that each lane
+  // holds 16 consecutive columns of one row and runs the epilogue on 8-column
+  // chunks (16-byte loads of bias and residual, 16-byte stores) instead of one
+  // element at a time.
+  {
+    constexpr int SROW = 68;
+    static_assert(4 * 16 * SROW * 4 <= SC * C_BYTES, "epilogue staging fits the code slots");
+    float* stg = reinterpret_cast<float*>(c_lds) + wn * (16 * SROW);
+    const bool vec = epilogue_vec_ok(epi);
+    const int rr = lane >> 2, cs = (lane & 3) * 16;
+    static_for<MB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(4 * fk + r) * SROW + j * 16 + fr] = acc[i][j][r];
+      __syncthreads();
+      const int64_t m = m0 + i * 16 + rr;
+      const int64_t nw = n0 + wn * TN + cs;  // this lane's 16 columns
+      const float* src = stg + rr * SROW + cs;
+      if (m < M) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 8) {
+          const float4 lo = *reinterpret_cast<const float4*>(src + c);
+          const float4 hi = *reinterpret_cast<const float4*>(src + c + 4);
+          const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          epilogue_store8(epi, m, nw + c, v, N, vec);
+        }
+      }
+      __syncthreads();
+    });
   }
 }
 
