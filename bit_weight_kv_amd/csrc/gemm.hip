@@ -783,11 +783,17 @@ __device__ inline void kv_append_epilogue(const Epilogue& e, const KvAppend& kv,
 // 256 x 256 block tile, 4 waves side by side in N, each 256 x 64 (16 x 4 MFMA
 // 16x16x32 tiles, 256 fp32 accumulators pinned to AGPRs), K step 64 (two
 // MFMA k slices, one quantisation group) per barrier.
-//   * A: four LDS stages of 256 rows x 128 bytes (chunk c of row r at slot
-//     c ^ (r & 7)); step kt+3's copies are issued during step kt, one copy
-//     instruction per row block of MFMAs.
-//   * codes: three slots of 256 rows x 32 code bytes + 256 {min, scale}
-//     pairs; step kt+3's copies are issued during step kt.
+//   * A: four LDS stages of 256 rows x 128 bytes (16-byte chunk c of row r
+//     at slot c ^ ((r / 2) & 7)); step kt+3's copies are issued during step
+//     kt, one copy instruction per row block of MFMAs.
+//   * codes: three slots of 256 rows x 32 code bytes (16-byte half c of row
+//     r at slot c ^ ((r / 8) & 1)) + 256 {min, scale} pairs; step kt+3's
+//     copies are issued during step kt.
+//   * k order: slice ks of lane group g (lanes 16 g .. 16 g + 15) covers the
+//     step's 8-element k chunk 2 g + ks on both operands, so a lane's two
+//     code words of a step are adjacent (one 8-byte LDS read per column
+//     block); with the two swizzles every 32 lanes of a fragment or code read
+//     touch each LDS bank equally often.
 //   * the weight operand never passes through LDS as fp16: each wave rebuilds
 //     its own 64 weight rows x the next step's 64 k (8 code words per lane)
 //     in registers, one rebuild carried by every 16 MFMAs; no two waves
@@ -862,9 +868,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // a fixed 32-bit byte offset per lane.  The wave index is read into a
   // scalar register once, so every LDS destination is scalar too.
   //   A: instruction q (0..31) fills rows 8q..8q+7 (lane -> row 8q + lane / 8,
-  //   slot lane & 7 holding chunk slot ^ (row & 7)); wave w issues q = w + 4t.
+  //   slot lane & 7 holding chunk slot ^ ((row / 2) & 7)); wave w issues
+  //   q = w + 4t.
   //   codes: instruction p (0..7) fills rows 32p..32p+31 (lane -> row
-  //   32p + lane / 2, 16 bytes each); wave w issues p = w and w + 4.
+  //   32p + lane / 2, slot lane & 1 holding half slot ^ ((row / 8) & 1));
+  //   wave w issues p = w and w + 4.
   //   meta: wave w copies rows 64w..64w+63, 4 bytes per lane.
   // Rows beyond M or N are clamped to the last one: read, never stored.
   const int swave = __builtin_amdgcn_readfirstlane(wave);
@@ -875,11 +883,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int r = 8 * (wave + 4 * t) + (lane >> 3);
-    a_off[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * lda * 2 + ((lane & 7) ^ (r & 7)) * 16);
+    a_off[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * lda * 2 + ((lane & 7) ^ ((r >> 1) & 7)) * 16);
   }
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-    c_off[t] = (uint32_t)((min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) - n0) * (K / 2) + (lane & 1) * 16);
+  for (int t = 0; t < 2; ++t) {
+    const int r = 32 * (wave + 4 * t) + (lane >> 1);
+    c_off[t] = (uint32_t)((min(n0 + r, N - 1) - n0) * (K / 2) + ((lane & 1) ^ ((r >> 3) & 1)) * 16);
+  }
   const uint32_t m_off = (uint32_t)((min(n0 + 64 * wave + lane, N - 1) - n0) * (K / 64) * 4);
   const uint32_t m_base = (uint32_t)(uintptr_t)m_lds;
   const uint32_t c_base = (uint32_t)(uintptr_t)c_lds;
@@ -898,7 +908,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     dma_lds16_s(m_off, m_blk + (int64_t)g * 16, m_base + buf * M_BYTES + swave * 1024);
   };
   // this lane's weight operand: column block j = weight row 64 wn + 16 j + fr,
-  // slice ks = k chunk 4 ks + fk of the step (one code word), {min, scale} per row
+  // slice ks = k chunk 2 fk + ks of the step (one code word), {min, scale} per row
   uint32_t cw[2][FN], cm[FN];
   auto read_codes = [&](int kt) {
     const uint8_t* slot = c_lds + (kt % SC) * C_BYTES;
@@ -906,8 +916,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = wn * TN + j * 16 + fr;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) cw[ks][j] = *reinterpret_cast<const uint32_t*>(slot + row * 32 + (4 * ks + fk) * 4);
+      const uint2 w = *reinterpret_cast<const uint2*>(slot + row * 32 + (((fk >> 1) ^ ((row >> 3) & 1)) * 16) +
+                                                      (fk & 1) * 8);
+      cw[0][j] = w.x, cw[1][j] = w.y;
       cm[j] = *reinterpret_cast<const uint32_t*>(mrow + row * 16);
     }
   };
@@ -921,7 +932,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto a_frag = [&](const uint8_t* As_, int ks, int i) {
     const int r = i * 16 + fr;
-    return *reinterpret_cast<const half8_t*>(As_ + r * ROWB + (((4 * ks + fk) ^ (r & 7)) * 16));
+    return *reinterpret_cast<const half8_t*>(As_ + r * ROWB + (((2 * fk + ks) ^ ((r >> 1) & 7)) * 16));
   };
 
   float4_t acc[FM][FN];
