@@ -1443,10 +1443,10 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
 // Slice ks gives lane group g the k chunk 2 g + ks (8 values), as the
 // two-waves-per-SIMD decode kernel does, so the two add the same products in
 // the same order (outputs identical bit for bit).
-template <int MB>
+template <int MB, bool SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_decode_w4_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t lda, const uint8_t* __restrict__ codes,
-    const uint16_t* __restrict__ meta, int64_t N, int64_t K, int k_tiles_per_split, Epilogue epi,
+    const uint16_t* __restrict__ meta, int64_t N, int64_t K, int k_tiles_per_split, int sk_per, Epilogue epi,
     float* __restrict__ partial) {
   constexpr int ROWS = MB * 16, NSL = 2 * MB;        // A rows per block, row-block slots per step
   constexpr int NQ = ROWS / 8;                       // A copies per step (8 rows of 128 B)
@@ -1471,221 +1471,254 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave, fr = lane & 15, fk = lane >> 4;
   const int swave = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t n0 = (int64_t)blockIdx.x * 256, m0 = (int64_t)blockIdx.z * ROWS;
+  const int64_t m0 = (int64_t)blockIdx.z * ROWS;
   const int KT = (int)(K / BK);
-  const int kt0 = blockIdx.y * k_tiles_per_split;
-  const int kt1 = min(KT, kt0 + k_tiles_per_split);  // kt1 - kt0: a positive multiple of 4 (host)
+  // One segment: K steps kt0..kt1 (a positive multiple of 4, host) of the
+  // 256-column tile at n0; fp32 partials, if any, to slab `slab`.
+  auto segment = [&](const int64_t n0, const int kt0, const int kt1, const int slab) {
 
-  const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(A + m0 * lda);
-  const uint8_t* c_blk = codes + n0 * (K / 2);
-  const uint8_t* m_blk = reinterpret_cast<const uint8_t*>(meta + n0 * (K / 64) * 2);
-  // A: instruction q = w + 4t (q < NQ) fills rows 8q..8q+7; codes: instruction
-  // p = w, w + 4 fills rows 32p..32p+31; meta: wave w rows 64w..64w+63
-  uint32_t a_off[A_MAX], c_off[2];
+    const uint8_t* a_blk = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+    const uint8_t* c_blk = codes + n0 * (K / 2);
+    const uint8_t* m_blk = reinterpret_cast<const uint8_t*>(meta + n0 * (K / 64) * 2);
+    // A: instruction q = w + 4t (q < NQ) fills rows 8q..8q+7; codes: instruction
+    // p = w, w + 4 fills rows 32p..32p+31; meta: wave w rows 64w..64w+63
+    uint32_t a_off[A_MAX], c_off[2];
 #pragma unroll
-  for (int t = 0; t < A_MAX; ++t) {
-    const int r = 8 * (wave + 4 * t) + (lane >> 3);
-    a_off[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * lda * 2 + ((lane & 7) ^ (r & 7)) * 16);
-  }
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    c_off[t] = (uint32_t)((min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) - n0) * (K / 2) + (lane & 1) * 16);
-  const uint32_t m_off = (uint32_t)((min(n0 + 64 * wave + lane, N - 1) - n0) * (K / 64) * 4);
-  const uint32_t c_base = (uint32_t)(uintptr_t)c_lds, m_base = (uint32_t)(uintptr_t)m_lds;
-  auto issue_a = [&](auto s, int kt) {
-    const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + swave * 1024;
-#pragma unroll
-    for (int t = 0; t < A_MAX; ++t)
-      if (t + 1 < A_MAX || swave < EXTRA) dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, dst + t * 4096);
-  };
-  auto issue_codes = [&](int kt) {
-    const uint32_t dst = c_base + (kt % SC) * C_BYTES;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) dma_lds16_s(c_off[t], c_blk + (int64_t)kt * 32, dst + (swave + 4 * t) * 1024);
-  };
-  // {min, scale} of 4-step group g into buffer buf
-  auto issue_meta = [&](int g, int buf) {
-    dma_lds16_s(m_off, m_blk + (int64_t)g * 16, m_base + buf * M_BYTES + swave * 1024);
-  };
-  uint32_t cw[2][FN], cm[FN];
-  auto read_codes = [&](int kt) {
-    const uint8_t* slot = c_lds + (kt % SC) * C_BYTES;
-    const uint8_t* mrow = m_lds + ((kt >> 2) & 1) * M_BYTES + (kt & 3) * 4;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wn * TN + j * 16 + fr;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) cw[ks][j] = *reinterpret_cast<const uint32_t*>(slot + row * 32 + (2 * fk + ks) * 4);
-      cm[j] = *reinterpret_cast<const uint32_t*>(mrow + row * 16);
+    for (int t = 0; t < A_MAX; ++t) {
+      const int r = 8 * (wave + 4 * t) + (lane >> 3);
+      a_off[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * lda * 2 + ((lane & 7) ^ (r & 7)) * 16);
     }
-  };
-  auto rebuild = [&](int ks, int j) {
-    const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
-    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
-    const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
-    uint32_t o[4];
-    dequant8(cw[ks][j], mn2, s2, o);
-    return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
-  };
-  auto a_frag = [&](const uint8_t* As_, int ks, int i) {
-    const int r = i * 16 + fr;
-    return *reinterpret_cast<const half8_t*>(As_ + r * 128 + (((2 * fk + ks) ^ (r & 7)) * 16));
-  };
-
-  float4_t acc[MB][FN];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int t = 0; t < 2; ++t)
+      c_off[t] = (uint32_t)((min(n0 + 32 * (wave + 4 * t) + (lane >> 1), N - 1) - n0) * (K / 2) + (lane & 1) * 16);
+    const uint32_t m_off = (uint32_t)((min(n0 + 64 * wave + lane, N - 1) - n0) * (K / 64) * 4);
+    const uint32_t c_base = (uint32_t)(uintptr_t)c_lds, m_base = (uint32_t)(uintptr_t)m_lds;
+    auto issue_a = [&](auto s, int kt) {
+      const uint32_t dst = (uint32_t)(uintptr_t)a_st(s) + swave * 1024;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  // prologue: codes and A of the split's first three steps, {min, scale} of
-  // its first 4-step group; operand of the first step rebuilt
-  issue_codes(kt0);
-  issue_codes(kt0 + 1);
-  issue_codes(kt0 + 2);
-  issue_meta(kt0 >> 2, (kt0 >> 2) & 1);
-  issue_a(I0{}, kt0);
-  issue_a(I1{}, kt0 + 1);
-  issue_a(I2{}, kt0 + 2);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  half8_t bA[2][FN], bB[2][FN];
-  read_codes(kt0);
+      for (int t = 0; t < A_MAX; ++t)
+        if (t + 1 < A_MAX || swave < EXTRA) dma_lds16_s(a_off[t], a_blk + (int64_t)kt * 128, dst + t * 4096);
+    };
+    auto issue_codes = [&](int kt) {
+      const uint32_t dst = c_base + (kt % SC) * C_BYTES;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+      for (int t = 0; t < 2; ++t) dma_lds16_s(c_off[t], c_blk + (int64_t)kt * 32, dst + (swave + 4 * t) * 1024);
+    };
+    // {min, scale} of 4-step group g into buffer buf
+    auto issue_meta = [&](int g, int buf) {
+      dma_lds16_s(m_off, m_blk + (int64_t)g * 16, m_base + buf * M_BYTES + swave * 1024);
+    };
+    uint32_t cw[2][FN], cm[FN];
+    auto read_codes = [&](int kt) {
+      const uint8_t* slot = c_lds + (kt % SC) * C_BYTES;
+      const uint8_t* mrow = m_lds + ((kt >> 2) & 1) * M_BYTES + (kt & 3) * 4;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bA[ks][j] = rebuild(ks, j);
-  half8_t fa[RING];
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * TN + j * 16 + fr;
 #pragma unroll
-  for (int t = 0; t < 3; ++t) fa[t] = a_frag(a_lds0, t / MB, t % MB);
-
-  // step kt (S = (kt - kt0) % 4): as in the prefill kernel; per wave A_w + 2
-  // copies, + 1 {min, scale} copy when S == 0 (group kt/4 + 1)
-  auto step = [&](auto s, int kt) {
-    constexpr int S = decltype(s)::value;
-    constexpr int P = S & 1;
-    using S3 = std::integral_constant<int, (S + 3) % 4>;
-    using S1 = std::integral_constant<int, (S + 1) % 4>;
-    half8_t(&bcur)[2][FN] = P == 0 ? bA : bB;
-    half8_t(&bnxt)[2][FN] = P == 0 ? bB : bA;
-    const uint8_t* As_ = a_st(s);
-    read_codes(kt + 1);  // stale but harmless past the split's last step
-    const int kc = min(kt + 3, kt1 - 1);
-    const uint8_t* a_step = a_blk + (int64_t)kc * 128;
-    const uint8_t* c_step = c_blk + (int64_t)kc * 32;
-    const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
-    const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
-    const int gm = min((kt >> 2) + 1, (kt1 >> 2) - 1);
-    static_for<NSL>([&](auto sc) {
-      constexpr int SL = decltype(sc)::value;
-      constexpr int ks = SL / MB, i = SL % MB;
-      if constexpr (SL < A_MAX) {
-        if (SL + 1 < A_MAX || swave < EXTRA) dma_lds16_s(a_off[SL], a_step, a_dst + SL * 4096);
-      } else if constexpr (SL == 5 || SL == 6) {
-        dma_lds16_s(c_off[SL - 5], c_step, c_dst + (swave + 4 * (SL - 5)) * 1024);
-      } else if constexpr (SL == 7 && S == 0) {
-        // group kt/4 + 1 into its buffer; past the split's end the copy is
-        // clamped to the last group but still lands in the buffer no later
-        // step reads
-        issue_meta(gm, ((kt >> 2) + 1) & 1);
+        for (int ks = 0; ks < 2; ++ks) cw[ks][j] = *reinterpret_cast<const uint32_t*>(slot + row * 32 + (2 * fk + ks) * 4);
+        cm[j] = *reinterpret_cast<const uint32_t*>(mrow + row * 16);
       }
-      constexpr int NX = SL + 3;
-      fa[NX % RING] = NX < NSL ? a_frag(As_, NX / MB, NX % MB) : a_frag(a_st(S1{}), (NX - NSL) / MB, (NX - NSL) % MB);
-      __builtin_amdgcn_sched_barrier(0);
-      const half8_t& af = fa[SL % RING];
-      if constexpr (SL >= NSL - 8) {
-        constexpr int r = SL - (NSL - 8);
-        half8_t nb;
-        mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
-                         bcur[ks][2], bcur[ks][3], cw[r / FN][r % FN], cm[r % FN], nb);
-        bnxt[r / FN][r % FN] = nb;
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
-      }
-    });
-    if (swave < EXTRA) {
-      if constexpr (S == 0)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 3) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 2) : "memory");
-    } else {
-      if constexpr (S == 0)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 2) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 1) : "memory");
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), where the compiler sees it
-  };
-  for (int kt = kt0; kt < kt1; kt += 4) {
-    step(I0{}, kt);
-    step(I1{}, kt + 1);
-    step(I2{}, kt + 2);
-    step(I3{}, kt + 3);
-  }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  mfma_results_ready();  // the last MFMAs' results are read below
+    };
+    auto rebuild = [&](int ks, int j) {
+      const half_t mn = __builtin_bit_cast(half_t, (uint16_t)(cm[j] & 0xFFFF));
+      const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(cm[j] >> 16));
+      const half2_t mn2 = {mn, mn}, s2 = {sc, sc};
+      uint32_t o[4];
+      dequant8(cw[ks][j], mn2, s2, o);
+      return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+    };
+    auto a_frag = [&](const uint8_t* As_, int ks, int i) {
+      const int r = i * 16 + fr;
+      return *reinterpret_cast<const half8_t*>(As_ + r * 128 + (((2 * fk + ks) ^ (r & 7)) * 16));
+    };
 
-  if (partial) {
-    // fp32 split-K partials: one element per store, 16 consecutive columns
-    // per 16 lanes (staging them through LDS first was slower here)
+    float4_t acc[MB][FN];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t n = n0 + wn * TN + j * 16 + fr;
+      for (int j = 0; j < FN; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // prologue: codes and A of the split's first three steps, {min, scale} of
+    // its first 4-step group; operand of the first step rebuilt
+    issue_codes(kt0);
+    issue_codes(kt0 + 1);
+    issue_codes(kt0 + 2);
+    issue_meta(kt0 >> 2, (kt0 >> 2) & 1);
+    issue_a(I0{}, kt0);
+    issue_a(I1{}, kt0 + 1);
+    issue_a(I2{}, kt0 + 2);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    half8_t bA[2][FN], bB[2][FN];
+    read_codes(kt0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t m = m0 + i * 16 + 4 * fk + r;
-          if (m < M && n < N) partial[((int64_t)blockIdx.y * M + m) * N + n] = acc[i][j][r];
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bA[ks][j] = rebuild(ks, j);
+    half8_t fa[RING];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) fa[t] = a_frag(a_lds0, t / MB, t % MB);
+
+    // step kt (S = (kt - kt0) % 4): as in the prefill kernel; per wave A_w + 2
+    // copies, + 1 {min, scale} copy when S == 0 (group kt/4 + 1)
+    auto step = [&](auto s, int kt) {
+      constexpr int S = decltype(s)::value;
+      constexpr int P = S & 1;
+      using S3 = std::integral_constant<int, (S + 3) % 4>;
+      using S1 = std::integral_constant<int, (S + 1) % 4>;
+      half8_t(&bcur)[2][FN] = P == 0 ? bA : bB;
+      half8_t(&bnxt)[2][FN] = P == 0 ? bB : bA;
+      const uint8_t* As_ = a_st(s);
+      read_codes(kt + 1);  // stale but harmless past the split's last step
+      const int kc = min(kt + 3, kt1 - 1);
+      const uint8_t* a_step = a_blk + (int64_t)kc * 128;
+      const uint8_t* c_step = c_blk + (int64_t)kc * 32;
+      const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
+      const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
+      const int gm = min((kt >> 2) + 1, (kt1 >> 2) - 1);
+      static_for<NSL>([&](auto sc) {
+        constexpr int SL = decltype(sc)::value;
+        constexpr int ks = SL / MB, i = SL % MB;
+        if constexpr (SL < A_MAX) {
+          if (SL + 1 < A_MAX || swave < EXTRA) dma_lds16_s(a_off[SL], a_step, a_dst + SL * 4096);
+        } else if constexpr (SL == 5 || SL == 6) {
+          dma_lds16_s(c_off[SL - 5], c_step, c_dst + (swave + 4 * (SL - 5)) * 1024);
+        } else if constexpr (SL == 7 && S == 0) {
+          // group kt/4 + 1 into its buffer; past the split's end the copy is
+          // clamped to the last group but still lands in the buffer no later
+          // step reads
+          issue_meta(gm, ((kt >> 2) + 1) & 1);
         }
-      }
-    return;
-  }
-  // Final outputs: staged through LDS (the code slots, free now), 16 rows x 64
-  // columns per wave at a time (row stride 68 floats), so that each lane
-  // holds 16 consecutive columns of one row and runs the epilogue on 8-column
-  // chunks (16-byte loads of bias and residual, 16-byte stores) instead of one
-  // element at a time.
-  {
-    constexpr int SROW = 68;
-    static_assert(4 * 16 * SROW * 4 <= SC * C_BYTES, "epilogue staging fits the code slots");
-    float* stg = reinterpret_cast<float*>(c_lds) + wn * (16 * SROW);
-    const bool vec = epilogue_vec_ok(epi);
-    const int rr = lane >> 2, cs = (lane & 3) * 16;
-    static_for<MB>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
+        constexpr int NX = SL + 3;
+        fa[NX % RING] = NX < NSL ? a_frag(As_, NX / MB, NX % MB) : a_frag(a_st(S1{}), (NX - NSL) / MB, (NX - NSL) % MB);
+        __builtin_amdgcn_sched_barrier(0);
+        const half8_t& af = fa[SL % RING];
+        if constexpr (SL >= NSL - 8) {
+          constexpr int r = SL - (NSL - 8);
+          half8_t nb;
+          mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
+                           bcur[ks][2], bcur[ks][3], cw[r / FN][r % FN], cm[r % FN], nb);
+          bnxt[r / FN][r % FN] = nb;
+        } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) stg[(4 * fk + r) * SROW + j * 16 + fr] = acc[i][j][r];
-      __syncthreads();
-      const int64_t m = m0 + i * 16 + rr;
-      const int64_t nw = n0 + wn * TN + cs;  // this lane's 16 columns
-      const float* src = stg + rr * SROW + cs;
-      if (m < M) {
-#pragma unroll
-        for (int c = 0; c < 16; c += 8) {
-          const float4 lo = *reinterpret_cast<const float4*>(src + c);
-          const float4 hi = *reinterpret_cast<const float4*>(src + c + 4);
-          const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          epilogue_store8(epi, m, nw + c, v, N, vec);
+          for (int j = 0; j < FN; ++j) mfma16x16x32_acc_ordered(acc[i][j], af, bcur[ks][j]);
         }
+      });
+      if (swave < EXTRA) {
+        if constexpr (S == 0)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 3) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 2) : "memory");
+      } else {
+        if constexpr (S == 0)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 2) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(A_MAX + 1) : "memory");
       }
-      __syncthreads();
-    });
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), where the compiler sees it
+    };
+    for (int kt = kt0; kt < kt1; kt += 4) {
+      step(I0{}, kt);
+      step(I1{}, kt + 1);
+      step(I2{}, kt + 2);
+      step(I3{}, kt + 3);
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    mfma_results_ready();  // the last MFMAs' results are read below
+
+    if (SK || partial) {
+      // fp32 split-K partials: one element per store, 16 consecutive columns
+      // per 16 lanes (staging them through LDS first was slower here)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = n0 + wn * TN + j * 16 + fr;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + i * 16 + 4 * fk + r;
+            if (m < M && n < N) partial[((int64_t)slab * M + m) * N + n] = acc[i][j][r];
+          }
+        }
+      return;
+    }
+    // Final outputs: staged through LDS (the code slots, free now), 16 rows x 64
+    // columns per wave at a time (row stride 68 floats), so that each lane
+    // holds 16 consecutive columns of one row and runs the epilogue on 8-column
+    // chunks (16-byte loads of bias and residual, 16-byte stores) instead of one
+    // element at a time.
+    {
+      constexpr int SROW = 68;
+      static_assert(4 * 16 * SROW * 4 <= SC * C_BYTES, "epilogue staging fits the code slots");
+      float* stg = reinterpret_cast<float*>(c_lds) + wn * (16 * SROW);
+      const bool vec = epilogue_vec_ok(epi);
+      const int rr = lane >> 2, cs = (lane & 3) * 16;
+      static_for<MB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) stg[(4 * fk + r) * SROW + j * 16 + fr] = acc[i][j][r];
+        __syncthreads();
+        const int64_t m = m0 + i * 16 + rr;
+        const int64_t nw = n0 + wn * TN + cs;  // this lane's 16 columns
+        const float* src = stg + rr * SROW + cs;
+        if (m < M) {
+#pragma unroll
+          for (int c = 0; c < 16; c += 8) {
+            const float4 lo = *reinterpret_cast<const float4*>(src + c);
+            const float4 hi = *reinterpret_cast<const float4*>(src + c + 4);
+            const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            epilogue_store8(epi, m, nw + c, v, N, vec);
+          }
+        }
+        __syncthreads();
+      });
+    }
+  };
+  if constexpr (SK) {
+    // Stream K (one block per CU): the block runs (256-column tile, K step)
+    // units blockIdx.x * sk_per onward, sk_per of them, tile-major, in one
+    // segment per tile it touches; a tile's segments go to partial slabs 0,
+    // 1, ... in the order of the blocks that run them.  A segment's LDS reads
+    // all complete before its last barrier, so the next segment's copies may
+    // overwrite the rings.  (32-bit unit arithmetic: the host keeps
+    // n_tiles * KT below 2^31.)
+    const int n_tiles = (int)((N + 255) / 256);
+    int unit = (int)blockIdx.x * sk_per;
+    const int unit_end = min(unit + sk_per, n_tiles * KT);
+    while (unit < unit_end) {
+      const int tile = unit / KT;
+      const int kt0 = unit - tile * KT;
+      const int kt1 = min(KT, kt0 + (unit_end - unit));
+      segment((int64_t)tile * 256, kt0, kt1, (int)blockIdx.x - tile * KT / sk_per);
+      unit = tile * KT + kt1;
+    }
+  } else {
+    // Split K: tile blockIdx.x, steps from blockIdx.y * k_tiles_per_split,
+    // partial slab blockIdx.y (no partials when K is not split)
+    const int kt0 = blockIdx.y * k_tiles_per_split;
+    segment((int64_t)blockIdx.x * 256, kt0, min(KT, kt0 + k_tiles_per_split), (int)blockIdx.y);
   }
 }
 
 // Sum of the split-K partials ([split][M][N] fp32), in split order from
 // zero, then the epilogue: 8 columns of one row per thread, with 16-byte
-// loads when N is a multiple of 8 (every chunk whole and aligned).
+// loads when N is a multiple of 8 (every chunk whole and aligned).  With
+// sk_per > 0 (the stream-K schedule of the decode kernel over KT steps) the
+// 256-column tile t holds one slab per block that ran part of it:
+// (t + 1) KT / sk_per - t KT / sk_per of them, rounded as the kernel splits.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int64_t M,
-                                                            int64_t N, Epilogue epi) {
+                                                            int64_t N, Epilogue epi, int64_t KT = 0, int sk_per = 0) {
   const int64_t nc = (N + 7) / 8;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= M * nc) return;
   const int64_t m = t / nc, n = (t - m * nc) * 8;
   const int64_t mn = M * N;
+  if (sk_per > 0) {
+    const int64_t tile = n / 256;
+    splits = (int)(((tile + 1) * KT - 1) / sk_per - tile * KT / sk_per + 1);
+  }
   const float* p = partial + m * N + n;
   float v[8];
 #pragma unroll
@@ -1785,7 +1818,7 @@ fq_status run_skinny(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
 // takes most of a CU's LDS), so pick the split that minimises rounds of 256
 // blocks x (K steps per block + ring fill), plus the fp32 partial traffic
 // (written and read back by the reduction) priced at 4 TB/s.
-int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB) {
+int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB, double* t_out) {
   // measured: one K step of a block takes ~1.3 us at 9 row groups
   const double step_us = std::max(0.15, 0.145 * MB);
   int best = 1;
@@ -1800,7 +1833,40 @@ int decode_splits(int64_t nblk, int KT, int64_t M, int64_t N, int MB) {
       best = s;
     }
   }
+  *t_out = best_t;
   return best;
+}
+
+// Stream-K schedule of the one-wave-per-SIMD decode kernel: 256 / zb blocks
+// per row group (one per CU), each running `per` consecutive (256-column tile,
+// K step) units, a multiple of 4, in one segment per tile it touches; each
+// segment writes an fp32 partial slab that the reduction sums in block order.
+// It removes the partly filled last round of a split-K grid at the price of a
+// ring fill per segment and more partial slabs.  Priced with the split-K
+// model: steps plus ring fills of the busiest block, partials at 4 TB/s.
+struct StreamK {
+  int per = 0;        // units per block
+  int blocks = 0;     // blocks per row group
+  int max_slabs = 0;  // the most segments any tile has
+  double t = 1e30;    // predicted time, us
+};
+StreamK stream_k_plan(int64_t n_tiles, int KT, int64_t zb, int64_t M, int MB) {
+  const double step_us = std::max(0.15, 0.145 * MB);
+  StreamK p;
+  const int64_t total = n_tiles * KT;
+  const int64_t per = (ceil_div(total, std::max<int64_t>(1, 256 / zb)) + 3) & ~int64_t{3};
+  int64_t segs = 0, max_s = 0;
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int64_t sgs = ((t + 1) * KT - 1) / per - t * KT / per + 1;
+    segs += sgs;
+    max_s = std::max(max_s, sgs);
+  }
+  p.per = (int)per;
+  p.blocks = (int)ceil_div(total, per);
+  p.max_slabs = (int)max_s;
+  p.t = (per + 6.0 * (double)std::min<int64_t>(ceil_div(per, KT) + 1, n_tiles)) * step_us +
+        (double)segs * M * 256 * 8.0 / 4e6;
+  return p;
 }
 
 template <int MB>
@@ -1808,22 +1874,35 @@ fq_status run_decode(const uint16_t* A, int64_t M, int64_t lda, const fq_weight*
                      hipStream_t st) {
   const int64_t N = W->n;
   const int KT = (int)(W->k / BK);
-  const int64_t zb = ceil_div(M, 16 * MB);
-  int splits = decode_splits(ceil_div(N, 256) * zb, KT, M, N, MB);
+  const int64_t zb = ceil_div(M, 16 * MB), n_tiles = ceil_div(N, 256);
+  double split_t = 0.0;
+  int splits = decode_splits(n_tiles * zb, KT, M, N, MB, &split_t);
   // the kernel runs K steps in groups: a multiple of 4 per split when the
   // {min, scale} go 4 steps at a time (K a multiple of 256 and that array
   // 16-byte aligned), else an even number (KT is even here)
   const bool meta4 = KT % 4 == 0 && (uintptr_t)W->packed.meta % 16 == 0;
   const int kps = meta4 ? ((KT + splits - 1) / splits + 3) & ~3 : ((KT + splits - 1) / splits + 1) & ~1;
   splits = (KT + kps - 1) / kps;
+  // stream K instead where every block gets at least 16 steps and the model
+  // predicts 5 % less time (one-wave-per-SIMD kernel only)
+  const StreamK sk = meta4 ? stream_k_plan(n_tiles, KT, zb, M, MB) : StreamK{};
+  if (sk.per >= 16 && sk.t < 0.95 * split_t && n_tiles * KT < (int64_t{1} << 31)) {
+    float* partial = nullptr;
+    FQ_TRY(get_workspace((size_t)sk.max_slabs * M * N * sizeof(float), &partial));
+    gemm_decode_w4_kernel<MB, true><<<dim3((unsigned)sk.blocks, 1, (unsigned)zb), dim3(256), 0, st>>>(
+        A, M, lda, W->packed.codes, W->packed.meta, N, W->k, 0, sk.per, epi, partial);
+    FQ_TRY(launch_check("gemm_decode_w4_kernel"));
+    splitk_reduce_kernel<<<dim3(reduce_blocks(M, N)), dim3(256), 0, st>>>(partial, 0, M, N, epi, KT, sk.per);
+    return launch_check("splitk_reduce_kernel");
+  }
   float* partial = nullptr;
   if (splits > 1) FQ_TRY(get_workspace((size_t)splits * M * N * sizeof(float), &partial));
-  const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)splits, (unsigned)zb);
+  const dim3 grid((unsigned)n_tiles, (unsigned)splits, (unsigned)zb);
   // one wave per SIMD when the {min, scale} go 4 steps at a time, else the
   // two-waves-per-SIMD kernel
   if (meta4) {
-    gemm_decode_w4_kernel<MB><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k, kps,
-                                                          epi, partial);
+    gemm_decode_w4_kernel<MB, false><<<grid, dim3(256), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,
+                                                                 kps, 0, epi, partial);
     FQ_TRY(launch_check("gemm_decode_w4_kernel"));
   } else {
     gemm_decode8_kernel<MB, false><<<grid, dim3(512), 0, st>>>(A, M, lda, W->packed.codes, W->packed.meta, N, W->k,

@@ -141,8 +141,10 @@ fq_status fq_dequant_gemm(const uint16_t* A, int64_t M, int64_t lda, const fq_we
  * process ends, instead of a workspace grown with hipMalloc.  The call
  * allocates nothing and records no fq_timing_* events.
  *   Errors: those of fq_dequant_gemm, and FQ_ERR_INVALID when a shape would
- *   need more than 64 MiB of partials (the message gives the size; the
- *   decode shapes of the OPT-175B workloads need at most about 35 MB).
+ *   need more than 64 MiB of partials (the message gives the size; at batch
+ *   144 the four OPT-175B decode products need at most 61 MiB, the QKV
+ *   product's three slabs of 144 x 36864; at batch 256 that product needs
+ *   72 MiB and is rejected).
  * Calls that overlap on one GPU (several streams or host threads) share that
  * GPU's scratch and race; serialise them.  Nothing in the scratch needs to
  * start at zero (every partial read is written first in the same call). */

@@ -74,6 +74,18 @@ def test_gemm_decode_kernels(M, K):
     _tol_check(got, ref, f"decode kernel M={M} K={K}")
 
 
+@pytest.mark.parametrize("M", [200, 256])
+def test_gemm_decode_stream_k_ragged(M):
+    """The decode kernel's stream-K schedule (one block per CU, each running an
+    equal share of (256-column tile, K step) units; a tile's partial slabs
+    summed in block order): N = 1003 (a ragged last tile), K = 32768 (512
+    steps, 32 segments per tile), two row groups of 128 (the second partly
+    past M at 200 rows), bias and residual in the reduction's epilogue."""
+    log(f"gemm decode stream-K M={M} N=1003 K=32768")
+    got, ref = _run(M, 1003, 32768, fq.FQ_EPI_BIAS | fq.FQ_EPI_RESIDUAL, seed=M + 5)
+    _tol_check(got, ref, f"stream-K M={M}")
+
+
 @pytest.mark.parametrize("M,packed", [(5, True), (144, True), (37, False)])
 def test_gemm_splitk_ragged_n(M, packed):
     """Split K with N not a multiple of 8: the reduction's scalar path, the
@@ -229,11 +241,13 @@ def test_gemm_empty_m_is_noop():
     assert (out == 7.0).all()
 
 
-@pytest.mark.parametrize("M,which", [(144, "w_qkv"), (144, "w_fc2"), (8192, "w_fc1")])
+@pytest.mark.parametrize("M,which", [(144, "w_qkv"), (144, "w_fc1"), (144, "w_fc2"), (8192, "w_fc1")])
 def test_gemm_full_size_sampled(M, which):
     """OPT-175B projection shapes (h = 12288, F = 49152) in the launch
-    configuration of the decode (M = 144) and prefill-chunk (M = 8192) steps;
-    weights generated on the GPU and quantised there; sampled outputs against
+    configuration of the decode (M = 144: QKV and FC1 on the decode kernel's
+    stream-K schedule, FC2 split K) and prefill-chunk (M = 8192) steps;
+    weights generated on the GPU and quantised there; sampled outputs (the
+    first and last column of 16 random 256-column tiles among them) against
     float64 dot products of the oracle's reconstruction of the same rows."""
     h, F = 12288, 49152
     N, K = {"w_qkv": (3 * h, h), "w_fc2": (h, F), "w_fc1": (F, h)}[which]
@@ -252,7 +266,8 @@ def test_gemm_full_size_sampled(M, which):
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 10)]))
+    tiles = rng.integers(0, N // 256, 16) * 256
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 10), tiles, tiles + 255]))
     ai = (rows[:, None] * K + np.arange(K)[None]).astype(np.uint64).ravel()
     wi = (cols[:, None] * K + np.arange(K)[None]).astype(np.uint64).ravel()
     arows = synth.normal_f16(0, synth.STREAM["hidden"], sigma=1.0, index=ai).reshape(len(rows), K)

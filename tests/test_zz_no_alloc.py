@@ -66,10 +66,11 @@ def test_noalloc_matches_dequant_gemm_twice_then_smaller():
 
 
 def test_noalloc_rejects_partials_beyond_the_scratch():
-    """M 256, N 12288, K 65536: the decode kernel splits K into 8 parts of fp32
-    partials, about 100 MB, above the 64 MiB scratch: rejected before any
-    launch (the buffers are never read)."""
-    M, N, K = 256, 12288, 65536
+    """M 256, N 36864, K 12288 (the OPT-175B QKV product at batch 256): the
+    decode kernel's stream-K schedule needs two fp32 partial slabs, 72 MiB,
+    above the 64 MiB scratch: rejected before any launch (the buffers are
+    never read)."""
+    M, N, K = 256, 36864, 12288
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda:0")
     meta = torch.empty((N, K // 64, 2), dtype=torch.float16, device="cuda:0")
     W = fq.weight_packed(codes, meta, N, K)
