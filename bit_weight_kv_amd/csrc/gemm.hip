@@ -1437,12 +1437,14 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
 // side in N (64 weight rows each, one wave per SIMD) over the batch's 16 MB
 // rows, K step 64, each A fragment feeding 4 MFMAs; the same copies as the
 // prefill kernel (scalar base + 32-bit lane offsets, unconditional, {min,
-// scale} 4 steps at a time) and split-K over ranges of a multiple of 4 steps.
+// scale} 4 steps at a time); K is split over ranges of a multiple of 4
+// steps, either per tile (SK false: grid.y splits) or as a stream-K schedule
+// (SK true: one block per CU, each an equal run of (tile, step) units).
 // Slot = 16-row block of one k slice (2 MB slots per step): copies in slots
 // 0..7, rebuilds (full, 13 instructions with 4 MFMAs) in the last 8 slots.
 // Slice ks gives lane group g the k chunk 2 g + ks (8 values), as the
-// two-waves-per-SIMD decode kernel does, so the two add the same products in
-// the same order (outputs identical bit for bit).
+// two-waves-per-SIMD decode kernel does, so under the same split the two add
+// the same products in the same order (outputs identical bit for bit).
 template <int MB, bool SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_decode_w4_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t lda, const uint8_t* __restrict__ codes,
