@@ -349,6 +349,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 }
 
 // ---- causal prefill on the matrix cores ------------------------------------
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
 // Work-group = 4 waves x 32 queries of one (b, h); keys in chunks of 64.
 // Per chunk the work-group stages the chunk's K and V codes in LDS as exact
 // fp16 integers (the fp16 cache: the stored values) and, for the 4-bit cache,
@@ -357,9 +359,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 //   online softmax    (per query, reduced over the 4 lane groups)
 //   O^T += V^T P^T    (P taken straight from the S^T registers)
 // 4-bit cache, without rounding the reconstructed cache to fp16:
-//   scores: per group g, T_g = C_g Q_g^T over the group's 64 channels (exact
-//     products of fp16 queries and integer codes, fp32 sums), then
-//     s = sum_g (scale_g * T_g + min_g * sum(q_g)) in fp32;
+//   scores, in log2 units: per group g, T_g = C_g Q_g^T over the group's 64
+//     channels (exact products of fp16 queries and integer codes, fp32 sums);
+//     the min terms sum_g min_g * sum(q_g) log2(e) on the matrix cores too,
+//     from min_g (fp16) and each query's group sum times log2(e) split into
+//     two fp16 parts (hi + lo: 22 significant bits), which start the score
+//     accumulator; then one fp32 FMA per group, s += (scale_g log2(e)) T_g.
+//     If a scaled group sum reaches 2^15 (fp16 would overflow) the
+//     work-group takes all its scores 2^-e smaller (e > 0, exact) and
+//     multiplies them back inside the exponent;
 //   values: with the codes centred (c' = c - 8, exact in fp16) and
 //     min' = min + 8 scale, per group g, O_g^T += C'_g^T P'_g^T with
 //     P'_g = fp16(p * scale_g * 2^-E_g), 2^E_g the power of two just above the
@@ -389,9 +397,10 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   constexpr int MG = F16 ? 1 : G;  // {min, scale} arrays (unused with the fp16 cache)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[KHALF][KC * 64];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * KC];
-  __shared__ __attribute__((aligned(16))) float kmin_lds[MG][KC], ksc_lds[MG][KC], vmin_lds[MG][KC],
-      vsc_lds[MG][KC];
-  __shared__ float red[4][G];
+  __shared__ __attribute__((aligned(16))) float ksc_lds[MG][KC], vmin_lds[MG][KC], vsc_lds[MG][KC];
+  // each key's {min_g, min_g} fp16 pairs, g = 0, 1 (the A operand of the min-term product)
+  __shared__ __attribute__((aligned(16))) uint32_t kmin2_lds[F16 ? 1 : KC][2];
+  __shared__ float red[4][G + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -411,8 +420,15 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   }
   // 4-bit cache: sum of each group's query channels (query l16 of block qb)
   float qsum[2][G];
-  // and 2^-E_g per value group (in LDS: read at staging and at the end)
-  __shared__ float vmul[G];
+  // and 2^-E_g per value group (in LDS: read at staging and at the end);
+  // sgrp = {2^-e, 2^e}, the work-group's score scaling (1 unless a query's
+  // scaled group sum would overflow fp16)
+  __shared__ float vmul[G], sgrp[2];
+  constexpr float kL2e = 1.4426950408889634f;
+  // B operand of the min-term product (16x16x16: k = 4 * lane group + i):
+  // {hi, lo} of sum(q_g) log2(e) 2^-e for g = 0, 1 in lane group 0, zeros elsewhere
+  half4_t qminb[2];
+  float spow = 1.f;  // 2^e
   if constexpr (!F16) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -425,8 +441,15 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
           for (int e = 0; e < 8; ++e) sq += (float)qf[qb][kd][e];
         sq += __shfl_xor(sq, 16);
         sq += __shfl_xor(sq, 32);
-        qsum[qb][g] = sq;
+        qsum[qb][g] = sq * kL2e;
       }
+    float qa = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < G; ++g) qa = fmaxf(qa, fabsf(qsum[qb][g]));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) qa = fmaxf(qa, __shfl_xor(qa, o));
     float smax[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) smax[g] = 0.f;
@@ -439,6 +462,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       for (int o = 32; o > 0; o >>= 1) smax[g] = fmaxf(smax[g], __shfl_xor(smax[g], o));
       if (lane == 0) red[wave][g] = smax[g];
     }
+    if (lane == 0) red[wave][G] = qa;
     __syncthreads();
     if (tid < G) {
       const int g = tid;
@@ -446,8 +470,33 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       int e = 0;
       (void)frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1) (m = 0: e = 0)
       vmul[g] = m > 0.f ? ldexpf(1.0f, -e) : 1.0f;
+      if (g == 0) {
+        // smallest e >= 0 with every |sum(q_g) log2(e)| 2^-e < 2^15 (fp16 hi part finite)
+        const float qm = fmaxf(fmaxf(red[0][G], red[1][G]), fmaxf(red[2][G], red[3][G]));
+        int eq = 0;
+        (void)frexpf(qm, &eq);  // qm < 2^eq
+        const int es = eq > 15 ? eq - 15 : 0;
+        sgrp[0] = ldexpf(1.0f, -es);
+        sgrp[1] = ldexpf(1.0f, es);
+      }
     }
-    // (the first chunk's barrier orders these writes before any read)
+    __syncthreads();
+    const float sdown = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sgrp[0])));
+    spow = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sgrp[1])));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      half4_t bq = {};
+      if (g4 == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float v = qsum[qb][g] * sdown;  // exact (a power of two)
+          const half_t hi = (half_t)v;
+          bq[2 * g] = hi;
+          bq[2 * g + 1] = (half_t)(v - (float)hi);  // v - hi exact in fp32
+        }
+      }
+      qminb[qb] = bq;
+    }
   }
   float4_t oacc[NDB][2];
 #pragma unroll
@@ -460,7 +509,6 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int g = 0; g < G; ++g) msum[qb][g] = 0.f;
-  constexpr float kL2e = 1.4426950408889634f;
 
   // Staging: every thread stages part of K and part of V of each chunk.
   //   K: key tid / 4, channels (tid % 4) * D/4 .. + D/4 - 1 (D/32 code words);
@@ -560,8 +608,9 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     if constexpr (!F16) {
       if (mact) {
         const float vmg = vmul[mg];
-        kmin_lds[mg][mkey] = h2f((uint16_t)(rkm & 0xFFFF));
-        ksc_lds[mg][mkey] = h2f((uint16_t)(rkm >> 16));
+        kmin2_lds[mkey][mg] = (rkm & 0xFFFFu) * 0x00010001u;  // {min, min}
+        if (G == 1) kmin2_lds[mkey][1] = 0u;
+        ksc_lds[mg][mkey] = h2f((uint16_t)(rkm >> 16)) * kL2e * sgrp[0];
         const float vsf = h2f((uint16_t)(rvm >> 16));
         vmin_lds[mg][mkey] = h2f((uint16_t)(rvm & 0xFFFF)) + 8.0f * vsf;  // min + 8 s: the centre of the codes
         vsc_lds[mg][mkey] = vsf * vmg;  // exact: a power of two
@@ -588,11 +637,19 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
             sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], sacc[kb][qb], 0, 0, 0);
         }
       } else {
-        // group by group: t = codes . q over the group's 64 channels, then
-        // s += scale * t + min * sum(q_g) for keys kb*16 + 4*g4 + r of this lane
+        // min terms first (key kb*16 + l16 in lane group 0), then group by
+        // group: t = codes . q over the group's 64 channels and
+        // s += scale * t for keys kb*16 + 4*g4 + r of this lane
         const int kbase = kb * 16 + 4 * g4;
+        {
+          // A: {min_0, min_0, min_1, min_1} of key kb*16 + l16 in every lane
+          // group (B is zero outside lane group 0)
+          const half4_t amin = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2*>(&kmin2_lds[key][0]));
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+          for (int qb = 0; qb < 2; ++qb)
+            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16f16(amin, qminb[qb], (float4_t){0.f, 0.f, 0.f, 0.f},
+                                                                0, 0, 0);
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float4_t tg[2] = {(float4_t){0.f, 0.f, 0.f, 0.f}, (float4_t){0.f, 0.f, 0.f, 0.f}};
@@ -603,13 +660,12 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) tg[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][kd], tg[qb], 0, 0, 0);
           }
-          const float4 mn = *reinterpret_cast<const float4*>(&kmin_lds[g][kbase]);
           const float4 sc = *reinterpret_cast<const float4*>(&ksc_lds[g][kbase]);
-          const float mnr[4] = {mn.x, mn.y, mn.z, mn.w}, scr[4] = {sc.x, sc.y, sc.z, sc.w};
+          const float scr[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[kb][qb][r] += scr[r] * tg[qb][r] + mnr[r] * qsum[qb][g];
+            for (int r = 0; r < 4; ++r) sacc[kb][qb][r] = fmaf(scr[r], tg[qb][r], sacc[kb][qb][r]);
         }
         // the scores of this key block are formed here: the empty asm keeps
         // the compiler from sinking the combination into the softmax (which
@@ -634,7 +690,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = sacc[kb][qb][r] * kL2e;
+          float v = F16 ? sacc[kb][qb][r] * kL2e : sacc[kb][qb][r];  // 4-bit: already log2 units, 2^-e
           if (!unmasked) {
             const int kpos = (int)k0 + kb * 16 + 4 * g4 + r;
             v = (kpos <= qpos && kpos < (int)nkeys) ? v : -INFINITY;
@@ -644,6 +700,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= spow;  // exact
       if (__any(mx > mrun[qb] + 8.f)) {
         const float mnew = mx > mrun[qb] + 8.f ? mx : mrun[qb];
         const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun[qb] - mnew);
@@ -660,7 +717,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(sacc[kb][qb][r] - mb);
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], spow, -mb));
           sacc[kb][qb][r] = e;
           sum += e;
         }
@@ -711,7 +768,7 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float pv = sacc[kb][qb][r];
-                ph[qb][kh * 4 + r] = (half_t)(pv * vsr[r]);
+                ph[qb][kh * 4 + r] = (half_t)fmaf(pv, vsr[r], 0.f);  // one v_fma_mix per value
                 msum[qb][g] += pv * vnr[r];
               }
           }

@@ -222,7 +222,9 @@ fq_status fq_decode_attention(const uint16_t* q, int64_t ldq, const fq_kv_layer*
  * prompt pass of the README's "Benchmark Results" workload (input length 512)
  * over the 4-bit attention cache ("Extreme Compression").  On the matrix
  * cores with the codes as exact fp16 integers: per quantisation group g the
- * scores are s_g (q . c) + min_g sum(q_g) in fp32; the values take the codes
+ * scores are s_g (q . c) + min_g sum(q_g), in log2 units, in fp32 (the min
+ * terms as a product of the fp16 minima with each group sum split into two
+ * fp16 parts, 22 significant bits); the values take the codes
  * centred (c - 8) against fp16(p * s_g * 2^-E_g) (2^E_g just above the
  * largest value scale of the group among the keys read), the minima (+ 8 s)
  * in fp32.  An fp16 cache is read as stored.
