@@ -116,7 +116,9 @@ def measured_traffic(kernel):
     summary = {"gemm_prefill": ("profiles/gemm_prefill_opt175b_4bit_b144.md", gemm_src),
                "gemm_decode": ("profiles/gemm_decode_opt175b_4bit_b144.md", gemm_src),
                "decode_attention": ("profiles/decode_attention_opt175b_4bit_b144.md",
-                                    [csrc + "attention.hip", csrc + "common.h"])}
+                                    [csrc + "attention.hip", csrc + "common.h"]),
+               "prefill_attention": ("profiles/prefill_attention_opt175b_4bit_b144.md",
+                                     [csrc + "attention.hip", csrc + "common.h"])}
     if kernel not in summary:
         return None
     md, srcs = summary[kernel]

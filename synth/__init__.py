@@ -21,9 +21,13 @@ standard deviation sigma, and support +-3.46 sigma: a bounded stand-in for
 N(0, sigma^2) with the same variance.
 
 Token ids: Lemire's multiply-shift on the high 32 bits, ((u >> 32) * V) >> 32.
+
+Heavy-tailed test inputs (NumPy only; the library has no counterpart):
+Student's t(3), Laplace and a normal with 1-in-64 outliers, from the same
+counters through float64 transforms (heavy_tailed_f16).
 """
 from .gen import (GAMMA, MASK64, mix64, stream_key, raw_u64, normal_f16, normal_scale_f32,
-                  token_ids, STREAM, TENSOR)
+                  token_ids, heavy_tailed_f16, STREAM, TENSOR)
 
 __all__ = ["GAMMA", "MASK64", "mix64", "stream_key", "raw_u64", "normal_f16", "normal_scale_f32",
-           "token_ids", "STREAM", "TENSOR"]
+           "token_ids", "heavy_tailed_f16", "STREAM", "TENSOR"]

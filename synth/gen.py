@@ -105,3 +105,40 @@ def token_ids(seed: int, stream: int, shape, vocab: int) -> np.ndarray:
     with np.errstate(over="ignore"):
         ids = ((u >> np.uint64(32)) * np.uint64(vocab)) >> np.uint64(32)
     return ids.astype(np.int32).reshape(shape)
+
+
+def _unit_open(u):
+    """Uniform variates in (0, 1) from 64-bit outputs: the top 53 bits plus half a step."""
+    return ((u >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+
+
+def heavy_tailed_f16(seed: int, stream: int, shape, sigma: float, kind: str) -> np.ndarray:
+    """Heavy-tailed fp16 variates of scale ``sigma`` (test inputs whose
+    quantisation groups span a wide range, unlike the bounded normal_f16):
+      "student_t3": Student's t with 3 degrees of freedom, Z / sqrt(chi2_3 / 3);
+      "laplace":    Laplace with scale sigma / sqrt(2) (std sigma), by inversion;
+      "outliers":   normal variates (Box-Muller) with every 64th one, at a
+                    pseudo-random place, multiplied by 40.
+    Four uniforms per element come from flat counters 4i .. 4i+3 of the stream;
+    the result is computed in float64 and rounded once to fp16."""
+    n = int(np.prod(shape))
+    ctr = np.arange(4 * n, dtype=np.uint64)
+    u = _unit_open(raw_u64(seed, stream, ctr)).reshape(n, 4)
+
+    def box_muller(a, b):
+        r = np.sqrt(-2.0 * np.log(a))
+        return r * np.cos(2.0 * np.pi * b), r * np.sin(2.0 * np.pi * b)
+
+    if kind == "student_t3":
+        z0, z1 = box_muller(u[:, 0], u[:, 1])
+        z2, z3 = box_muller(u[:, 2], u[:, 3])
+        x = z0 / np.sqrt((z1 * z1 + z2 * z2 + z3 * z3) / 3.0) * sigma
+    elif kind == "laplace":
+        c = u[:, 0] - 0.5
+        x = -np.sign(c) * np.log1p(-2.0 * np.abs(c)) * (sigma / math.sqrt(2.0))
+    elif kind == "outliers":
+        z0, _ = box_muller(u[:, 0], u[:, 1])
+        x = z0 * sigma * np.where(u[:, 2] < 1.0 / 64.0, 40.0, 1.0)
+    else:
+        raise ValueError(f"unknown kind {kind!r}")
+    return np.clip(x, -65504.0, 65504.0).astype(np.float16).reshape(shape)

@@ -35,3 +35,25 @@ def test_streams_differ_and_ids_in_range():
     ids = synth.token_ids(0, synth.STREAM["prompt"], (64, 512), 50272)
     assert ids.min() >= 0 and ids.max() < 50272
     assert len(np.unique(ids)) > 20000
+
+
+def test_heavy_tailed_kinds():
+    """Scale and tails of the heavy-tailed test inputs: t(3) has variance 3
+    sigma^2 and a far tail (P(|t| > 10) ~ 2e-3); the Laplace draw has std sigma
+    and kurtosis 6; the outlier mixture has about 1/64 of its entries at 40x."""
+    n = 1 << 18
+    t = synth.heavy_tailed_f16(0, 5, (n,), 1.0, "student_t3").astype(np.float64)
+    assert abs(np.median(t)) < 0.02
+    assert 0.37 < np.mean(np.abs(t) > 1.0) < 0.41  # P(|t3| > 1) = 0.391
+    assert np.mean(np.abs(t) > 10.0) > 5e-4
+    lap = synth.heavy_tailed_f16(0, 6, (n,), 0.02, "laplace").astype(np.float64)
+    assert abs(lap.std() - 0.02) < 5e-4
+    kurt = np.mean(lap ** 4) / np.mean(lap ** 2) ** 2
+    assert 5.0 < kurt < 7.0
+    o = synth.heavy_tailed_f16(0, 7, (n,), 0.02, "outliers").astype(np.float64)
+    frac = np.mean(np.abs(o) > 0.02 * 6)
+    assert 0.8 / 64 < frac < 1.2 / 64
+    # counter form: the same element from a longer tensor
+    a = synth.heavy_tailed_f16(1, 9, (100,), 1.0, "laplace")
+    b = synth.heavy_tailed_f16(1, 9, (10, 20), 1.0, "laplace").ravel()[:100]
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
