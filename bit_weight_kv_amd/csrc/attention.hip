@@ -404,10 +404,18 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int t0 = blockIdx.x * 128 + wave * 32;     // first query of this wave
+  // Work-group order: the hardware deals consecutive work-groups to the 8
+  // XCDs in turn, and a query block's work grows with its index (causal), so
+  // the index is taken from the high part of the linear id -- every XCD gets
+  // an equal share of every query block -- longest blocks first.
+  // (1-D grid of query blocks x sequences x heads.)
+  const int nqb = (T + 127) / 128, nbh = (int)(gridDim.x / nqb);
+  const int lin = (int)blockIdx.x;
+  const int qblk = nqb - 1 - lin / nbh;
+  const int bh = lin % nbh, b = bh / H, h = bh % H;
+  const int t0 = qblk * 128 + wave * 32;           // first query of this wave
   const int64_t row0 = ((b0 + b) * H + h) * cap;   // first cache row of this (b, h)
-  const int64_t nkeys = pos + min(T, (int)(blockIdx.x * 128 + 128));
+  const int64_t nkeys = pos + min(T, qblk * 128 + 128);
 
   // Q^T operand: lane (query l16 of q-block qb, d slice kd, chunk g4)
   half8_t qf[2][NKD];
@@ -893,7 +901,9 @@ extern "C" fq_status fq_prefill_attention(const uint16_t* q, int64_t ldq, const 
                "fq_prefill_attention: q/out NULL or misaligned");
   hipStream_t st = as_stream(stream);
   const int tk = timing_begin(FQ_KC_PREFILL_ATTN, st);
-  const dim3 grid((unsigned)ceil_div(T, 128), (unsigned)kv->heads, (unsigned)B);
+  const int64_t nwg = ceil_div(T, 128) * kv->heads * B;  // query blocks x sequences x heads
+  FQ_CHECK_ARG(nwg < (int64_t)1 << 31, "fq_prefill_attention: too many work-groups");
+  const dim3 grid((unsigned)nwg);
   by_format(*kv, [&](auto d, auto f16) {
     prefill_attention_mfma_kernel<decltype(d)::value, decltype(f16)::value><<<grid, dim3(256), 0, st>>>(
         q, ldq, kv->k_codes, kv->k_meta, kv->v_codes, kv->v_meta, kv->heads, kv->capacity, b0, (int)T, pos, out,
