@@ -1441,7 +1441,9 @@ __global__ __launch_bounds__(512) void gemm_decode8_kernel(const uint16_t* __res
 // steps, either per tile (SK false: grid.y splits) or as a stream-K schedule
 // (SK true: one block per CU, each an equal run of (tile, step) units).
 // Slot = 16-row block of one k slice (2 MB slots per step): copies in slots
-// 0..7, rebuilds (full, 13 instructions with 4 MFMAs) in the last 8 slots.
+// 0..7; the 8 rebuilds of the next step's weights (13 instructions each) in
+// halves over the last 16 slots when there are 16 or more (MB >= 8), else
+// whole, one with each group of 4 MFMAs, in the last 8 slots.
 // Slice ks gives lane group g the k chunk 2 g + ks (8 values), as the
 // two-waves-per-SIMD decode kernel does, so under the same split the two add
 // the same products in the same order (outputs identical bit for bit).
@@ -1578,6 +1580,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const uint32_t a_dst = (uint32_t)(uintptr_t)a_st(S3{}) + swave * 1024;
       const uint32_t c_dst = c_base + ((kt + 3) % SC) * C_BYTES;
       const int gm = min((kt >> 2) + 1, (kt1 >> 2) - 1);
+      uint32_t hp0 = 0, hp1 = 0, ho0 = 0;  // a rebuild between its two halves
       static_for<NSL>([&](auto sc) {
         constexpr int SL = decltype(sc)::value;
         constexpr int ks = SL / MB, i = SL % MB;
@@ -1595,7 +1598,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         fa[NX % RING] = NX < NSL ? a_frag(As_, NX / MB, NX % MB) : a_frag(a_st(S1{}), (NX - NSL) / MB, (NX - NSL) % MB);
         __builtin_amdgcn_sched_barrier(0);
         const half8_t& af = fa[SL % RING];
-        if constexpr (SL >= NSL - 8) {
+        if constexpr (NSL >= 16 && SL >= NSL - 16) {
+          // 16 or more slots: each rebuild in two halves over two slots (at
+          // most 7 VALU instructions beside each group of 4 MFMAs)
+          constexpr int q = SL - (NSL - 16), r = q / 2;
+          if constexpr (q % 2 == 0) {
+            mfma4_rebuild_h1(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, bcur[ks][0], bcur[ks][1], bcur[ks][2],
+                             bcur[ks][3], cw[r / FN][r % FN], hp0, hp1, ho0);
+          } else {
+            half8_t nb;
+            mfma4_rebuild_h2(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, bcur[ks][0], bcur[ks][1], bcur[ks][2],
+                             bcur[ks][3], hp0, hp1, ho0, cm[r % FN], nb);
+            bnxt[r / FN][r % FN] = nb;
+          }
+        } else if constexpr (NSL < 16 && SL >= NSL - 8) {
           constexpr int r = SL - (NSL - 8);
           half8_t nb;
           mfma4_rebuild_ab(acc[i][0], acc[i][1], acc[i][2], acc[i][3], af, af, af, af, bcur[ks][0], bcur[ks][1],
