@@ -74,8 +74,11 @@ def test_decode_attention_long_and_peaked(fmt):
 
 @pytest.mark.parametrize("fmt", ["q4", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("T,pos", [(1, 0), (5, 0), (64, 0), (65, 0), (130, 0), (9, 7), (300, 40)])
+@pytest.mark.parametrize("T,pos", [(1, 0), (5, 0), (64, 0), (65, 0), (130, 0), (9, 7), (300, 40), (600, 23)])
 def test_prefill_attention_causal(d, T, pos, fmt):
+    """Causal attention of T new tokens after pos cached ones against the
+    oracle's attention per query; (600, 23): five 128-query blocks per (b, h),
+    the last one ragged, dealt over the XCDs longest first."""
     B, H = 2, 3
     kernel = "mfma"
     log(f"prefill attention {fmt} d={d} T={T} pos={pos}")
