@@ -846,8 +846,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wn = wave;
   const int fr = lane & 15, fk = lane >> 4;
 
-  // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 4 M
-  // tiles x 8 N tiles
+  // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 2 M
+  // tiles x 16 N tiles (measured 1.0-1.4 % faster than 4 x 8 and 2-3 %
+  // faster than 1 x 32 or 8 x 4 over the four OPT-175B prefill products)
   const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
   const int64_t nblk = tiles_m * tiles_n;
   const int64_t bid = blockIdx.x;
@@ -856,7 +857,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t per_xcd = nblk / 8;
     if (bid < per_xcd * 8) lid = (bid % 8) * per_xcd + bid / 8;
   }
-  constexpr int GM = 4;
+  constexpr int GM = 2;
   const int64_t group = lid / (GM * tiles_n);
   const int64_t first_m = group * GM;
   const int64_t gsize = min((int64_t)GM, tiles_m - first_m);
