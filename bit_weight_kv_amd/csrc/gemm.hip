@@ -847,8 +847,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int fr = lane & 15, fk = lane >> 4;
 
   // XCD-aware grouped order: the 32 blocks an XCD runs at once cover 2 M
-  // tiles x 16 N tiles (measured 1.0-1.4 % faster than 4 x 8 and 2-3 %
-  // faster than 1 x 32 or 8 x 4 over the four OPT-175B prefill products)
+  // tiles x 16 N tiles (over the four OPT-175B prefill products measured
+  // 1.0-1.4 % faster than 4 x 8, 2 % faster than 1 x 32, 7 % than 8 x 4)
   const int64_t tiles_m = (M + BMx - 1) / BMx, tiles_n = (N + BNx - 1) / BNx;
   const int64_t nblk = tiles_m * tiles_n;
   const int64_t bid = blockIdx.x;
