@@ -15,11 +15,11 @@ pytestmark = pytest.mark.gpu
 fq = pytest.importorskip("bit_weight_kv_amd")
 
 
-def _cache(B, H, d, n, cap, seed, b_off=0, fmt="q4", v_sigma=1.0):
+def _cache(B, H, d, n, cap, seed, b_off=0, fmt="q4", v_sigma=1.0, k_sigma=1.0):
     """fp16 K/V [B, n, H*d] from the generator -> GPU cache (appended) and the
     oracle's reading of the same cache (fmt "q4": 4-bit, "f16": fp16)."""
     h = H * d
-    k = synth.normal_f16(seed, synth.STREAM["aux"] + 20, (B * n, h), 1.0)
+    k = synth.normal_f16(seed, synth.STREAM["aux"] + 20, (B * n, h), k_sigma)
     v = synth.normal_f16(seed, synth.STREAM["aux"] + 21, (B * n, h), v_sigma)
     if fmt == "q4":
         kc = torch.zeros((B + b_off, H, cap, d // 2), dtype=torch.uint8, device="cuda:0")
@@ -96,6 +96,35 @@ def test_prefill_attention_causal(d, T, pos, fmt):
     ref = ref.transpose(0, 2, 1, 3).reshape(B * T, H * d)
     r, m = assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill {kernel} {fmt} d={d} T={T} pos={pos}")
     log(f"prefill {kernel} {fmt} d={d} T={T} pos={pos}: rel_l2 {r:.2e} max_abs {m:.2e}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_attention_large_query_sums(d):
+    """Queries whose channel sums over a quantisation group exceed what fp16
+    holds once scaled by log2(e) (every channel 400 + N(0, 20): about 25600 per
+    group, 36900 in log2 units): the 4-bit prefill kernel then takes all its
+    scores 2^-1 smaller for the min-term product and restores them in the
+    exponent.  Keys of small spread (sigma 1e-3) keep the softmax from
+    collapsing onto one key: the min terms (min_g times the group sums) are
+    the large part of every score.  Held to the same bounds as the other
+    prefill cases against the oracle's float64 attention."""
+    B, H, T, pos = 2, 3, 130, 20
+    n = pos + T
+    view, keep, kh, vh = _cache(B, H, d, n, n + 1, seed=77 + d, fmt="q4", k_sigma=1e-3)
+    q = (400.0 + synth.normal_f16(2, synth.STREAM["aux"] + 24, (B * T, H * d), 20.0).astype(np.float32)).astype(
+        np.float16)
+    qs = q.astype(np.float64).reshape(B * T, H, d // 64, 64).sum(-1) * 1.4426950408889634
+    assert qs.min() > 2.0 ** 15  # the rescaled path
+    out = torch.empty((B * T, H * d), dtype=torch.float16, device="cuda:0")
+    fq.fq_prefill_attention(dev(q), view, 0, B, T, pos, out)
+    torch.cuda.synchronize()
+    q4 = q.reshape(B, T, H, d).transpose(0, 2, 1, 3).astype(np.float64)
+    ref = np.empty((B, H, T, d))
+    for t in range(T):
+        ref[:, :, t] = oracle.attention_decode(q4[:, :, t], kh[:, :, :pos + t + 1], vh[:, :, :pos + t + 1])
+    ref = ref.transpose(0, 2, 1, 3).reshape(B * T, H * d)
+    r, m = assert_close(host(out), ref, rel=2e-3, abs_=4e-3, what=f"prefill large query sums d={d}")
+    log(f"prefill large query sums d={d}: rel_l2 {r:.2e} max_abs {m:.2e}")
 
 
 @pytest.mark.parametrize("v_sigma", [2.0 ** -8, 64.0])
