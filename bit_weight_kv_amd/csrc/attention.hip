@@ -689,20 +689,28 @@ __global__ __launch_bounds__(256) void prefill_attention_mfma_kernel(
     // same base), and the rescale of O is skipped in most chunks (a
     // wave-uniform branch).  Chunks wholly below the wave's first query and
     // inside the keys need no mask.
-    const bool unmasked = k0 + KC - 1 <= pos + t0 && k0 + KC <= nkeys;
+    // The causal mask, on chunks that cross this wave's diagonal (a
+    // wave-uniform branch): key kpos = k0 + 16 kb + 4 g4 + r is kept for query
+    // qpos = pos + t0 + 16 qb + l16 iff 16 kb + r - 16 qb <= dq, one compare
+    // with a constant per score.  Keys at or past nkeys always fail it for a
+    // query that is stored (qpos < nkeys); rows past T are never stored.
+    if (k0 + KC - 1 > pos + t0) {
+      const int dq = (int)(pos + t0 - k0) + l16 - 4 * g4;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[kb][qb][r] = 16 * kb + r - 16 * qb <= dq ? sacc[kb][qb][r] : -INFINITY;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qpos = (int)(pos + t0) + qb * 16 + l16;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = F16 ? sacc[kb][qb][r] * kL2e : sacc[kb][qb][r];  // 4-bit: already log2 units, 2^-e
-          if (!unmasked) {
-            const int kpos = (int)k0 + kb * 16 + 4 * g4 + r;
-            v = (kpos <= qpos && kpos < (int)nkeys) ? v : -INFINITY;
-          }
+          const float v = F16 ? sacc[kb][qb][r] * kL2e : sacc[kb][qb][r];  // 4-bit: already log2 units, 2^-e
           sacc[kb][qb][r] = v;
           mx = fmaxf(mx, v);
         }
